@@ -1,0 +1,432 @@
+"""CPU oracle for the tree speculative-decoding hot path.
+
+TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers; the library's product path
+never imports, links or runs anything here, and this module imports nothing
+from the library.
+
+Plain numpy.  Every floating-point step runs in float64 on the stored input
+values (float32 inputs widen exactly, bf16 bit patterns are widened here).
+Loops follow the pages' own order; numpy's matmul, argmax, exp and sort are
+used as library primitives for single steps, never to reorder the method.
+
+Sources (web pages, cited by title and section):
+  [P1] "SGLang 源码完全拆解(十一):投机解码——草稿生成、批量验证与 token 接受如何接进同一条前向"
+  [P2] "投机解码 Accept:从 Verify 行到最终输出路径"
+  [P4] "Speculative Decoding" (sglang-internals book, part 3, execution model)
+  [P5] "把投机采样讲透:以 SGLang 中的 EAGLE-2 为例"
+
+Readings where the pages are silent (each also listed in the design notes):
+  * torch.topk's order among equal scores is unstated: rank by (score
+    descending, flat index ascending).
+  * A node's parent is found through the parent list as
+    parents[f // topk] (the score row of flat index f holds the flat index of
+    the token it was expanded from; -1 in row 0 is the root).
+  * The tree mask includes the diagonal (a node attends to itself).
+  * Bit-packed mask rows are LSB-first: bit j of row k set iff node j is
+    visible to node k; word width 8 << ceil(log2(ceil(n / 8))).
+  * Children and siblings are ordered by ascending node index.
+  * Softmax scale is 1/sqrt(head_dim) unless the caller gives one.
+  * Sampled accept: one uniform per tree node tests that node; one final
+    uniform per request draws the terminal token by inverse CDF in vocabulary
+    order; rejected siblings update the residual recursively.
+  * Malformed trees: a node whose parent is not selected (or whose parent
+    index is out of range) hangs off the root and raises a status bit.
+
+Status bits (OR-ed per call): 1 index out of range, 2 selection not closed
+under ancestors, 4 accepted path longer than the accept_index row, 8 residual
+mass exactly zero (informational).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ST_RANGE = 1
+ST_NOT_CLOSED = 2
+ST_DEPTH = 4
+ST_ZERO_RESIDUAL = 8
+
+MASK_QLEN_U8 = 1
+MASK_QLEN_BITS = 2
+
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values as float64.  bf16 arrives as uint16 bit patterns."""
+    if dtype == "bf16":
+        bits = np.ascontiguousarray(x, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# C1  Tree build
+# ---------------------------------------------------------------------------
+
+def select_nodes(scores_row: np.ndarray, count: int) -> np.ndarray:
+    """[P1] organize_draft_results: take the ``count`` best flat candidates
+    by path score, then sort the chosen flat indices ascending so every parent
+    comes before its children."""
+    s = np.asarray(scores_row, dtype=np.float64)
+    order = sorted(range(s.size), key=lambda f: (-s[f], f))
+    return np.array(sorted(order[:count]), dtype=np.int64)
+
+
+def mask_word_bits(n: int) -> int:
+    """[P1] 三种 mask 形态 (QLEN_ONLY_BITPACKING): the packed dtype index is
+    ceil(log2(ceil(n/8))); the word is 8 << index bits wide."""
+    idx = math.ceil(math.log2(max(1, (n + 7) // 8)))
+    return 8 << idx
+
+
+def build_tree(scores, tokens, parents, bonus, seq_lens, topk, num_steps, n):
+    """[P1] build_tree_kernel_efficient and the retrieve_* adjacency lists;
+    [P5] 4.3 tree mask and positions; [P2] 二 (first-child / next-sibling).
+
+    Returns a dict of numpy arrays:
+      draft_tokens [b*n], positions [b*n], mask bool [b, n, n],
+      retrieve_index / next_token / next_sibling [b, n], selected [b, n-1],
+      parent [b, n], depth [b, n], status int.
+    """
+    scores = np.asarray(scores)
+    b = scores.shape[0]
+    ncand = topk + (num_steps - 1) * topk * topk
+    npar = 1 + (num_steps - 1) * topk
+    assert scores.shape == (b, ncand) and np.shape(tokens) == (b, ncand)
+    assert np.shape(parents) == (b, npar)
+    assert 1 <= n and n - 1 <= ncand
+    status = 0
+    draft_tokens = np.zeros(b * n, np.int64)
+    positions = np.zeros(b * n, np.int64)
+    mask = np.zeros((b, n, n), bool)
+    r_index = np.full((b, n), -1, np.int64)
+    r_next = np.full((b, n), -1, np.int64)
+    r_sib = np.full((b, n), -1, np.int64)
+    selected = np.zeros((b, max(n - 1, 0)), np.int64)
+    parent = np.full((b, n), -1, np.int64)
+    depth = np.zeros((b, n), np.int64)
+    for r in range(b):
+        sel = select_nodes(scores[r], n - 1)
+        selected[r] = sel
+        # node 0 is the bonus token from the previous round; node k >= 1 is sel[k-1]
+        draft_tokens[r * n] = bonus[r]
+        for k in range(1, n):
+            draft_tokens[r * n + k] = tokens[r, sel[k - 1]]
+        where = {int(f): k for k, f in enumerate(sel, start=1)}
+        for k in range(1, n):
+            f = int(sel[k - 1])
+            if f < topk:
+                parent[r, k] = 0                      # step-0 candidates hang off the root
+                continue
+            g = int(parents[r, f // topk])            # flat index this score row expanded
+            if g < 0 or g >= ncand:
+                status |= ST_RANGE
+                parent[r, k] = 0
+            elif g not in where or where[g] >= k:
+                status |= ST_NOT_CLOSED
+                parent[r, k] = 0
+            else:
+                parent[r, k] = where[g]
+        for k in range(1, n):
+            depth[r, k] = depth[r, parent[r, k]] + 1
+        for k in range(n):
+            positions[r * n + k] = int(seq_lens[r]) + depth[r, k]
+            # visible set of node k: itself and every ancestor up to the root
+            j = k
+            while True:
+                mask[r, k, j] = True
+                if j == 0:
+                    break
+                j = int(parent[r, j])
+            r_index[r, k] = r * n + k
+        for k in range(n):
+            kids = [c for c in range(1, n) if parent[r, c] == k]
+            r_next[r, k] = kids[0] if kids else -1
+            if k > 0:
+                later = [c for c in range(k + 1, n) if parent[r, c] == parent[r, k]]
+                r_sib[r, k] = later[0] if later else -1
+    return dict(draft_tokens=draft_tokens, positions=positions, mask=mask,
+                retrieve_index=r_index, retrieve_next_token=r_next,
+                retrieve_next_sibling=r_sib, selected=selected, parent=parent,
+                depth=depth, status=status)
+
+
+def pack_mask(mask: np.ndarray, mode: int) -> np.ndarray:
+    """[P1] 三种 mask 形态: QLEN_ONLY as [b, n, n] bytes, or QLEN_ONLY bit-packed
+    into one word per row (bit j = node j visible)."""
+    b, n, _ = mask.shape
+    if mode == MASK_QLEN_U8:
+        return mask.astype(np.uint8)
+    bits = mask_word_bits(n)
+    dt = {8: np.uint8, 16: np.uint16, 32: np.uint32, 64: np.uint64}[bits]
+    out = np.zeros((b, n), np.uint64)
+    for j in range(n):
+        out |= mask[:, :, j].astype(np.uint64) << np.uint64(j)
+    return out.astype(dt)
+
+
+def unpack_mask(words: np.ndarray, n: int) -> np.ndarray:
+    w = np.asarray(words).astype(np.uint64)
+    return ((w[..., None] >> np.arange(n, dtype=np.uint64)) & np.uint64(1)).astype(bool)
+
+
+# ---------------------------------------------------------------------------
+# C2  Tree-masked verify attention
+# ---------------------------------------------------------------------------
+
+def slot_of(page_table, page_size, r, pos):
+    return int(page_table[r, pos // page_size]) * page_size + pos % page_size
+
+
+def verify_attention(q, k_pool, v_pool, page_table, seq_lens, out_cache_loc, mask,
+                     num_q_heads, num_kv_heads, page_size, dtype, sm_scale=None,
+                     rows=None):
+    """[P5] 4.2 / 4.3: each flattened tree node is a query over the cached
+    history of its request plus the tree nodes its mask row allows (itself and
+    its ancestors); [P1] the tree nodes' K/V sit at out_cache_loc.
+
+    q [b*n, hq, d]; k_pool / v_pool [slots, hkv, d]; mask bool [b, n, n].
+    Query head h reads KV head h // (hq / hkv).  Returns float64
+    [b*n, hq, d], or, when ``rows`` lists (row, head) pairs, only those
+    vectors as [len(rows), d].
+    """
+    b, n, _ = mask.shape
+    d = q.shape[-1]
+    G = num_q_heads // num_kv_heads
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    want = None
+    if rows is not None:
+        want = {}
+        for i, (row, h) in enumerate(rows):
+            want.setdefault((row // n, h // G), []).append((i, row, h))
+        out = np.zeros((len(rows), d))
+    else:
+        out = np.zeros((b * n, num_q_heads, d))
+    for r in range(b):
+        L = int(seq_lens[r])
+        hist = np.array([slot_of(page_table, page_size, r, p) for p in range(L)], np.int64)
+        tree = np.asarray(out_cache_loc[r * n:(r + 1) * n], np.int64)
+        for g in range(num_kv_heads):
+            if want is not None and (r, g) not in want:
+                continue
+            K = widen(np.concatenate([k_pool[hist, g], k_pool[tree, g]]), dtype)
+            V = widen(np.concatenate([v_pool[hist, g], v_pool[tree, g]]), dtype)
+            pairs = (want[(r, g)] if want is not None else
+                     [(None, r * n + k, h) for k in range(n) for h in range(g * G, (g + 1) * G)])
+            for i, row, h in pairs:
+                k = row - r * n
+                visible = np.concatenate([np.ones(L, bool), mask[r, k]])
+                s = scale * (K[visible] @ widen(q[row, h], dtype))
+                p = np.exp(s - s.max())
+                o = (p / p.sum()) @ V[visible]
+                if i is None:
+                    out[row, h] = o
+                else:
+                    out[i] = o
+    return out
+
+
+# ---------------------------------------------------------------------------
+# C3  Greedy accept
+# ---------------------------------------------------------------------------
+
+def argmax_rows(logits: np.ndarray, dtype: str) -> np.ndarray:
+    """[P1] 三条判定路径: the target's choice per verify row is torch.argmax,
+    which returns the first index among equal maxima."""
+    x = widen(logits, dtype)
+    return np.argmax(x, axis=-1).astype(np.int64)
+
+
+def accept_greedy(target_logits, candidates, retrieve_index, retrieve_next_token,
+                  retrieve_next_sibling, b, n, s1, dtype):
+    """[P2] 三 (Greedy Accept 的行索引与输出) and [P5] 5.3: from the root,
+    scan children by first-child / next-sibling for the candidate equal to
+    the target's choice at the current node; descend on a match; the target's
+    choice at the last node is the terminal token.  accept_index holds verify
+    rows; accept_length counts accepted drafts plus the terminal token.
+    """
+    tp = argmax_rows(target_logits, dtype)
+    predict = np.zeros(b * n, np.int64)
+    accept_index = np.full((b, s1), -1, np.int64)
+    accept_length = np.zeros(b, np.int64)
+    status = 0
+    cand = np.asarray(candidates).reshape(b, n)
+    for r in range(b):
+        cur = 0
+        cnt = 0
+        accept_index[r, 0] = retrieve_index[r, 0]
+        while True:
+            want = tp[retrieve_index[r, cur]]
+            c = int(retrieve_next_token[r, cur])
+            hit = -1
+            while c != -1:
+                if cand[r, c] == want:
+                    hit = c
+                    break
+                c = int(retrieve_next_sibling[r, c])
+            if hit < 0:
+                break
+            if cnt + 1 >= s1:
+                status |= ST_DEPTH
+                break
+            predict[retrieve_index[r, cur]] = cand[r, hit]
+            cnt += 1
+            accept_index[r, cnt] = retrieve_index[r, hit]
+            cur = hit
+        predict[retrieve_index[r, cur]] = tp[retrieve_index[r, cur]]
+        accept_length[r] = cnt + 1
+    return dict(predict=predict, accept_index=accept_index, accept_length=accept_length,
+                target_predict=tp, status=status)
+
+
+# ---------------------------------------------------------------------------
+# C4  Rejection-sampled accept
+# ---------------------------------------------------------------------------
+
+def softmax_t(logits_row: np.ndarray, temperature: float) -> np.ndarray:
+    """[P2] 四: the target (and draft) distribution at temperature T,
+    max-subtracted, float64."""
+    x = np.asarray(logits_row, dtype=np.float64)
+    e = np.exp((x - x.max()) / float(temperature))
+    return e / e.sum()
+
+
+def accept_sample(target_logits, draft_logits, temperature, uniforms, final_uniforms,
+                  candidates, retrieve_index, retrieve_next_token, retrieve_next_sibling,
+                  b, n, s1, dtype, band=1e-6):
+    """[P4] 接受/拒绝 and [P2] 四 (Classic Rejection Sampling): at node cur
+    the residual R starts as the target distribution p of row(cur); each child
+    c (sibling order) with token t is accepted iff u[c] < min(1, R(t)/q(t)),
+    q being the draft distribution of row(cur).  A rejection replaces R by
+    max(0, R - q) renormalised.  When no child is accepted (or cur is a leaf)
+    the terminal token is drawn from R by inverse CDF with the request's final
+    uniform.  [P5] 5.6: the walk is the greedy walk's.
+
+    Also returns, per request, the smallest margin to a decision boundary
+    (|u - min(1, ratio)| for each test, the final draw's distance to the
+    nearest CDF edge over the residual mass, and the residual masses):
+    a request with a margin below ``band`` may legitimately differ under
+    rounding.
+    """
+    tl = widen(target_logits, dtype)
+    dl = widen(draft_logits, dtype)
+    cand = np.asarray(candidates).reshape(b, n)
+    predict = np.zeros(b * n, np.int64)
+    accept_index = np.full((b, s1), -1, np.int64)
+    accept_length = np.zeros(b, np.int64)
+    margin = np.full(b, np.inf)
+    status = 0
+    for r in range(b):
+        T = float(temperature[r])
+        cur = 0
+        cnt = 0
+        accept_index[r, 0] = retrieve_index[r, 0]
+        while True:
+            row = int(retrieve_index[r, cur])
+            R = softmax_t(tl[row], T)
+            q = softmax_t(dl[row], T)
+            c = int(retrieve_next_token[r, cur])
+            hit = -1
+            while c != -1:
+                t = int(cand[r, c])
+                if q[t] > 0:
+                    ratio = R[t] / q[t]
+                else:
+                    ratio = math.inf if R[t] > 0 else 0.0
+                thr = min(1.0, ratio)
+                u = float(uniforms[r, c])
+                margin[r] = min(margin[r], abs(u - thr))
+                if u < thr:
+                    hit = c
+                    break
+                resid = np.maximum(R - q, 0.0)
+                Z = resid.sum()
+                margin[r] = min(margin[r], Z)
+                if Z > 0:
+                    R = resid / Z
+                else:
+                    status |= ST_ZERO_RESIDUAL
+                c = int(retrieve_next_sibling[r, c])
+            if hit < 0:
+                break
+            if cnt + 1 >= s1:
+                status |= ST_DEPTH
+                break
+            predict[row] = cand[r, hit]
+            cnt += 1
+            accept_index[r, cnt] = retrieve_index[r, hit]
+            cur = hit
+        # terminal token: inverse CDF of the current residual in vocabulary order
+        row = int(retrieve_index[r, cur])
+        total = R.sum()
+        target = float(final_uniforms[r]) * total
+        cdf = np.cumsum(R)
+        x = int(np.argmax(cdf > target)) if cdf[-1] > target else int(R.size - 1)
+        lo = cdf[x - 1] if x > 0 else 0.0
+        margin[r] = min(margin[r], (target - lo) / total, (cdf[x] - target) / total)
+        predict[row] = x
+        accept_length[r] = cnt + 1
+    return dict(predict=predict, accept_index=accept_index, accept_length=accept_length,
+                margin=margin, exempt=margin < band, status=status)
+
+
+# ---------------------------------------------------------------------------
+# C5  Accepted-KV compaction
+# ---------------------------------------------------------------------------
+
+def compact_kv(k_pool, v_pool, page_table, seq_lens, out_cache_loc, accept_index,
+               accept_length, b, n, page_size):
+    """[P1] KV 回写 (move_accept_tokens_to_target_kvcache) and [P2] 六: the
+    verify rows named by accept_index (root plus accepted drafts, not the
+    terminal token) move from their verify slots to the request's sequence
+    positions [L, L + accept_length); the sequence grows by accept_length and
+    every verify slot that is not a target slot is returned free.
+
+    Pools are [layers, slots, hkv, d] (any dtype; copied bit for bit).
+    Returns new copies of the pools plus new_seq_lens [b], free_slots [b*n]
+    (request r's list at r*n, padded with -1), num_free [b], status.
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    nslots = k_out.shape[1]
+    new_seq_lens = np.zeros(b, np.int64)
+    free_slots = np.full(b * n, -1, np.int64)
+    num_free = np.zeros(b, np.int64)
+    status = 0
+    for r in range(b):
+        L = int(seq_lens[r])
+        m = int(accept_length[r])
+        src, tgt = [], []
+        for j in range(m):
+            row = int(accept_index[r, j])
+            if row < 0:
+                continue
+            if row >= b * n:
+                status |= 1
+                continue
+            s = int(out_cache_loc[row])
+            pos = L + j
+            page = int(page_table[r, pos // page_size])
+            t = page * page_size + pos % page_size
+            if not (0 <= s < nslots) or page < 0 or not (0 <= t < nslots):
+                status |= 1
+                continue
+            src.append(s)
+            tgt.append(t)
+        # all source rows are read before any target row is written
+        k_rows = k_out[:, src].copy()
+        v_rows = v_out[:, src].copy()
+        k_out[:, tgt] = k_rows
+        v_out[:, tgt] = v_rows
+        new_seq_lens[r] = L + m
+        kept = set(tgt)
+        cnt = 0
+        for k in range(n):
+            s = int(out_cache_loc[r * n + k])
+            if s not in kept:
+                free_slots[r * n + cnt] = s
+                cnt += 1
+        num_free[r] = cnt
+    return dict(k_pool=k_out, v_pool=v_out, new_seq_lens=new_seq_lens,
+                free_slots=free_slots, num_free=num_free, status=status)
