@@ -1,0 +1,259 @@
+/*
+ * spec.h - C ABI of the tree speculative-decoding hot path for AMD MI355X
+ * (gfx950): tree build, tree-masked verify attention, greedy and
+ * rejection-sampled tree accept, accepted-KV compaction.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "SGLang 源码完全拆解(十一):投机解码——草稿生成、批量验证与 token 接受如何接进同一条前向"
+ *   [P2] "投机解码 Accept:从 Verify 行到最终输出路径"
+ *   [P4] "Speculative Decoding" (sglang-internals book, execution model)
+ *   [P5] "把投机采样讲透:以 SGLang 中的 EAGLE-2 为例"
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a device pointer on the current HIP device unless a
+ *     comment says otherwise.  All tensors are dense and row-major.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work: they never synchronise, never allocate and
+ *     keep no state between calls, so they are re-entrant.
+ *   - The caller owns every buffer.  Inputs are never written, except the KV
+ *     pools of spec_compact_kv, which are updated in place.
+ *   - Return value: SPEC_OK, or a negative SPEC_ERR_* when a host-side check
+ *     fails; then nothing was launched.
+ *   - `dev_status` (may be NULL) is one int32 on the device.  Kernels OR the
+ *     SPEC_ST_* bits into it for data-dependent problems; the caller zeroes it
+ *     and reads it whenever it likes.  This replaces the index-range guard
+ *     the pages run before gathers ([P1] organize_draft_results, KV 回写).
+ *   - batch == 0 is a valid no-op (the pages' idle batch returns empty
+ *     results, [P1] eagle_sample 的骨架).
+ *   - -1 means "none" in retrieve_* and accept_index ([P1] 邻接表:retrieve_* 三兄弟).
+ *   - Tree node k of request b occupies flattened verify row b*n + k.
+ *   - bf16 tensors are raw bfloat16 (16-bit) values; f32 are IEEE binary32.
+ */
+#ifndef SPECMI_SPEC_H
+#define SPECMI_SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum spec_error {
+    SPEC_OK = 0,
+    SPEC_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    SPEC_ERR_SHAPE = -2,       /* sizes inconsistent or out of the supported range */
+    SPEC_ERR_DTYPE = -3,       /* dtype code not SPEC_F32 / SPEC_BF16              */
+    SPEC_ERR_UNSUPPORTED = -4, /* valid request this build does not implement      */
+    SPEC_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required          */
+    SPEC_ERR_HIP = -6          /* a HIP launch reported an error                   */
+};
+
+enum spec_status_bits {
+    SPEC_ST_RANGE = 1,          /* an index (parent, row, slot, page) out of range  */
+    SPEC_ST_NOT_CLOSED = 2,     /* a kept node's parent was not kept                */
+    SPEC_ST_DEPTH = 4,          /* accepted path longer than accept_width           */
+    SPEC_ST_ZERO_RESIDUAL = 8   /* residual mass exactly zero (informational)       */
+};
+
+enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 };
+enum spec_mask_mode { SPEC_MASK_QLEN_U8 = 1, SPEC_MASK_QLEN_BITS = 2 };
+
+typedef void *spec_stream_t;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int spec_version(void);
+
+/* Human-readable text of a return code. */
+const char *spec_status_string(int status);
+
+/* Bytes per row of a SPEC_MASK_QLEN_BITS tree mask: 1, 2, 4 or 8, i.e. the
+ * word of 8 << ceil(log2(ceil(n / 8))) bits the page gives for
+ * QLEN_ONLY_BITPACKING ([P1] 三种 mask 形态).  0 if n is outside 1..64. */
+int spec_mask_word_bytes(int num_draft_tokens);
+
+/*
+ * Tree build.  [P1] organize_draft_results and build_tree_kernel_efficient;
+ * [P5] 4.3 (tree mask, positions); [P2] 二 (first-child / next-sibling).
+ *
+ * Inputs, per request b (ncand = topk + (num_steps-1)*topk*topk,
+ * npar = 1 + (num_steps-1)*topk):
+ *   scores   [batch, ncand] f32  path score of every draft candidate, in the
+ *                                order the draft steps produced them (the
+ *                                score list concatenated and flattened)
+ *   tokens   [batch, ncand] i32  token id of every candidate (same order)
+ *   parents  [batch, npar]  i32  the parent list of all steps but the last:
+ *                                entry r is the flat candidate index whose
+ *                                expansion produced score row r (entry 0 is
+ *                                the root sentinel -1 and is not read)
+ *   bonus    [batch]        i32  previous round's terminal token = tree root
+ *   seq_lens [batch]        i32  committed history length (prefix length)
+ * What is computed:
+ *   the num_draft_tokens-1 candidates with the largest scores are kept
+ *   (ties: lower flat index first), their flat indices sorted ascending;
+ *   node 0 is the bonus token, node k >= 1 is kept candidate k-1.  A kept
+ *   candidate f < topk hangs off the root; otherwise its parent is the node
+ *   holding flat index parents[f / topk].
+ * Outputs:
+ *   draft_tokens [batch*n] i32       node tokens, root first
+ *   positions    [batch*n] i32       seq_lens[b] + depth (siblings share one)
+ *   tree_mask    SPEC_MASK_QLEN_U8:   [batch, n, n] u8, 1 where column node j
+ *                                     is row node k itself or an ancestor
+ *                SPEC_MASK_QLEN_BITS: [batch, n] words of
+ *                                     spec_mask_word_bytes(n) bytes,
+ *                                     little-endian, bit j = node j visible
+ *   retrieve_index        [batch, n] i32  b*n + k
+ *   retrieve_next_token   [batch, n] i32  smallest child index, -1 if leaf
+ *   retrieve_next_sibling [batch, n] i32  next larger index with the same
+ *                                         parent, -1 if none (root: -1)
+ *   selected [batch, n-1] i32 (optional, NULL to skip) kept flat indices
+ * Data errors: parent index outside [0, ncand) -> SPEC_ST_RANGE; parent not
+ *   kept -> SPEC_ST_NOT_CLOSED; such a node is attached to the root.
+ * Limits: 1 <= n <= 64, n-1 <= ncand <= 4096, topk >= 1, num_steps >= 1.
+ * Scores must not be NaN.
+ */
+int spec_build_tree(int batch, int topk, int num_steps, int num_draft_tokens, int mask_mode,
+                    const float *scores, const int32_t *tokens, const int32_t *parents,
+                    const int32_t *bonus, const int32_t *seq_lens,
+                    int32_t *draft_tokens, int32_t *positions, void *tree_mask,
+                    int32_t *retrieve_index, int32_t *retrieve_next_token,
+                    int32_t *retrieve_next_sibling, int32_t *selected,
+                    int32_t *dev_status, spec_stream_t stream);
+
+/*
+ * Verify attention.  [P5] 4.2-4.3 and [P1] 验证前向的组装: every tree node
+ * is a query row; it attends to the request's whole cached history and to
+ * the tree nodes its mask row allows (itself and its ancestors), whose K/V
+ * the verify forward has written at out_cache_loc.
+ *
+ *   q        [batch*n, num_q_heads, head_dim]   dtype
+ *   k_pool, v_pool [num_slots, num_kv_heads, head_dim]  dtype (one layer)
+ *   page_table [batch, max_pages] i32  history position p of request b is
+ *            slot page_table[b][p / page_size] * page_size + p % page_size
+ *   seq_lens [batch] i32  history length L_b (0 allowed); positions
+ *            0 .. L_b-1 are history, the tree's K/V are at out_cache_loc
+ *   max_seq_len  host int, an upper bound of seq_lens (sizes the launch);
+ *            a request with L_b > max_seq_len raises SPEC_ST_RANGE and its
+ *            output is left unwritten
+ *   out_cache_loc [batch*n] i32  slot of tree node k of request b
+ *   tree_mask  [batch, n] SPEC_MASK_QLEN_BITS words (spec_mask_word_bytes)
+ *   out      [batch*n, num_q_heads, head_dim]  dtype of q
+ *   sm_scale   softmax scale; <= 0 selects 1/sqrt(head_dim)
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).  Scores,
+ * softmax and accumulation are fp32 (online softmax); bf16 operands use the
+ * matrix cores.
+ * workspace: at least spec_verify_attention_workspace_size(...) bytes, any
+ * contents.  Slots or page ids out of range raise SPEC_ST_RANGE and read as
+ * zero vectors.
+ * Limits: 1 <= n <= 64; head_dim 64 or 128; num_q_heads % num_kv_heads == 0;
+ * page_size >= 1.
+ */
+size_t spec_verify_attention_workspace_size(int batch, int num_draft_tokens, int num_q_heads,
+                                            int num_kv_heads, int head_dim, int max_seq_len,
+                                            int dtype);
+int spec_verify_attention(int batch, int num_draft_tokens, int num_q_heads, int num_kv_heads,
+                          int head_dim, int page_size, int dtype, float sm_scale,
+                          const void *q, const void *k_pool, const void *v_pool,
+                          int64_t num_slots, const int32_t *page_table, int max_pages,
+                          const int32_t *seq_lens, int max_seq_len,
+                          const int32_t *out_cache_loc, const void *tree_mask, void *out,
+                          void *workspace, size_t workspace_bytes, int32_t *dev_status,
+                          spec_stream_t stream);
+
+/*
+ * Greedy tree accept.  [P1] 三条判定路径 (argmax, then the tree walk);
+ * [P2] 三 (row indices and the one-position offset); [P5] 5.3.
+ *
+ *   target_logits [batch*n, vocab] dtype   verify rows' logits
+ *   candidates    [batch*n] i32            = draft_tokens of the tree build
+ *   retrieve_*    [batch, n] i32           from spec_build_tree
+ *   accept_width  = num_steps + 1 (columns of accept_index)
+ * For every row the target's choice is the first index of the row maximum.
+ * From the root the walk scans the children (first child, then siblings) for
+ * the candidate equal to the current row's choice, descends on a match and
+ * stops otherwise.  Outputs (all fully written):
+ *   predict       [batch*n] i32  on the path, row(node) holds the accepted
+ *                                child's token, the last node's row the
+ *                                target's choice (the terminal token);
+ *                                other rows 0
+ *   accept_index  [batch, accept_width] i32  verify rows of root and
+ *                                accepted nodes, then -1
+ *   accept_length [batch] i32    accepted drafts + 1
+ *   target_predict [batch*n] i32 (optional, NULL to skip) every row's choice
+ * A path that would exceed accept_width raises SPEC_ST_DEPTH and stops there.
+ * workspace: spec_accept_workspace_size(batch, n, vocab, 0) bytes.
+ * Logits must not be NaN.
+ */
+size_t spec_accept_workspace_size(int batch, int num_draft_tokens, int64_t vocab, int sampled);
+int spec_accept_greedy(int batch, int num_draft_tokens, int accept_width, int64_t vocab,
+                       int dtype, const void *target_logits, const int32_t *candidates,
+                       const int32_t *retrieve_index, const int32_t *retrieve_next_token,
+                       const int32_t *retrieve_next_sibling, int32_t *predict,
+                       int32_t *accept_index, int32_t *accept_length, int32_t *target_predict,
+                       void *workspace, size_t workspace_bytes, int32_t *dev_status,
+                       spec_stream_t stream);
+
+/*
+ * Rejection-sampled tree accept.  [P4] 接受/拒绝 and [P2] 四 (Classic
+ * Rejection Sampling); [P5] 5.6 (same walk, other test).
+ *
+ *   target_logits, draft_logits [batch*n, vocab] dtype; draft_logits NULL
+ *       -> SPEC_ERR_NULL (no proposal distribution, [P1] 三条判定路径)
+ *   temperature  [batch] f32 > 0, applied to both distributions
+ *   uniforms     [batch, n] f32 in [0,1): uniforms[b][k] tests node k
+ *   final_uniforms [batch] f32 in [0,1): the terminal draw
+ * At node cur the residual R starts as softmax(target_logits[row(cur)]/T);
+ * q = softmax(draft_logits[row(cur)]/T).  Children are tried in sibling
+ * order; child c with token t is accepted iff uniforms[b][c] < min(1,
+ * R(t)/q(t)).  A rejection sets R = max(0, R - q) / sum(max(0, R - q)) (left
+ * unchanged, with SPEC_ST_ZERO_RESIDUAL, if that sum is 0).  With no child
+ * accepted, or at a leaf, the terminal token is the smallest x whose
+ * cumulative R (vocabulary order) exceeds final_uniforms[b] * sum(R).
+ * Outputs as spec_accept_greedy.  Distribution statistics are fp32 sweeps
+ * with fp64 reductions; a decision closer than ~1e-6 to its threshold may
+ * differ from an exact evaluation.
+ * workspace: spec_accept_workspace_size(batch, n, vocab, 1) bytes.
+ */
+int spec_accept_sample(int batch, int num_draft_tokens, int accept_width, int64_t vocab,
+                       int dtype, const void *target_logits, const void *draft_logits,
+                       const float *temperature, const float *uniforms,
+                       const float *final_uniforms, const int32_t *candidates,
+                       const int32_t *retrieve_index, const int32_t *retrieve_next_token,
+                       const int32_t *retrieve_next_sibling, int32_t *predict,
+                       int32_t *accept_index, int32_t *accept_length, void *workspace,
+                       size_t workspace_bytes, int32_t *dev_status, spec_stream_t stream);
+
+/*
+ * Accepted-KV compaction.  [P1] KV 回写 (move_accept_tokens_to_target_kvcache)
+ * and [P2] 六: the verify rows in accept_index (root plus accepted drafts;
+ * the terminal token has no KV yet) move to the request's sequence positions
+ * L_b .. L_b + accept_length - 1.
+ *
+ *   k_pool, v_pool [num_layers, num_slots, num_kv_heads, head_dim] dtype,
+ *       updated in place; every source row is read before any target row
+ *       of the same request is written
+ *   page_table [batch, max_pages], seq_lens [batch]: as verify attention
+ *   out_cache_loc [batch*n] i32, accept_index [batch, accept_width] i32,
+ *   accept_length [batch] i32: as produced by the accept calls
+ * Outputs:
+ *   new_seq_lens [batch] i32  seq_lens + accept_length
+ *   free_slots   [batch*n] i32  request b's verify slots that are not a
+ *                target slot, ascending node order, from b*n; padded with -1
+ *   num_free     [batch] i32
+ * Entries of accept_index that are -1 are skipped; rows, slots or pages out
+ * of range raise SPEC_ST_RANGE and that row is not moved.  Requests must
+ * own disjoint slots.
+ */
+int spec_compact_kv(int batch, int num_draft_tokens, int accept_width, int num_layers,
+                    int num_kv_heads, int head_dim, int page_size, int dtype, void *k_pool,
+                    void *v_pool, int64_t num_slots, const int32_t *page_table, int max_pages,
+                    const int32_t *seq_lens, const int32_t *out_cache_loc,
+                    const int32_t *accept_index, const int32_t *accept_length,
+                    int32_t *new_seq_lens, int32_t *free_slots, int32_t *num_free,
+                    int32_t *dev_status, spec_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECMI_SPEC_H */

@@ -294,7 +294,7 @@ def softmax_t(logits_row: np.ndarray, temperature: float) -> np.ndarray:
 
 def accept_sample(target_logits, draft_logits, temperature, uniforms, final_uniforms,
                   candidates, retrieve_index, retrieve_next_token, retrieve_next_sibling,
-                  b, n, s1, dtype, band=1e-6):
+                  b, n, s1, dtype, band=1e-6, draw_band=2e-8):
     """[P4] 接受/拒绝 and [P2] 四 (Classic Rejection Sampling): at node cur
     the residual R starts as the target distribution p of row(cur); each child
     c (sibling order) with token t is accepted iff u[c] < min(1, R(t)/q(t)),
@@ -303,11 +303,15 @@ def accept_sample(target_logits, draft_logits, temperature, uniforms, final_unif
     the terminal token is drawn from R by inverse CDF with the request's final
     uniform.  [P5] 5.6: the walk is the greedy walk's.
 
-    Also returns, per request, the smallest margin to a decision boundary
-    (|u - min(1, ratio)| for each test, the final draw's distance to the
-    nearest CDF edge over the residual mass, and the residual masses):
-    a request with a margin below ``band`` may legitimately differ under
-    rounding.
+    Also returns, per request, how close each decision came to its
+    boundary: ``margin`` = smallest |u - min(1, ratio)| over the tests made
+    (and the smallest residual mass Z), ``draw_margin`` = the final uniform's
+    distance to the nearest CDF edge, relative to the residual mass.  A
+    request is ``exempt`` from bit-exact comparison when margin < ``band``
+    (the 1e-6 band stated for the ratio test) or draw_margin < ``draw_band``
+    (the terminal draw has no stated band; 2e-8 covers float32 evaluation of
+    the exponentials with float64 accumulation, whose CDF error stays below
+    about 5e-9 of the mass at vocabulary 128256).
     """
     tl = widen(target_logits, dtype)
     dl = widen(draft_logits, dtype)
@@ -316,6 +320,7 @@ def accept_sample(target_logits, draft_logits, temperature, uniforms, final_unif
     accept_index = np.full((b, s1), -1, np.int64)
     accept_length = np.zeros(b, np.int64)
     margin = np.full(b, np.inf)
+    draw_margin = np.full(b, np.inf)
     status = 0
     for r in range(b):
         T = float(temperature[r])
@@ -364,11 +369,12 @@ def accept_sample(target_logits, draft_logits, temperature, uniforms, final_unif
         cdf = np.cumsum(R)
         x = int(np.argmax(cdf > target)) if cdf[-1] > target else int(R.size - 1)
         lo = cdf[x - 1] if x > 0 else 0.0
-        margin[r] = min(margin[r], (target - lo) / total, (cdf[x] - target) / total)
+        draw_margin[r] = min((target - lo) / total, (cdf[x] - target) / total)
         predict[row] = x
         accept_length[r] = cnt + 1
     return dict(predict=predict, accept_index=accept_index, accept_length=accept_length,
-                margin=margin, exempt=margin < band, status=status)
+                margin=margin, draw_margin=draw_margin,
+                exempt=(margin < band) | (draw_margin < draw_band), status=status)
 
 
 # ---------------------------------------------------------------------------

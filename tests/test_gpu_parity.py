@@ -1,0 +1,274 @@
+"""Parity of the HIP path with the CPU oracle on the same seeded inputs.
+
+Integer outputs (tree build, greedy accept, compaction) must match bit for
+bit.  Sampled accept must match bit for bit except for requests whose
+oracle decision lies within 1e-6 of a threshold.  Attention must stay within
+a max relative error (per output vector, inf-norm) of 1e-5 for f32 and 2e-2
+for bf16.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import _gpu as G
+    import speculative_decoding_build_amd as S
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+ATTN_TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+SMALL = {
+    "c1": W.CONFIGS[1],
+    "c1_long_f32": W.shrink(W.CONFIGS[1], hist=("fixed", 500), vocab=1001),
+    "c2s": W.shrink(W.CONFIGS[2], hist=("fixed", 300), vocab=20000),
+    "c3s": W.shrink(W.CONFIGS[3], batch=3, hist=("uniform", 0, 400), vocab=9000),
+    "c4s": W.shrink(W.CONFIGS[4], batch=5, hist=("fixed", 130), vocab=17000),
+    "c5s": W.shrink(W.CONFIGS[5], batch=2, hist=("fixed", 700), vocab=8200),
+    "ps3_v1001": W.shrink(W.CONFIGS[3], batch=2, hist=("uniform", 50, 90), vocab=1001, page_size=3),
+    "root_only": W.shrink(W.CONFIGS[3], batch=2, hist=("fixed", 40), vocab=500, num_draft_tokens=1),
+    "d64_bf16": W.shrink(W.CONFIGS[3], batch=2, hist=("fixed", 200), vocab=700, head_dim=64),
+}
+
+_cache = {}
+
+
+def workload(name, seed=11):
+    key = (name, seed)
+    if key not in _cache:
+        cfg = SMALL[name] if name in SMALL else W.CONFIGS[int(name[-1])]
+        _cache.clear()
+        w = W.make_workload(cfg, seed)
+        t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                              cfg.num_steps, cfg.num_draft_tokens)
+        tl, dl = W.verify_logits(w, t["selected"])
+        _cache[key] = (w, t, tl, dl)
+    return _cache[key]
+
+
+def _tree_for_gpu(t, b, n):
+    return dict(draft_tokens=t["draft_tokens"].astype(np.int32),
+                retrieve_index=t["retrieve_index"].reshape(-1).astype(np.int32),
+                retrieve_next_token=t["retrieve_next_token"].reshape(-1).astype(np.int32),
+                retrieve_next_sibling=t["retrieve_next_sibling"].reshape(-1).astype(np.int32))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_build_tree_bit_exact(name):
+    w, t, _, _ = workload(name)
+    cfg = w.cfg
+    b, n = cfg.batch, cfg.num_draft_tokens
+    say(f"[build_tree] {name} b={b} topk={cfg.topk} S={cfg.num_steps} n={n}")
+    for mode in (S.SPEC_MASK_QLEN_BITS, S.SPEC_MASK_QLEN_U8):
+        g = G.build_tree(w, mode)
+        assert g["status"] == t["status"] == 0
+        np.testing.assert_array_equal(g["draft_tokens"], t["draft_tokens"])
+        np.testing.assert_array_equal(g["positions"], t["positions"])
+        np.testing.assert_array_equal(g["retrieve_index"].reshape(b, n), t["retrieve_index"])
+        np.testing.assert_array_equal(g["retrieve_next_token"].reshape(b, n), t["retrieve_next_token"])
+        np.testing.assert_array_equal(g["retrieve_next_sibling"].reshape(b, n), t["retrieve_next_sibling"])
+        if n > 1:
+            np.testing.assert_array_equal(g["selected"][:b * (n - 1)].reshape(b, n - 1), t["selected"])
+        np.testing.assert_array_equal(g["tree_mask"], oracle.pack_mask(t["mask"], mode))
+
+
+def _attn_err(got, ref):
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    return float((num / np.maximum(den, 1e-30)).max())
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_verify_attention_small(name):
+    w, t, _, _ = workload(name)
+    cfg = w.cfg
+    say(f"[attention] {name} b={cfg.batch} n={cfg.num_draft_tokens} hq={cfg.num_q_heads} "
+        f"hkv={cfg.num_kv_heads} d={cfg.head_dim} ps={cfg.page_size} L={w.seq_lens.tolist()}")
+    words = oracle.pack_mask(t["mask"], oracle.MASK_QLEN_BITS)
+    got, st = G.verify_attention(w, words)
+    assert st == 0
+    ref = oracle.verify_attention(w.q, w.k_pool[0], w.v_pool[0], w.page_table, w.seq_lens,
+                                  w.out_cache_loc, t["mask"], cfg.num_q_heads, cfg.num_kv_heads,
+                                  cfg.page_size, cfg.dtype)
+    err = _attn_err(got, ref)
+    say(f"    max rel err {err:.3e}")
+    assert err <= ATTN_TOL[cfg.dtype]
+
+
+def _compare_accept(g, o, b, n, exempt=None):
+    bad = []
+    for r in range(b):
+        if exempt is not None and exempt[r]:
+            continue
+        same = (g["accept_length"][r] == o["accept_length"][r]
+                and np.array_equal(g["accept_index"][r], o["accept_index"][r])
+                and np.array_equal(g["predict"][r * n:(r + 1) * n], o["predict"][r * n:(r + 1) * n]))
+        if not same:
+            bad.append(r)
+    return bad
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_accept_greedy_small(name):
+    w, t, tl, _ = workload(name)
+    cfg = w.cfg
+    b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
+    say(f"[greedy] {name} b={b} n={n} V={cfg.vocab}")
+    o = oracle.accept_greedy(tl, t["draft_tokens"], t["retrieve_index"], t["retrieve_next_token"],
+                             t["retrieve_next_sibling"], b, n, s1, cfg.dtype)
+    g = G.accept_greedy(w, tl, _tree_for_gpu(t, b, n))
+    assert g["status"] == o["status"] == 0
+    np.testing.assert_array_equal(g["target_predict"], o["target_predict"])
+    assert _compare_accept(g, o, b, n) == []
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_accept_sample_small(name):
+    w, t, tl, dl = workload(name)
+    cfg = w.cfg
+    b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
+    say(f"[sample] {name} b={b} n={n} V={cfg.vocab} T={cfg.temperature}")
+    o = oracle.accept_sample(tl, dl, w.temperature, w.uniforms, w.final_uniforms,
+                             t["draft_tokens"], t["retrieve_index"], t["retrieve_next_token"],
+                             t["retrieve_next_sibling"], b, n, s1, cfg.dtype)
+    g = G.accept_sample(w, tl, dl, _tree_for_gpu(t, b, n))
+    assert (g["status"] & ~S.SPEC_ST_ZERO_RESIDUAL) == 0
+    bad = _compare_accept(g, o, b, n, o["exempt"])
+    say(f"    exempt {int(o['exempt'].sum())}/{b}, mismatched {bad}")
+    assert bad == []
+
+
+@pytest.mark.parametrize("name", ["c1", "c3s", "c5s", "ps3_v1001"])
+@pytest.mark.parametrize("layers", [1, 3])
+def test_compact_kv_small(name, layers):
+    w, t, tl, _ = workload(name)
+    cfg = w.cfg
+    b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
+    say(f"[compact] {name} b={b} layers={layers}")
+    o_acc = oracle.accept_greedy(tl, t["draft_tokens"], t["retrieve_index"], t["retrieve_next_token"],
+                                 t["retrieve_next_sibling"], b, n, s1, cfg.dtype)
+    rng = np.random.default_rng(5)
+    shape = (layers,) + w.k_pool.shape[1:]
+    if cfg.dtype == "bf16":
+        kp = rng.integers(0, 2 ** 16, shape, dtype=np.uint16)
+        vp = rng.integers(0, 2 ** 16, shape, dtype=np.uint16)
+    else:
+        kp = rng.standard_normal(shape, dtype=np.float32)
+        vp = rng.standard_normal(shape, dtype=np.float32)
+    # force a long accepted path on request 0 to exercise overlapping moves
+    ai = o_acc["accept_index"].copy()
+    al = o_acc["accept_length"].copy()
+    o = oracle.compact_kv(kp, vp, w.page_table, w.seq_lens, w.out_cache_loc, ai, al, b, n,
+                          cfg.page_size)
+    g = G.compact_kv(cfg, kp, vp, w.page_table, w.seq_lens, w.out_cache_loc, ai, al)
+    assert g["status"] == o["status"] == 0
+    np.testing.assert_array_equal(g["new_seq_lens"], o["new_seq_lens"])
+    np.testing.assert_array_equal(g["num_free"], o["num_free"])
+    np.testing.assert_array_equal(g["free_slots"], o["free_slots"])
+    assert np.array_equal(g["k_pool"].view(np.uint8), o["k_pool"].view(np.uint8))
+    assert np.array_equal(g["v_pool"].view(np.uint8), o["v_pool"].view(np.uint8))
+
+
+def test_compact_kv_overlap_in_place():
+    """Accepted rows [0, 2, 3] of a request whose verify rows sit at its next
+    positions: sources and targets overlap."""
+    cfg = W.shrink(W.CONFIGS[1], batch=1, hist=("fixed", 4))
+    L, n = 4, cfg.num_draft_tokens
+    page_table = np.arange(L + n, dtype=np.int32)[None]
+    loc = np.arange(L, L + n, dtype=np.int32)
+    rng = np.random.default_rng(1)
+    kp = rng.standard_normal((2, L + n, 1, 64), dtype=np.float32)
+    vp = rng.standard_normal((2, L + n, 1, 64), dtype=np.float32)
+    ai = np.array([[0, 2, 3, -1]])
+    al = np.array([3])
+    o = oracle.compact_kv(kp, vp, page_table, np.array([L], np.int32), loc, ai, al, 1, n, 1)
+    g = G.compact_kv(cfg, kp, vp, page_table, np.array([L], np.int32), loc, ai, al)
+    assert np.array_equal(g["k_pool"], o["k_pool"]) and np.array_equal(g["v_pool"], o["v_pool"])
+    np.testing.assert_array_equal(g["free_slots"], o["free_slots"])
+
+
+def test_batch_zero_is_noop():
+    S.spec_build_tree(0, 2, 3, 6, S.SPEC_MASK_QLEN_BITS, *[torch.empty(0, device="cuda")] * 11)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (the shapes the benchmark times)
+# ---------------------------------------------------------------------------
+
+_full = {}
+
+
+def full(cid, attention):
+    key = (cid, attention)
+    if key not in _full:
+        _full.clear()
+        cfg = W.CONFIGS[cid]
+        w = W.make_workload(cfg, 1000 * cid + 1, attention=attention)
+        t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                              cfg.num_steps, cfg.num_draft_tokens)
+        _full[key] = (w, t)
+    return _full[key]
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_full_tree_and_accept(cid):
+    w, t = full(cid, False)
+    cfg = w.cfg
+    b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
+    say(f"[full tree+accept] cfg{cid} b={b} n={n} V={cfg.vocab}")
+    g = G.build_tree(w)
+    np.testing.assert_array_equal(g["draft_tokens"], t["draft_tokens"])
+    np.testing.assert_array_equal(g["tree_mask"], oracle.pack_mask(t["mask"], oracle.MASK_QLEN_BITS))
+    np.testing.assert_array_equal(g["retrieve_next_token"].reshape(b, n), t["retrieve_next_token"])
+    np.testing.assert_array_equal(g["retrieve_next_sibling"].reshape(b, n), t["retrieve_next_sibling"])
+    tl, dl = W.verify_logits(w, t["selected"])
+    tree = _tree_for_gpu(t, b, n)
+    if "greedy" in cfg.accept:
+        o = oracle.accept_greedy(tl, t["draft_tokens"], t["retrieve_index"], t["retrieve_next_token"],
+                                 t["retrieve_next_sibling"], b, n, s1, cfg.dtype)
+        gg = G.accept_greedy(w, tl, tree)
+        np.testing.assert_array_equal(gg["target_predict"], o["target_predict"])
+        assert _compare_accept(gg, o, b, n) == []
+        say(f"    greedy accept lengths {o['accept_length'].tolist()[:16]}")
+    if "sample" in cfg.accept:
+        o = oracle.accept_sample(tl, dl, w.temperature, w.uniforms, w.final_uniforms,
+                                 t["draft_tokens"], t["retrieve_index"], t["retrieve_next_token"],
+                                 t["retrieve_next_sibling"], b, n, s1, cfg.dtype)
+        gs = G.accept_sample(w, tl, dl, tree)
+        bad = _compare_accept(gs, o, b, n, o["exempt"])
+        say(f"    sample exempt {int(o['exempt'].sum())}/{b} mismatched {bad} "
+            f"lengths {o['accept_length'].tolist()[:16]}")
+        assert bad == []
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_full_attention_sampled_rows(cid):
+    w, t = full(cid, True)
+    cfg = w.cfg
+    b, n = cfg.batch, cfg.num_draft_tokens
+    say(f"[full attention] cfg{cid} b={b} n={n} L={w.seq_lens.tolist()[:8]}")
+    words = oracle.pack_mask(t["mask"], oracle.MASK_QLEN_BITS)
+    got, st = G.verify_attention(w, words)
+    assert st == 0
+    rng = np.random.default_rng(cid)
+    rows = [(int(rng.integers(0, b * n)), int(rng.integers(0, cfg.num_q_heads))) for _ in range(24)]
+    rows += [(b * n - 1, cfg.num_q_heads - 1), (0, 0)]
+    ref = oracle.verify_attention(w.q, w.k_pool[0], w.v_pool[0], w.page_table, w.seq_lens,
+                                  w.out_cache_loc, t["mask"], cfg.num_q_heads, cfg.num_kv_heads,
+                                  cfg.page_size, cfg.dtype, rows=rows)
+    sub = np.stack([got[r, h] for r, h in rows])
+    err = _attn_err(sub, ref)
+    say(f"    max rel err {err:.3e} over {len(rows)} sampled vectors")
+    assert err <= ATTN_TOL[cfg.dtype]
+    assert np.isfinite(got).all()
