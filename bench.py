@@ -1,0 +1,308 @@
+"""Benchmark of the tree speculative-decoding hot path on one MI355X.
+
+One step = one pass of every operation of the path over one batch of
+synthetic input: tree build -> verify attention -> greedy accept -> sampled
+accept -> accepted-KV compaction, all through the C-ABI library.  The
+default workload is the single-request Llama-3-8B-shaped tree (batch 1,
+topk 8, 5 steps, 64 draft tokens, 32 query / 8 KV heads, head dim 128, bf16
+KV, 4096 cached tokens, vocab 128256); ``--config`` picks another.
+
+Inputs are resident in HBM before timing starts.  Several copies of them are
+rotated through the steps so that each step reads cold memory (the 256 MB
+last-level cache cannot hold the rotation).  Per-operation times come from
+HIP events recorded on the stream the kernels run on.
+
+Prints one JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+import workloads as W
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+ROTATION_BYTES = 768 << 20     # rotate at least this many bytes of inputs
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(W.CONFIGS))
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    return ap.parse_args()
+
+
+class Inputs:
+    """One resident copy of every input of a step, plus its outputs."""
+
+    def __init__(self, torch, S, w, tl, dl):
+        cfg = w.cfg
+        d = lambda a: _dev(torch, a)
+        b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
+        self.scores, self.tokens, self.parents = d(w.scores), d(w.tokens), d(w.parents)
+        self.bonus, self.seq_lens = d(w.bonus), d(w.seq_lens)
+        self.q = d(w.q)
+        self.k_pool, self.v_pool = d(w.k_pool), d(w.v_pool)
+        self.page_table, self.out_cache_loc = d(w.page_table), d(w.out_cache_loc)
+        self.tl, self.dl = d(tl), d(dl)
+        self.temperature, self.uniforms, self.final_uniforms = (
+            d(w.temperature), d(w.uniforms), d(w.final_uniforms))
+        i32 = lambda k: torch.zeros(k, dtype=torch.int32, device="cuda")
+        self.draft_tokens, self.positions = i32(b * n), i32(b * n)
+        self.retrieve_index, self.retrieve_next_token, self.retrieve_next_sibling = (
+            i32(b * n), i32(b * n), i32(b * n))
+        self.selected = i32(max(1, b * (n - 1)))
+        self.tree_mask = torch.zeros(b * n * S.spec_mask_word_bytes(n), dtype=torch.uint8,
+                                     device="cuda")
+        self.attn_out = torch.empty_like(self.q)
+        self.predict, self.accept_index, self.accept_length = i32(b * n), i32(b * s1), i32(b)
+        self.target_predict = i32(b * n)
+        self.spredict, self.saccept_index, self.saccept_length = i32(b * n), i32(b * s1), i32(b)
+        self.new_seq_lens, self.free_slots, self.num_free = i32(b), i32(b * n), i32(b)
+        self.status = i32(1)
+
+    def clone(self, torch):
+        other = object.__new__(Inputs)
+        for k, v in self.__dict__.items():
+            other.__dict__[k] = v.clone()
+        return other
+
+    def nbytes(self):
+        return sum(v.numel() * v.element_size() for v in self.__dict__.values())
+
+
+def _dev(torch, a):
+    a = np.ascontiguousarray(a)
+    view = {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32,
+            np.dtype(np.uint64): np.int64}.get(a.dtype)
+    if view is not None:
+        a = a.view(view)
+    return torch.from_numpy(a).to("cuda")
+
+
+def run_ops(S, cfg, x, ws_attn, ws_greedy, ws_sample, events=None):
+    """Enqueue one step on the current stream.  ``events`` (optional) is a
+    list of 6 torch.cuda.Event recorded around the five operations."""
+    b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
+    code = S.SPEC_BF16 if cfg.dtype == "bf16" else S.SPEC_F32
+    rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+    rec(0)
+    S.spec_build_tree(b, cfg.topk, cfg.num_steps, n, S.SPEC_MASK_QLEN_BITS, x.scores, x.tokens,
+                      x.parents, x.bonus, x.seq_lens, x.draft_tokens, x.positions, x.tree_mask,
+                      x.retrieve_index, x.retrieve_next_token, x.retrieve_next_sibling,
+                      selected=x.selected, dev_status=x.status)
+    rec(1)
+    S.spec_verify_attention(b, n, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size,
+                            code, 0.0, x.q, x.k_pool, x.v_pool, x.k_pool.shape[1], x.page_table,
+                            x.page_table.shape[1], x.seq_lens, cfg_max_len(cfg), x.out_cache_loc,
+                            x.tree_mask, x.attn_out, workspace=ws_attn, dev_status=x.status)
+    rec(2)
+    S.spec_accept_greedy(b, n, s1, cfg.vocab, code, x.tl, x.draft_tokens, x.retrieve_index,
+                         x.retrieve_next_token, x.retrieve_next_sibling, x.predict,
+                         x.accept_index, x.accept_length, target_predict=x.target_predict,
+                         workspace=ws_greedy, dev_status=x.status)
+    rec(3)
+    S.spec_accept_sample(b, n, s1, cfg.vocab, code, x.tl, x.dl, x.temperature, x.uniforms,
+                         x.final_uniforms, x.draft_tokens, x.retrieve_index,
+                         x.retrieve_next_token, x.retrieve_next_sibling, x.spredict,
+                         x.saccept_index, x.saccept_length, workspace=ws_sample,
+                         dev_status=x.status)
+    rec(4)
+    ai, al = ((x.accept_index, x.accept_length) if "greedy" in cfg.accept
+              else (x.saccept_index, x.saccept_length))
+    S.spec_compact_kv(b, n, s1, x.k_pool.shape[0], cfg.num_kv_heads, cfg.head_dim, cfg.page_size,
+                      code, x.k_pool, x.v_pool, x.k_pool.shape[1], x.page_table,
+                      x.page_table.shape[1], x.seq_lens, x.out_cache_loc, ai, al, x.new_seq_lens,
+                      x.free_slots, x.num_free, dev_status=x.status)
+    rec(5)
+
+
+_MAXLEN = {}
+
+
+def cfg_max_len(cfg):
+    return _MAXLEN[cfg.name]
+
+
+OPS = ("build_tree", "verify_attention", "accept_greedy", "accept_sample", "compact_kv")
+
+
+def cpu_baseline(cfg, w, tl, dl, budget_s):
+    """The CPU oracle on the same host arrays, single BLAS thread.  Tree
+    build, both accepts and compaction run whole; attention runs on a subset
+    of (row, head) vectors sized to the time budget and is scaled to the
+    whole batch."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return _cpu_baseline(cfg, w, tl, dl, budget_s)
+
+
+def _cpu_baseline(cfg, w, tl, dl, budget_s):
+    import oracle
+    b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
+    t0 = time.perf_counter()
+    t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                          cfg.num_steps, n)
+    t_build = time.perf_counter() - t0
+    # attention: time a growing subset until the budget share is used
+    pairs_total = b * n * cfg.num_q_heads
+    rng = np.random.default_rng(0)
+    want = max(1, min(pairs_total, 8))
+    spent, done = 0.0, 0
+    while True:
+        rows = [(int(r), int(h)) for r, h in zip(rng.integers(0, b * n, want),
+                                                   rng.integers(0, cfg.num_q_heads, want))]
+        t0 = time.perf_counter()
+        oracle.verify_attention(w.q, w.k_pool[0], w.v_pool[0], w.page_table, w.seq_lens,
+                                w.out_cache_loc, t["mask"], cfg.num_q_heads, cfg.num_kv_heads,
+                                cfg.page_size, cfg.dtype, rows=rows)
+        spent += time.perf_counter() - t0
+        done += want
+        if spent > 0.5 * budget_s or done >= pairs_total:
+            break
+        want = min(pairs_total - done, want * 4)
+    t_attn = spent / done * pairs_total
+    t0 = time.perf_counter()
+    g = oracle.accept_greedy(tl, t["draft_tokens"], t["retrieve_index"], t["retrieve_next_token"],
+                             t["retrieve_next_sibling"], b, n, s1, cfg.dtype)
+    t_greedy = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.accept_sample(tl, dl, w.temperature, w.uniforms, w.final_uniforms, t["draft_tokens"],
+                         t["retrieve_index"], t["retrieve_next_token"], t["retrieve_next_sibling"],
+                         b, n, s1, cfg.dtype)
+    t_sample = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.compact_kv(w.k_pool, w.v_pool, w.page_table, w.seq_lens, w.out_cache_loc,
+                      g["accept_index"], g["accept_length"], b, n, cfg.page_size)
+    t_compact = time.perf_counter() - t0
+    total = t_build + t_attn + t_greedy + t_sample + t_compact
+    return {
+        "value": b * n / total,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"whole step except verify attention, which ran {done} of {pairs_total} "
+                   f"(row, head) vectors and was scaled up; float64 numpy, one thread"),
+        "op_seconds": {"build_tree": t_build, "verify_attention": t_attn,
+                       "accept_greedy": t_greedy, "accept_sample": t_sample,
+                       "compact_kv": t_compact},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path "
+              "shards by request and by KV head with no exchange, see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import speculative_decoding_build_amd as S
+
+    cfg = W.CONFIGS[args.config]
+    seed = args.seed if args.seed is not None else 1000 * args.config + 1
+    w = W.make_workload(cfg, seed)
+    _MAXLEN[cfg.name] = int(w.seq_lens.max())
+    b, n = cfg.batch, cfg.num_draft_tokens
+    code = S.SPEC_BF16 if cfg.dtype == "bf16" else S.SPEC_F32
+
+    torch.cuda.set_device(0)
+    # the verify rows' logits follow the tree the GPU builds from these lists
+    tl0 = np.zeros((b * n, cfg.vocab), np.uint16 if cfg.dtype == "bf16" else np.float32)
+    base = Inputs(torch, S, w, tl0, tl0)
+    ws_attn = torch.empty(max(1, S.spec_verify_attention_workspace_size(
+        b, n, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, _MAXLEN[cfg.name], code)),
+        dtype=torch.uint8, device="cuda")
+    ws_greedy = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
+                            device="cuda")
+    ws_sample = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
+                            device="cuda")
+    S.spec_build_tree(b, cfg.topk, cfg.num_steps, n, S.SPEC_MASK_QLEN_BITS, base.scores,
+                      base.tokens, base.parents, base.bonus, base.seq_lens, base.draft_tokens,
+                      base.positions, base.tree_mask, base.retrieve_index,
+                      base.retrieve_next_token, base.retrieve_next_sibling,
+                      selected=base.selected, dev_status=base.status)
+    sel = base.selected.cpu().numpy()[:b * (n - 1)].reshape(b, max(n - 1, 0))
+    tl, dl = W.verify_logits(w, sel)
+    base.tl, base.dl = _dev(torch, tl), _dev(torch, dl)
+
+    copies = max(1, min(16, math.ceil(ROTATION_BYTES / max(1, base.nbytes()))))
+    xs = [base] + [base.clone(torch) for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample)
+    torch.cuda.synchronize()
+    status = int(base.status.cpu()[0])
+
+    # timed region: K steps, events around every operation
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample, events=ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    op_ms = {op: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
+             for j, op in enumerate(OPS)}
+    step_ms = wall * 1e3 / args.steps
+
+    acc_len = base.accept_length.cpu().numpy() if "greedy" in cfg.accept else \
+        base.saccept_length.cpu().numpy()
+    attn_bytes = W.attention_bytes(cfg, w.seq_lens)
+    sweep_g = b * n * cfg.vocab * (2 if cfg.dtype == "bf16" else 4)
+    attn_gbs = attn_bytes / (op_ms["verify_attention"] * 1e-3) / 1e9
+    greedy_gbs = sweep_g / (op_ms["accept_greedy"] * 1e-3) / 1e9
+    sample_gbs = 2 * sweep_g / (op_ms["accept_sample"] * 1e-3) / 1e9
+    accept_op = "accept_greedy" if "greedy" in cfg.accept else "accept_sample"
+
+    line = {
+        "metric": "verified tree tokens/s (whole path per step)",
+        "value": b * n / (step_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": b, "topk": cfg.topk,
+                   "num_steps": cfg.num_steps, "num_draft_tokens": n, "vocab": cfg.vocab,
+                   "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "page_size": cfg.page_size,
+                   "cached_tokens": int(w.seq_lens.sum()), "temperature": cfg.temperature,
+                   "input_copies_rotated": copies},
+        "accept_steps_per_s": b / (op_ms[accept_op] * 1e-3),
+        "op_ms": op_ms,
+        "verify_attn_gbs": attn_gbs,
+        "verify_attn_frac_hbm": attn_gbs / HBM_PEAK_GBS,
+        "accept_sweep_gbs": {"greedy": greedy_gbs, "sample": sample_gbs},
+        "mean_accept_length": float(acc_len.mean()),
+        "dev_status": status,
+        "roofline": {"kernel": "spec_verify_attention (split-KV MFMA + merge launches)",
+                     "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": attn_bytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, w, tl, dl, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
