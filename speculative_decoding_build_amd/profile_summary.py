@@ -20,10 +20,16 @@ def summarize(db, title="", command=""):
     out.append("| kernel | launches | avg us | min us | max us | total us |")
     out.append("|---|---|---|---|---|---|")
     for name, cnt, avg, mn, mx, tot in rows:
-        short = name.split("(")[0].replace("void ", "").replace("(anonymous namespace)::", "")
-        if len(name.split("(")) > 1 and "<" in short and not short.endswith(">"):
-            short = name.split(">(")[0] + ">"
-            short = short.replace("void ", "").replace("(anonymous namespace)::", "")
+        short = name.replace("(anonymous namespace)::", "")
+        if short.startswith("void "):
+            short = short[5:]
+        depth = 0
+        for i, ch in enumerate(short):          # cut at the argument list
+            depth += ch == "<"
+            depth -= ch == ">"
+            if ch == "(" and depth == 0:
+                short = short[:i]
+                break
         out.append(f"| {short} | {cnt} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | "
                    f"{tot / 1e3:.1f} |")
     return "\n".join(out) + "\n"
