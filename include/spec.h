@@ -53,7 +53,9 @@ enum spec_status_bits {
     SPEC_ST_RANGE = 1,          /* an index (parent, row, slot, page) out of range  */
     SPEC_ST_NOT_CLOSED = 2,     /* a kept node's parent was not kept                */
     SPEC_ST_DEPTH = 4,          /* accepted path longer than accept_width           */
-    SPEC_ST_ZERO_RESIDUAL = 8   /* residual mass exactly zero (informational)       */
+    SPEC_ST_ZERO_RESIDUAL = 8,  /* residual mass exactly zero (informational)       */
+    SPEC_ST_SYNC = 16           /* a workgroup group barrier timed out; that call's
+                                   sampled outputs are unspecified                  */
 };
 
 enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 };

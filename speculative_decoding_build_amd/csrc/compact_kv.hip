@@ -29,53 +29,83 @@ __global__ __launch_bounds__(kThreads) void compact_kv_kernel(
     const int32_t *__restrict__ accept_length, int32_t *__restrict__ new_seq_lens,
     int32_t *__restrict__ free_slots, int32_t *__restrict__ num_free, int32_t *__restrict__ status) {
     __shared__ int64_t s_src[kMaxRows], s_tgt[kMaxRows];
-    __shared__ int s_m;
+    __shared__ int64_t s_jsrc[kMaxRows], s_jtgt[kMaxRows];
+    __shared__ int s_m, s_err, s_keep[kMaxRows + 1];
     __shared__ uint4 s_stage[kStageUnits];
     const int b = blockIdx.x;
     const int layer = blockIdx.y;
     const int tid = threadIdx.x;
     const int L = seq_lens[b];
-
-    if (tid == 0) {
-        int err = 0;
-        int m = accept_length[b];
-        if (m < 0) { m = 0; err |= SPEC_ST_RANGE; }
-        if (m > s1) { m = s1; err |= SPEC_ST_RANGE; }
-        int cnt = 0;
-        for (int j = 0; j < m; ++j) {
+    int acc = accept_length[b];
+    int err = 0;
+    if (acc < 0) { acc = 0; err |= SPEC_ST_RANGE; }
+    if (acc > s1) { acc = s1; err |= SPEC_ST_RANGE; }
+    if (tid == 0) s_err = 0;
+    __syncthreads();
+    // thread j resolves move j: source = verify slot of accepted row j,
+    // target = slot of sequence position L + j (-1 when skipped)
+    if (tid < s1) {
+        int64_t src = -1, tgt = -1;
+        const int j = tid;
+        if (j < acc) {
             const int row = accept_index[(int64_t)b * s1 + j];
-            if (row < 0) continue;
-            if (row >= total_rows) { err |= SPEC_ST_RANGE; continue; }
-            const int64_t src = out_cache_loc[row];
-            const int64_t pos = (int64_t)L + j;
-            const int64_t pidx = pos / page_size;
-            if (L < 0 || pidx >= max_pages) { err |= SPEC_ST_RANGE; continue; }
-            const int page = page_table[(int64_t)b * max_pages + pidx];
-            const int64_t tgt = (int64_t)page * page_size + pos % page_size;
-            if (src < 0 || src >= num_slots || page < 0 || tgt < 0 || tgt >= num_slots) {
-                err |= SPEC_ST_RANGE;
-                continue;
+            if (row >= 0) {
+                if (row >= total_rows) {
+                    err |= SPEC_ST_RANGE;
+                } else {
+                    const int64_t pos = (int64_t)L + j;
+                    const int64_t pidx = pos / page_size;
+                    if (L < 0 || pidx >= max_pages) {
+                        err |= SPEC_ST_RANGE;
+                    } else {
+                        const int page = page_table[(int64_t)b * max_pages + pidx];
+                        const int64_t s = out_cache_loc[row];
+                        const int64_t t = (int64_t)page * page_size + pos % page_size;
+                        if (s < 0 || s >= num_slots || page < 0 || t < 0 || t >= num_slots)
+                            err |= SPEC_ST_RANGE;
+                        else { src = s; tgt = t; }
+                    }
+                }
             }
-            s_src[cnt] = src;
-            s_tgt[cnt] = tgt;
-            ++cnt;
         }
+        s_jsrc[j] = src;
+        s_jtgt[j] = tgt;
+    }
+    if (err) atomicOr(&s_err, err);
+    __syncthreads();
+    if (tid == 0) {
+        int cnt = 0;
+        for (int j = 0; j < acc; ++j)
+            if (s_jsrc[j] >= 0) { s_src[cnt] = s_jsrc[j]; s_tgt[cnt] = s_jtgt[j]; ++cnt; }
         s_m = cnt;
-        if (layer == 0) {
-            new_seq_lens[b] = L + (accept_length[b] < 0 ? 0 : min(accept_length[b], s1));
-            int nf = 0;
-            for (int k = 0; k < n; ++k) {
-                const int slot = out_cache_loc[(int64_t)b * n + k];
-                bool kept = false;
-                for (int j = 0; j < cnt; ++j) kept |= (s_tgt[j] == slot);
-                if (!kept) free_slots[(int64_t)b * n + nf++] = slot;
-            }
-            for (int k = nf; k < n; ++k) free_slots[(int64_t)b * n + k] = -1;
-            num_free[b] = nf;
-            spec::raise_status(status, err);
-        }
     }
     __syncthreads();
+    if (layer == 0) {
+        // free list: verify slots of the request that did not become a target
+        const int cnt = s_m;
+        int kept = 1;
+        int slot = -1;
+        if (tid < n) {
+            slot = out_cache_loc[(int64_t)b * n + tid];
+            kept = 0;
+            for (int j = 0; j < cnt; ++j) kept |= (s_tgt[j] == slot);
+            s_keep[tid] = kept;
+        }
+        __syncthreads();
+        if (tid < n) {
+            int before = 0;
+            for (int k = 0; k < tid; ++k) before += 1 - s_keep[k];
+            if (!kept) free_slots[(int64_t)b * n + before] = slot;
+            int total_free = before + (1 - kept);
+            for (int k = tid + 1; k < n; ++k) total_free += 1 - s_keep[k];
+            if (tid >= total_free) free_slots[(int64_t)b * n + tid] = -1;
+            if (tid == 0) num_free[b] = total_free;
+        }
+        if (tid == 0) {
+            new_seq_lens[b] = L + acc;
+            spec::raise_status(status, s_err);
+        }
+    }
     const int m = s_m;
     if (m == 0) return;
     const int chunk = max(1, min(row16, kStageUnits / m));   // 16-byte units per row per pass

@@ -16,9 +16,20 @@
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kMaxCand = 4096;
 constexpr int kMaxNodes = 64;
+
+// Order key of a candidate: larger score first, then smaller flat index.
+// The float maps monotonically onto uint32 (+0 and -0 made equal), the
+// index goes in the low word complemented, so "beats" is one unsigned
+// 64-bit comparison.
+__device__ __forceinline__ uint64_t order_key(float s, int f) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)f);
+}
 
 __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     int topk, int n, int ncand, int npar, int mask_mode, int word_bytes,
@@ -28,11 +39,11 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     int32_t *__restrict__ positions, uint8_t *__restrict__ tree_mask,
     int32_t *__restrict__ r_index, int32_t *__restrict__ r_next, int32_t *__restrict__ r_sib,
     int32_t *__restrict__ selected, int32_t *__restrict__ status) {
-    __shared__ float s_score[kMaxCand];
+    __shared__ __attribute__((aligned(16))) uint64_t s_key[kMaxCand];
     __shared__ int16_t s_node[kMaxCand];       // flat index -> node (0 = not kept)
     __shared__ int32_t s_flat[kMaxNodes];      // node -> flat index
     __shared__ int32_t s_parent[kMaxNodes];
-    __shared__ int32_t s_wave_cnt[kThreads / SPEC_WAVE + 1];
+    __shared__ int32_t s_wave_cnt[kThreads / SPEC_WAVE];
 
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
@@ -41,49 +52,52 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     const int keep = n - 1;
     const float *sc = scores + (size_t)r * ncand;
 
-    for (int f = tid; f < ncand; f += kThreads) s_score[f] = sc[f];
+    for (int f = tid; f < ncand; f += kThreads) s_key[f] = order_key(sc[f], f);
     if (tid < kMaxNodes) s_flat[tid] = 0;
     __syncthreads();
 
-    // ---- rank each candidate; kept iff rank < n-1 -------------------------
-    // Threads own flat indices in contiguous runs so the prefix count below
-    // follows flat order: thread t owns [t*per, (t+1)*per).
-    const int per = (ncand + kThreads - 1) / kThreads;   // <= 16
-    uint32_t kept_bits = 0;                                // bit i: f = t*per + i kept
-    for (int i = 0; i < per; ++i) {
-        const int f = tid * per + i;
-        if (f >= ncand || keep == 0) break;
-        const float v = s_score[f];
-        int beats = 0;
-        for (int g = 0; g < ncand && beats < keep; ++g) {
-            const float w = s_score[g];
-            beats += (w > v) || (w == v && g < f);
+    // ---- kept iff fewer than n-1 candidates beat it; node index = 1 + number
+    // of kept candidates with a smaller flat index (rounds of kThreads
+    // candidates keep flat order: round i holds f = i*kThreads + tid)
+    const int ncand2 = ncand & ~1;
+    int before_rounds = 0;
+    for (int f0 = 0; f0 < ncand; f0 += kThreads) {
+        const int f = f0 + tid;
+        bool kept = false;
+        if (f < ncand && keep > 0) {
+            const uint64_t mine = s_key[f];
+            int beats = 0;
+            for (int g = 0; g < ncand2; g += 2) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(&s_key[g]);
+                const uint64_t k0 = ((uint64_t)w.y << 32) | w.x;
+                const uint64_t k1 = ((uint64_t)w.w << 32) | w.z;
+                beats += (k0 > mine) + (k1 > mine);
+            }
+            if (ncand2 != ncand) beats += s_key[ncand - 1] > mine;
+            kept = beats < keep;
         }
-        if (beats < keep) kept_bits |= 1u << i;
-    }
-    // ---- prefix count of kept candidates in flat order --------------------
-    const int my_cnt = __popc(kept_bits);
-    int incl = my_cnt;
-#pragma unroll
-    for (int o = 1; o < SPEC_WAVE; o <<= 1) {
-        int x = __shfl_up(incl, o, SPEC_WAVE);
-        if (lane >= o) incl += x;
-    }
-    if (lane == SPEC_WAVE - 1) s_wave_cnt[wave] = incl;
-    __syncthreads();
-    int before = incl - my_cnt;
-    for (int w = 0; w < wave; ++w) before += s_wave_cnt[w];
-    for (int i = 0; i < per; ++i) {
-        const int f = tid * per + i;
-        if (f >= ncand) break;
-        int node = 0;
-        if ((kept_bits & (1u << i)) && before < keep) {
-            node = ++before;                 // node index 1 .. n-1
-            s_flat[node] = f;
+        // block prefix count of kept flags in thread order
+        const uint64_t ball = __ballot(kept);
+        const int in_wave = __popcll(ball & ((1ull << lane) - 1ull));
+        if (lane == 0) s_wave_cnt[wave] = __popcll(ball);
+        __syncthreads();
+        int before = before_rounds + in_wave;
+        int round_total = 0;
+        for (int w = 0; w < kThreads / SPEC_WAVE; ++w) {
+            if (w < wave) before += s_wave_cnt[w];
+            round_total += s_wave_cnt[w];
         }
-        s_node[f] = static_cast<int16_t>(node);
+        if (f < ncand) {
+            int node = 0;
+            if (kept && before < keep) {
+                node = before + 1;               // node index 1 .. n-1
+                s_flat[node] = f;
+            }
+            s_node[f] = static_cast<int16_t>(node);
+        }
+        before_rounds += round_total;
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- per-node structure, one lane of wave 0 per node ------------------
     const int k = lane;

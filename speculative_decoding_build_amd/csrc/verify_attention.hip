@@ -28,6 +28,8 @@
 //     merge kernel combines them by log-sum-exp.  One split writes O directly.
 #include <math.h>
 
+#include <algorithm>
+
 #include "spec_common.h"
 
 namespace {
@@ -37,6 +39,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTileKeys = 64;
+constexpr int kTargetGroups = 1024;     // workgroups a launch aims for
+constexpr int kMinTiles = 4;            // 64-key tiles per split at least
 
 struct AttnParams {
     int batch, n, hq, hkv, group, rows;   // rows = n * group
@@ -85,11 +89,54 @@ __device__ __forceinline__ int64_t key_slot(const AttnParams &P, int b, int L, i
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA split kernel
+// work decomposition shared by the split kernels
 // ---------------------------------------------------------------------------
 
-template <int D, int NW, int QT>
-__global__ __launch_bounds__(NW * 64) void attn_split_mfma_kernel(AttnParams P) {
+struct Work {
+    int b, kvh, split, rg;
+};
+
+// Workgroup w of the 1-D grid -> (request, KV head, split, row group).  The
+// row groups of one split read the same K/V, so they are made neighbours in
+// the dispatch order of one XCD (workgroups go to the 8 XCDs round-robin by
+// id): XCD x takes the contiguous run of work items x*total/8 .. .
+__device__ __forceinline__ Work decode_work(const AttnParams &P, int w, bool xcd_remap) {
+    const int total = P.nsplit * P.rowgroups * P.hkv * P.batch;
+    int j = w;
+    if (xcd_remap) j = (w % 8) * (total / 8) + w / 8;
+    Work k;
+    k.rg = j % P.rowgroups;
+    j /= P.rowgroups;
+    k.split = j % P.nsplit;
+    j /= P.nsplit;
+    k.kvh = j % P.hkv;
+    k.b = j / P.hkv;
+    return k;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA split kernel
+// ---------------------------------------------------------------------------
+//
+// One workgroup: NW waves, each owning 32 query rows (one 32x32 MFMA column
+// block).  Per 64-key tile the pipeline is
+//     write tile t+1 (registers -> LDS, V transposed)
+//     issue the global loads of tile t+3 (slots read from LDS)
+//     look up the slots of tile t+4 (page table / tree slots, wave 0)
+//     compute tile t (S^T = K Q^T, softmax, O^T += V^T P^T)
+//     barrier
+// so two tiles of K/V are in flight while one is computed, and the page
+// table is read two tiles before the data it addresses.
+//
+// Softmax runs in the log2 domain on raw scores: p = exp2(s*C - m) with
+// C = scale*log2(e).  The running max m is raised (and O, l rescaled) only
+// when a score exceeds it by more than kLazy, so probabilities stay below
+// 2^kLazy and most tiles skip the rescale.
+
+constexpr float kLazy = 8.0f;
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams P, int xcd_remap) {
     static_assert(D == 64 || D == 128, "head_dim");
     constexpr int KS = D + 8;              // K row stride (bf16), 16-byte pad
     constexpr int VS = kTileKeys + 8;      // V^T row stride (bf16)
@@ -103,132 +150,118 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma_kernel(AttnParams P) 
 
     __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kTileKeys * KS];
     __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * VS];
+    __shared__ int64_t s_slot[2][kTileKeys];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int half = lane >> 5;            // 0 / 1
+    const int half = lane >> 5;
     const int col = lane & 31;
 
-    const int split = blockIdx.x / P.rowgroups;
-    const int rg = blockIdx.x % P.rowgroups;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
+    const Work wk = decode_work(P, blockIdx.x, xcd_remap != 0);
+    const int b = wk.b, kvh = wk.kvh, split = wk.split, rg = wk.rg;
     const int L = P.seq_lens[b];
     int err = 0;
     if (L < 0 || L > P.max_seq_len) {
         if (tid == 0 && split == 0 && rg == 0) spec::raise_status(P.status, SPEC_ST_RANGE);
         return;
     }
-    const int total_keys = L + P.n;
     const int kb = split * P.split_len;
-    const int ke = min(total_keys, kb + P.split_len);
+    const int ke = min(L + P.n, kb + P.split_len);
     if (kb >= ke) return;
+    const int ntiles = (ke - kb + kTileKeys - 1) / kTileKeys;
 
     // ---- query fragments (B operand of S^T = K Q^T) -----------------------
-    bf16x8 qf[QT][DK];
-    uint64_t mword[QT];
-    int qrho[QT];
+    const int rho = rg * P.rows_per_group + wave * 32 + col;
+    const bool wave_active = rg * P.rows_per_group + wave * 32 < P.rows;
+    bf16x8 qf[DK];
+    uint64_t mword = 0;
+    if (rho < P.rows) {
+        const int node = rho / P.group;
+        const int h = kvh * P.group + rho % P.group;
+        const __bf16 *qp = static_cast<const __bf16 *>(P.q) +
+                           (((int64_t)b * P.n + node) * P.hq + h) * D + 8 * half;
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-        const int rho = rg * P.rows_per_group + (wave * QT + t) * 32 + col;
-        qrho[t] = rho;
-        if (rho < P.rows) {
-            const int node = rho / P.group;
-            const int h = kvh * P.group + rho % P.group;
-            const __bf16 *qp = static_cast<const __bf16 *>(P.q) +
-                               (((int64_t)b * P.n + node) * P.hq + h) * D + 8 * half;
+        for (int kk = 0; kk < DK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8 *>(qp + kk * 16);
+        mword = load_mask_word(P.mask + ((int64_t)b * P.n + node) * P.word_bytes, P.word_bytes);
+    } else {
 #pragma unroll
-            for (int kk = 0; kk < DK; ++kk)
-                qf[t][kk] = *reinterpret_cast<const bf16x8 *>(qp + kk * 16);
-            mword[t] = load_mask_word(P.mask + ((int64_t)b * P.n + node) * P.word_bytes, P.word_bytes);
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < DK; ++kk) qf[t][kk] = bf16x8{};
-            mword[t] = 0;
-        }
+        for (int kk = 0; kk < DK; ++kk) qf[kk] = bf16x8{};
     }
 
-    floatx16 oacc[QT][DT];
-    float m_run[QT], l_run[QT];
+    floatx16 oacc[DT];
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-        m_run[t] = -INFINITY;
-        l_run[t] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[t][dt] = floatx16{};
-    }
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = floatx16{};
+    float m_run = -INFINITY;   // running max, log2 domain (already times C)
+    float l_run = 0.f;         // this lane-half's share of the softmax sum
+    const float C = P.scale_log2;
 
-    // ---- global -> register staging of one 64-key tile --------------------
-    uint4 kreg[KPER];
-    uint4 vreg[VPER][4];
     const __bf16 *kpool = static_cast<const __bf16 *>(P.k_pool);
     const __bf16 *vpool = static_cast<const __bf16 *>(P.v_pool);
 
-    auto fetch = [&](int tile_base) {
+    // slot of key position p of this request, -1 past the split or invalid
+    auto lookup = [&](int p) -> int64_t {
+        if (p >= ke) return -1;
+        return key_slot(P, b, L, p, err);
+    };
+
+    // ---- register staging: two tiles in flight, in two statically named sets
+    uint4 kreg0[KPER], kreg1[KPER];
+    uint4 vreg0[VPER][4], vreg1[VPER][4];
+    auto issue = [&](uint4 (&kr)[KPER], uint4 (&vr)[VPER][4], int stage_slot) {
+        const int64_t *sl = s_slot[stage_slot];
 #pragma unroll
         for (int i = 0; i < KPER; ++i) {
             const int u = tid + i * NT;
-            kreg[i] = make_uint4(0, 0, 0, 0);
+            kr[i] = make_uint4(0, 0, 0, 0);
             if (u < KUNITS) {
-                const int key = u / (D / 8), d8 = u % (D / 8);
-                const int p = tile_base + key;
-                if (p < ke) {
-                    const int64_t slot = key_slot(P, b, L, p, err);
-                    if (slot >= 0)
-                        kreg[i] = *reinterpret_cast<const uint4 *>(
-                            kpool + (slot * P.hkv + kvh) * D + d8 * 8);
-                }
+                const int64_t slot = sl[u / (D / 8)];
+                if (slot >= 0)
+                    kr[i] = *reinterpret_cast<const uint4 *>(
+                        kpool + (slot * P.hkv + kvh) * D + (u % (D / 8)) * 8);
             }
         }
 #pragma unroll
         for (int i = 0; i < VPER; ++i) {
             const int u = tid + i * NT;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vreg[i][j] = make_uint4(0, 0, 0, 0);
-            if (u < VUNITS) {
-                const int kq = u % (kTileKeys / 4), d8 = u / (kTileKeys / 4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int p = tile_base + kq * 4 + j;
-                    if (p < ke) {
-                        const int64_t slot = key_slot(P, b, L, p, err);
-                        if (slot >= 0)
-                            vreg[i][j] = *reinterpret_cast<const uint4 *>(
-                                vpool + (slot * P.hkv + kvh) * D + d8 * 8);
-                    }
+            for (int j = 0; j < 4; ++j) {
+                vr[i][j] = make_uint4(0, 0, 0, 0);
+                if (u < VUNITS) {
+                    const int64_t slot = sl[(u % (kTileKeys / 4)) * 4 + j];
+                    if (slot >= 0)
+                        vr[i][j] = *reinterpret_cast<const uint4 *>(
+                            vpool + (slot * P.hkv + kvh) * D + (u / (kTileKeys / 4)) * 8);
                 }
             }
         }
     };
-
-    auto stash = [&](int stage) {
+    auto word = [](const uint4 &v, int k) -> uint32_t {
+        return k == 0 ? v.x : (k == 1 ? v.y : (k == 2 ? v.z : v.w));
+    };
+    auto stash = [&](const uint4 (&kr)[KPER], const uint4 (&vr)[VPER][4], int stage) {
 #pragma unroll
         for (int i = 0; i < KPER; ++i) {
             const int u = tid + i * NT;
-            if (u < KUNITS) {
-                const int key = u / (D / 8), d8 = u % (D / 8);
-                *reinterpret_cast<uint4 *>(&k_lds[stage][key * KS + d8 * 8]) = kreg[i];
-            }
+            if (u < KUNITS)
+                *reinterpret_cast<uint4 *>(&k_lds[stage][(u / (D / 8)) * KS + (u % (D / 8)) * 8]) =
+                    kr[i];
         }
 #pragma unroll
         for (int i = 0; i < VPER; ++i) {
             const int u = tid + i * NT;
             if (u < VUNITS) {
                 const int kq = u % (kTileKeys / 4), d8 = u / (kTileKeys / 4);
-                // vreg[i][j] holds dims d8*8 .. d8*8+7 of key kq*4+j; write, for
-                // each dim, the 4 keys as one 8-byte run of V^T.
-                const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&vreg[i][0]);
-                const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&vreg[i][1]);
-                const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&vreg[i][2]);
-                const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&vreg[i][3]);
+                // vr[i][j] holds dims d8*8 .. +7 of key kq*4+j; write, per dim,
+                // its 4 keys as one 8-byte run of V^T
 #pragma unroll
-                for (int pr = 0; pr < 4; ++pr) {       // dim pair (2*pr, 2*pr+1)
-                    const uint32_t a = w0[pr], bb = w1[pr], c = w2[pr], d = w3[pr];
+                for (int pr = 0; pr < 4; ++pr) {
+                    const uint32_t a = word(vr[i][0], pr), bb = word(vr[i][1], pr);
+                    const uint32_t c = word(vr[i][2], pr), d = word(vr[i][3], pr);
                     uint2 lo, hi;
-                    lo.x = __builtin_amdgcn_perm(bb, a, 0x05040100u);   // keys 0,1 of dim 2pr
-                    lo.y = __builtin_amdgcn_perm(d, c, 0x05040100u);    // keys 2,3
-                    hi.x = __builtin_amdgcn_perm(bb, a, 0x07060302u);   // keys 0,1 of dim 2pr+1
+                    lo.x = __builtin_amdgcn_perm(bb, a, 0x05040100u);
+                    lo.y = __builtin_amdgcn_perm(d, c, 0x05040100u);
+                    hi.x = __builtin_amdgcn_perm(bb, a, 0x07060302u);
                     hi.y = __builtin_amdgcn_perm(d, c, 0x07060302u);
                     const int dim = d8 * 8 + 2 * pr;
                     *reinterpret_cast<uint2 *>(&vt_lds[stage][dim * VS + kq * 4]) = lo;
@@ -238,88 +271,120 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma_kernel(AttnParams P) 
         }
     };
 
-    const int ntiles = (ke - kb + kTileKeys - 1) / kTileKeys;
-    fetch(kb);
-    for (int it = 0; it < ntiles; ++it) {
-        const int stage = it & 1;
-        const int tile_base = kb + it * kTileKeys;
-        stash(stage);
-        __syncthreads();
-        if (it + 1 < ntiles) fetch(tile_base + kTileKeys);
+    // ---- prologue: tiles 0 and 1 loading, tile 0 in LDS, slots of tiles 2
+    // and 3 in the slot stages, tile 2 loading --------------------------------
+    if (tid < kTileKeys) {
+        s_slot[0][tid] = lookup(kb + tid);
+        s_slot[1][tid] = lookup(kb + kTileKeys + tid);
+    }
+    __syncthreads();
+    issue(kreg0, vreg0, 0);
+    if (ntiles > 1) issue(kreg1, vreg1, 1);
+    int64_t pending = -1;
+    if (tid < kTileKeys) pending = lookup(kb + 2 * kTileKeys + tid);
+    __syncthreads();
+    if (tid < kTileKeys) {
+        s_slot[0][tid] = pending;                                  // tile 2
+        pending = lookup(kb + 3 * kTileKeys + tid);
+    }
+    stash(kreg0, vreg0, 0);
+    __syncthreads();
+    if (ntiles > 2) issue(kreg0, vreg0, 0);                        // tile 2
+    if (tid < kTileKeys) s_slot[1][tid] = pending;                 // tile 3
+    __syncthreads();
 
-        const __bf16 *kt = k_lds[stage];
-        const __bf16 *vt = vt_lds[stage];
+    // one pipeline step; tile it+1 and it+3 live in the register set (kr, vr)
+    auto step = [&](int it, uint4 (&kr)[KPER], uint4 (&vr)[VPER][4]) {
+        const int tile_base = kb + it * kTileKeys;
+        // write tile it+1 (registers -> LDS stage (it+1)&1), then reuse its
+        // registers for tile it+3, whose slots sit in s_slot[(it+3)&1]
+        if (it + 1 < ntiles) stash(kr, vr, (it + 1) & 1);
+        if (it + 3 < ntiles) issue(kr, vr, (it + 3) & 1);
+        if (tid < kTileKeys) pending = lookup(tile_base + 4 * kTileKeys + tid);   // tile it+4
+
+        if (wave_active) {
+            const __bf16 *kt = k_lds[it & 1];
+            const __bf16 *vt = vt_lds[it & 1];
+            const bool edge = (tile_base + kTileKeys > ke) || (tile_base + kTileKeys > L);
 #pragma unroll
-        for (int sub = 0; sub < kTileKeys / 32; ++sub) {
-            // K operand rows: key sub*32 + col, dims 8*half .. of each k-step
-            bf16x8 kf[DK];
-#pragma unroll
-            for (int kk = 0; kk < DK; ++kk)
-                kf[kk] = *reinterpret_cast<const bf16x8 *>(&kt[(sub * 32 + col) * KS + kk * 16 + 8 * half]);
-            // V^T operand: dim dt*32 + col; keys 16s + 4*half + {0..3} and +8
-            bf16x8 vf[DT][2];
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const __bf16 *vp = &vt[(dt * 32 + col) * VS + sub * 32 + 16 * s + 4 * half];
-                    const uint2 x0 = *reinterpret_cast<const uint2 *>(vp);
-                    const uint2 x1 = *reinterpret_cast<const uint2 *>(vp + 8);
-                    uint4 w = make_uint4(x0.x, x0.y, x1.x, x1.y);
-                    vf[dt][s] = *reinterpret_cast<const bf16x8 *>(&w);
-                }
-#pragma unroll
-            for (int t = 0; t < QT; ++t) {
-                if (wave * QT * 32 + t * 32 + rg * P.rows_per_group >= P.rows) continue;
+            for (int sub = 0; sub < kTileKeys / 32; ++sub) {
                 floatx16 sacc = floatx16{};
 #pragma unroll
-                for (int kk = 0; kk < DK; ++kk)
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[t][kk], sacc, 0, 0, 0);
-                // scores of keys sub*32 + 8*(i/4) + 4*half + i%4 for query col
-                float s[16];
-                float mx = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int p = tile_base + sub * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                    float v = sacc[i] * P.scale_log2;
-                    if (p >= ke) v = -INFINITY;
-                    else if (p >= L && !((mword[t] >> (p - L)) & 1ull)) v = -INFINITY;
-                    s[i] = v;
-                    mx = fmaxf(mx, v);
+                for (int kk = 0; kk < DK; ++kk) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
+                        &kt[(sub * 32 + col) * KS + kk * 16 + 8 * half]);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc, 0, 0, 0);
                 }
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float m_new = fmaxf(m_run[t], mx);
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = exp2f(m_run[t] - m_use);
-                m_run[t] = m_new;
+                // lane holds keys sub*32 + 8*(i/4) + 4*half + i%4 of query col;
+                // masking is a branch-free select on a plain float copy
+                float sv[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
+                if (edge) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int p = tile_base + sub * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                        const int rel = p - L;
+                        const uint32_t sh = (uint32_t)max(rel, 0) & 63u;
+                        const bool bit = ((mword >> sh) & 1ull) != 0;
+                        const bool vis = (p < ke) & ((rel < 0) | bit);
+                        sv[i] = vis ? sv[i] : -INFINITY;
+                    }
+                }
+                float mx = sv[0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * C;
+                // lazy rescale: raise the running max only when it is exceeded
+                // by more than kLazy (decided per wave, applied per lane)
+                const bool raise = mx > m_run + kLazy;
+                if (__ballot(raise)) {
+                    const float m_new = raise ? mx : m_run;
+                    const float alpha = (m_new == m_run) ? 1.f : exp2f(m_run - m_new);
+                    l_run *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+                    m_run = m_new;
+                }
+                const float mneg = (m_run == -INFINITY) ? 0.f : -m_run;
                 float lsum = 0.f;
+                bf16x8 pf0, pf1;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    s[i] = exp2f(s[i] - m_use);
-                    lsum += s[i];
+                for (int i = 0; i < 8; ++i) {
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[i], C, mneg));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[8 + i], C, mneg));
+                    lsum += e0 + e1;
+                    pf0[i] = static_cast<__bf16>(e0);
+                    pf1[i] = static_cast<__bf16>(e1);
                 }
-                l_run[t] = l_run[t] * alpha + lsum;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) oacc[t][dt] *= alpha;
+                l_run += lsum;
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
-                    bf16x8 pf;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) pf[e] = static_cast<__bf16>(s[8 * st + e]);
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt)
-                        oacc[t][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][st], pf, oacc[t][dt], 0, 0, 0);
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const __bf16 *vp = &vt[(dt * 32 + col) * VS + sub * 32 + 16 * st + 4 * half];
+                        const uint2 x0 = *reinterpret_cast<const uint2 *>(vp);
+                        const uint2 x1 = *reinterpret_cast<const uint2 *>(vp + 8);
+                        const uint4 w = make_uint4(x0.x, x0.y, x1.x, x1.y);
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, w), st == 0 ? pf0 : pf1, oacc[dt], 0, 0, 0);
+                    }
                 }
             }
         }
+        // tile it+4's slots go to the stage tile it+2's slots left (read when
+        // tile it+2 was issued, one iteration ago)
+        if (tid < kTileKeys) s_slot[it & 1][tid] = pending;
+        __syncthreads();
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+        step(it, kreg1, vreg1);                  // even step: tiles it+1, it+3 use set 1
+        if (it + 1 < ntiles) step(it + 1, kreg0, vreg0);
     }
 
-    // ---- epilogue -----------------------------------------------------------
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-        const int rho = qrho[t];
-        const float l_tot = l_run[t] + __shfl_xor(l_run[t], 32, 64);
-        if (rho >= P.rows) continue;
+    // ---- epilogue -------------------------------------------------------------
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (rho < P.rows) {
         const int node = rho / P.group;
         const int h = kvh * P.group + rho % P.group;
         if (P.nsplit == 1) {
@@ -329,13 +394,13 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma_kernel(AttnParams P) 
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int j4 = 0; j4 < 4; ++j4) {
-                    const int d0 = dt * 32 + 8 * j4 + 4 * half;
-                    uint2 w;
-                    __bf16 v4[4];
+                    uint32_t h[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) v4[j] = static_cast<__bf16>(oacc[t][dt][4 * j4 + j] * inv);
-                    w = *reinterpret_cast<uint2 *>(v4);
-                    *reinterpret_cast<uint2 *>(op + d0) = w;
+                    for (int j = 0; j < 4; ++j)
+                        h[j] = __builtin_bit_cast(uint16_t,
+                                                  static_cast<__bf16>(oacc[dt][4 * j4 + j] * inv));
+                    *reinterpret_cast<uint2 *>(op + dt * 32 + 8 * j4 + 4 * half) =
+                        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
                 }
         } else {
             const int64_t pidx = (((int64_t)b * P.hkv + kvh) * P.nsplit + split) * P.rows + rho;
@@ -343,16 +408,13 @@ __global__ __launch_bounds__(NW * 64) void attn_split_mfma_kernel(AttnParams P) 
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const int d0 = dt * 32 + 8 * j4 + 4 * half;
-                    *reinterpret_cast<float4 *>(po + d0) =
-                        make_float4(oacc[t][dt][4 * j4 + 0], oacc[t][dt][4 * j4 + 1],
-                                    oacc[t][dt][4 * j4 + 2], oacc[t][dt][4 * j4 + 3]);
-                }
-            if (half == 0) P.part_ml[pidx] = make_float2(m_run[t], l_tot);
+                for (int j4 = 0; j4 < 4; ++j4)
+                    *reinterpret_cast<float4 *>(po + dt * 32 + 8 * j4 + 4 * half) =
+                        make_float4(oacc[dt][4 * j4 + 0], oacc[dt][4 * j4 + 1],
+                                    oacc[dt][4 * j4 + 2], oacc[dt][4 * j4 + 3]);
+            if (half == 0) P.part_ml[pidx] = make_float2(m_run, l_tot);
         }
     }
-    // status: one atomic per wave at most
     for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, 64);
     if (lane == 0) spec::raise_status(P.status, err);
 }
@@ -367,10 +429,8 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(AttnParams P) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int split = blockIdx.x / P.rowgroups;
-    const int rg = blockIdx.x % P.rowgroups;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
+    const Work wk = decode_work(P, blockIdx.x, false);
+    const int split = wk.split, rg = wk.rg, kvh = wk.kvh, b = wk.b;
     const int L = P.seq_lens[b];
     int err = 0;
     if (L < 0 || L > P.max_seq_len) {
@@ -481,7 +541,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
 // ---------------------------------------------------------------------------
 
 struct Plan {
-    int nw, qt;           // waves per workgroup, 32-query tiles per wave (bf16)
+    int nw;               // waves per workgroup (bf16: one 32-row query tile each)
     int rows_per_group, rowgroups;
     int split_len, nsplit;
 };
@@ -490,23 +550,20 @@ Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
     Plan pl{};
     const int rows = n * (hq / hkv);
     if (dtype == SPEC_BF16) {
-        if (rows <= 64) { pl.nw = 2; pl.qt = 1; }
-        else if (rows <= 128) { pl.nw = 4; pl.qt = 1; }
-        else { pl.nw = 4; pl.qt = 2; }      // 256 rows per workgroup
-        pl.rows_per_group = pl.nw * pl.qt * 32;
+        pl.nw = rows <= 128 ? 4 : 8;
+        pl.rows_per_group = pl.nw * 32;
     } else {
         pl.nw = 4;
-        pl.qt = 1;
         pl.rows_per_group = rows;
     }
     pl.rowgroups = (rows + pl.rows_per_group - 1) / pl.rows_per_group;
+    // split the key range so the grid has about kTargetGroups workgroups,
+    // with at least kMinTiles tiles per split
     const int keys = max_seq_len + n;
     const int tiles = (keys + kTileKeys - 1) / kTileKeys;
     const int base = batch * hkv * pl.rowgroups;
-    const int target = 1024;                       // workgroups to aim for
-    int ns = (target + base - 1) / base;
-    ns = min(ns, max(1, tiles / 2));               // at least two tiles per split
-    ns = max(ns, 1);
+    int ns = (kTargetGroups + base - 1) / base;
+    ns = std::max(1, std::min(ns, tiles / kMinTiles));
     const int tiles_per = (tiles + ns - 1) / ns;
     pl.split_len = tiles_per * kTileKeys;
     pl.nsplit = (keys + pl.split_len - 1) / pl.split_len;
@@ -521,13 +578,12 @@ size_t workspace_bytes_for(const Plan &pl, int batch, int n, int hq, int hkv, in
 }
 
 template <int D>
-void launch_mfma(const Plan &pl, const AttnParams &P, dim3 grid, hipStream_t st) {
-    if (pl.nw == 2)
-        hipLaunchKernelGGL((attn_split_mfma_kernel<D, 2, 1>), grid, dim3(128), 0, st, P);
-    else if (pl.nw == 4 && pl.qt == 1)
-        hipLaunchKernelGGL((attn_split_mfma_kernel<D, 4, 1>), grid, dim3(256), 0, st, P);
+void launch_mfma(const Plan &pl, const AttnParams &P, unsigned groups, hipStream_t st) {
+    const int remap = groups % 8 == 0 ? 1 : 0;
+    if (pl.nw == 4)
+        hipLaunchKernelGGL((attn_split_mfma_kernel<D, 4>), dim3(groups), dim3(256), 0, st, P, remap);
     else
-        hipLaunchKernelGGL((attn_split_mfma_kernel<D, 4, 2>), grid, dim3(256), 0, st, P);
+        hipLaunchKernelGGL((attn_split_mfma_kernel<D, 8>), dim3(groups), dim3(512), 0, st, P, remap);
 }
 
 }  // namespace
@@ -588,13 +644,13 @@ extern "C" int spec_verify_attention(int batch, int n, int hq, int hkv, int d, i
     P.status = dev_status;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const dim3 grid(pl.nsplit * pl.rowgroups, hkv, batch);
+    const unsigned groups = (unsigned)(pl.nsplit * pl.rowgroups * hkv * batch);
     if (dtype == SPEC_BF16) {
-        if (d == 128) launch_mfma<128>(pl, P, grid, st);
-        else launch_mfma<64>(pl, P, grid, st);
+        if (d == 128) launch_mfma<128>(pl, P, groups, st);
+        else launch_mfma<64>(pl, P, groups, st);
     } else {
-        if (d == 128) hipLaunchKernelGGL(attn_split_f32_kernel<128>, grid, dim3(256), 0, st, P);
-        else hipLaunchKernelGGL(attn_split_f32_kernel<64>, grid, dim3(256), 0, st, P);
+        if (d == 128) hipLaunchKernelGGL(attn_split_f32_kernel<128>, dim3(groups), dim3(256), 0, st, P);
+        else hipLaunchKernelGGL(attn_split_f32_kernel<64>, dim3(groups), dim3(256), 0, st, P);
     }
     if (pl.nsplit > 1) {
         const int64_t nvec = (int64_t)batch * n * hq;

@@ -39,6 +39,9 @@ SMALL = {
     "ps3_v1001": W.shrink(W.CONFIGS[3], batch=2, hist=("uniform", 50, 90), vocab=1001, page_size=3),
     "root_only": W.shrink(W.CONFIGS[3], batch=2, hist=("fixed", 40), vocab=500, num_draft_tokens=1),
     "d64_bf16": W.shrink(W.CONFIGS[3], batch=2, hist=("fixed", 200), vocab=700, head_dim=64),
+    # more requests than the cooperative walk can hold at once: one
+    # workgroup per request walks instead
+    "many_req": W.shrink(W.CONFIGS[4], batch=1100, hist=("fixed", 8), vocab=5000),
 }
 
 _cache = {}
