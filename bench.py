@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="before warm-up, run a plain device copy of this many MiB three times "
+                         "(the reference kernel for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -237,6 +240,15 @@ def main():
     sel = base.selected.cpu().numpy()[:b * (n - 1)].reshape(b, max(n - 1, 0))
     tl, dl = W.verify_logits(w, sel)
     base.tl, base.dl = _dev(torch, tl), _dev(torch, dl)
+
+    if args.calibrate_copy_mb > 0:
+        nbytes = args.calibrate_copy_mb << 20
+        src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     copies = max(1, min(16, math.ceil(ROTATION_BYTES / max(1, base.nbytes()))))
     xs = [base] + [base.clone(torch) for _ in range(copies - 1)]
