@@ -9,8 +9,15 @@ KV, 4096 cached tokens, vocab 128256); ``--config`` picks another.
 
 Inputs are resident in HBM before timing starts.  Several copies of them are
 rotated through the steps so that each step reads cold memory (the 256 MB
-last-level cache cannot hold the rotation).  Per-operation times come from
-HIP events recorded on the stream the kernels run on.
+last-level cache cannot hold the rotation).
+
+Timing.  ``--mode graph`` (default) captures each copy's step once into a
+HIP graph and times K replays, so the GPU runs the step's kernels back to
+back as a serving loop would; ``--mode eager`` times K steps launched from
+Python.  Either way the line also carries the eager step time and, per
+operation, the GPU time of that operation alone: a graph holding the
+operation for every copy, replayed between two HIP events on the stream the
+kernels run on.
 
 Prints one JSON line (rank 0).
 """
@@ -41,6 +48,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
+                    help="graph: each input copy's step is captured once into a HIP graph and "
+                         "the timed steps replay the graphs (no host launch cost between "
+                         "kernels); eager: every step is launched from Python")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="before warm-up, run a plain device copy of this many MiB three times "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -95,41 +106,53 @@ def _dev(torch, a):
     return torch.from_numpy(a).to("cuda")
 
 
-def run_ops(S, cfg, x, ws_attn, ws_greedy, ws_sample, events=None):
-    """Enqueue one step on the current stream.  ``events`` (optional) is a
-    list of 6 torch.cuda.Event recorded around the five operations."""
+def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample):
+    """The five operations of one step on input copy ``x``, as callables that
+    enqueue their kernels on the current stream."""
     b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
     code = S.SPEC_BF16 if cfg.dtype == "bf16" else S.SPEC_F32
-    rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
-    rec(0)
-    S.spec_build_tree(b, cfg.topk, cfg.num_steps, n, S.SPEC_MASK_QLEN_BITS, x.scores, x.tokens,
-                      x.parents, x.bonus, x.seq_lens, x.draft_tokens, x.positions, x.tree_mask,
-                      x.retrieve_index, x.retrieve_next_token, x.retrieve_next_sibling,
-                      selected=x.selected, dev_status=x.status)
-    rec(1)
-    S.spec_verify_attention(b, n, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size,
-                            code, 0.0, x.q, x.k_pool, x.v_pool, x.k_pool.shape[1], x.page_table,
-                            x.page_table.shape[1], x.seq_lens, cfg_max_len(cfg), x.out_cache_loc,
-                            x.tree_mask, x.attn_out, workspace=ws_attn, dev_status=x.status)
-    rec(2)
-    S.spec_accept_greedy(b, n, s1, cfg.vocab, code, x.tl, x.draft_tokens, x.retrieve_index,
-                         x.retrieve_next_token, x.retrieve_next_sibling, x.predict,
-                         x.accept_index, x.accept_length, target_predict=x.target_predict,
-                         workspace=ws_greedy, dev_status=x.status)
-    rec(3)
-    S.spec_accept_sample(b, n, s1, cfg.vocab, code, x.tl, x.dl, x.temperature, x.uniforms,
-                         x.final_uniforms, x.draft_tokens, x.retrieve_index,
-                         x.retrieve_next_token, x.retrieve_next_sibling, x.spredict,
-                         x.saccept_index, x.saccept_length, workspace=ws_sample,
-                         dev_status=x.status)
-    rec(4)
-    ai, al = ((x.accept_index, x.accept_length) if "greedy" in cfg.accept
-              else (x.saccept_index, x.saccept_length))
-    S.spec_compact_kv(b, n, s1, x.k_pool.shape[0], cfg.num_kv_heads, cfg.head_dim, cfg.page_size,
-                      code, x.k_pool, x.v_pool, x.k_pool.shape[1], x.page_table,
-                      x.page_table.shape[1], x.seq_lens, x.out_cache_loc, ai, al, x.new_seq_lens,
-                      x.free_slots, x.num_free, dev_status=x.status)
-    rec(5)
+
+    def build():
+        S.spec_build_tree(b, cfg.topk, cfg.num_steps, n, S.SPEC_MASK_QLEN_BITS, x.scores,
+                          x.tokens, x.parents, x.bonus, x.seq_lens, x.draft_tokens, x.positions,
+                          x.tree_mask, x.retrieve_index, x.retrieve_next_token,
+                          x.retrieve_next_sibling, selected=x.selected, dev_status=x.status)
+
+    def attention():
+        S.spec_verify_attention(b, n, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                                cfg.page_size, code, 0.0, x.q, x.k_pool, x.v_pool,
+                                x.k_pool.shape[1], x.page_table, x.page_table.shape[1],
+                                x.seq_lens, cfg_max_len(cfg), x.out_cache_loc, x.tree_mask,
+                                x.attn_out, workspace=ws_attn, dev_status=x.status)
+
+    def greedy():
+        S.spec_accept_greedy(b, n, s1, cfg.vocab, code, x.tl, x.draft_tokens, x.retrieve_index,
+                             x.retrieve_next_token, x.retrieve_next_sibling, x.predict,
+                             x.accept_index, x.accept_length, target_predict=x.target_predict,
+                             workspace=ws_greedy, dev_status=x.status)
+
+    def sample():
+        S.spec_accept_sample(b, n, s1, cfg.vocab, code, x.tl, x.dl, x.temperature, x.uniforms,
+                             x.final_uniforms, x.draft_tokens, x.retrieve_index,
+                             x.retrieve_next_token, x.retrieve_next_sibling, x.spredict,
+                             x.saccept_index, x.saccept_length, workspace=ws_sample,
+                             dev_status=x.status)
+
+    def compact():
+        ai, al = ((x.accept_index, x.accept_length) if "greedy" in cfg.accept
+                  else (x.saccept_index, x.saccept_length))
+        S.spec_compact_kv(b, n, s1, x.k_pool.shape[0], cfg.num_kv_heads, cfg.head_dim,
+                          cfg.page_size, code, x.k_pool, x.v_pool, x.k_pool.shape[1],
+                          x.page_table, x.page_table.shape[1], x.seq_lens, x.out_cache_loc, ai,
+                          al, x.new_seq_lens, x.free_slots, x.num_free, dev_status=x.status)
+
+    return [build, attention, greedy, sample, compact]
+
+
+def run_ops(S, cfg, x, ws_attn, ws_greedy, ws_sample):
+    """Enqueue one step on the current stream."""
+    for f in op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample):
+        f()
 
 
 _MAXLEN = {}
@@ -257,19 +280,75 @@ def main():
     for i in range(args.warmup):
         run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample)
     torch.cuda.synchronize()
-    status = int(base.status.cpu()[0])
 
-    # timed region: K steps, events around every operation
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # per-operation GPU times: one graph per operation holding that operation
+    # for every input copy back to back, replayed between two events, so no
+    # host time falls between the launches
+    calls = [op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample) for x in xs]
+    reps = max(2, math.ceil(64 / copies))
+    op_ms = {}
+    for j, op in enumerate(OPS):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c[j]()
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        op_ms[op] = e0.elapsed_time(e1) / (reps * copies)
+        del g
+
+    # eager steps (every launch from Python)
+    k_e = max(5, min(args.steps, 20))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(k_e):
+        run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / k_e
+
+    graph_check = None
+    if args.mode == "graph":
+        # one whole-step graph per input copy; the tree and accept outputs of a
+        # replay must equal those of an eager step on the same copy (they do
+        # not depend on the KV state that compaction changes)
+        keys = ("draft_tokens", "retrieve_index", "retrieve_next_token", "retrieve_next_sibling",
+                "predict", "accept_index", "accept_length", "spredict", "saccept_index",
+                "saccept_length")
+        run_ops(S, cfg, xs[0], ws_attn, ws_greedy, ws_sample)
+        torch.cuda.synchronize()
+        ref = {k: getattr(xs[0], k).clone() for k in keys}
+        for k in keys:
+            getattr(xs[0], k).fill_(-9)
+        graphs = []
+        for x in xs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_ops(S, cfg, x, ws_attn, ws_greedy, ws_sample)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        graph_check = all(torch.equal(ref[k], getattr(xs[0], k)) for k in keys)
+        step = lambda i: graphs[i % copies].replay()
+    else:
+        step = lambda i: run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample)
+
+    # timed region: K steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample, events=ev[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    op_ms = {op: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
-             for j, op in enumerate(OPS)}
     step_ms = wall * 1e3 / args.steps
+    status = int(base.status.cpu()[0])
 
     acc_len = base.accept_length.cpu().numpy() if "greedy" in cfg.accept else \
         base.saccept_length.cpu().numpy()
@@ -299,6 +378,9 @@ def main():
                    "head_dim": cfg.head_dim, "page_size": cfg.page_size,
                    "cached_tokens": int(w.seq_lens.sum()), "temperature": cfg.temperature,
                    "input_copies_rotated": copies},
+        "mode": args.mode,
+        "graph_replay_matches_eager": graph_check,
+        "ms_per_step_eager": eager_ms,
         "accept_steps_per_s": b / (op_ms[accept_op] * 1e-3),
         "op_ms": op_ms,
         "verify_attn_gbs": attn_gbs,

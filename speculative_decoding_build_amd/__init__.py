@@ -94,22 +94,30 @@ def _check(call, rc):
 _ELEM = {SPEC_F32: 4, SPEC_BF16: 2}
 
 
-def _ptr(t, what, *, nbytes=None, optional=False):
+def _device():
+    """Index of the current GPU; ValueError when there is none (the calls
+    take device tensors only)."""
+    try:
+        return torch.cuda.current_device()
+    except (RuntimeError, AssertionError) as e:
+        raise ValueError(f"no usable GPU: {e}") from None
+
+
+def _ptr(t, what, dev, *, nbytes=None, optional=False):
     """Device pointer of tensor ``t`` after checking it is a contiguous tensor
-    on the current GPU with at least ``nbytes`` bytes."""
+    on GPU ``dev`` (the current one) with at least ``nbytes`` bytes."""
     if t is None:
         if optional:
             return None
         raise ValueError(f"{what}: tensor required")
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what}: expected a torch.Tensor")
-    if not t.is_cuda or t.device.index != torch.cuda.current_device():
+    if t.get_device() != dev:
         raise ValueError(f"{what}: must be on the current GPU (got {t.device})")
     if not t.is_contiguous():
         raise ValueError(f"{what}: must be contiguous")
-    have = t.numel() * t.element_size()
-    if nbytes is not None and have < nbytes:
-        raise ValueError(f"{what}: {have} bytes, the call needs {nbytes}")
+    if nbytes is not None and t.nbytes < nbytes:
+        raise ValueError(f"{what}: {t.nbytes} bytes, the call needs {nbytes}")
     return t.data_ptr() if t.numel() else None
 
 
@@ -134,25 +142,26 @@ def spec_build_tree(batch, topk, num_steps, num_draft_tokens, mask_mode, scores,
                     parents, bonus, seq_lens, draft_tokens, positions, tree_mask,
                     retrieve_index, retrieve_next_token, retrieve_next_sibling,
                     selected=None, dev_status=None, stream=None):
+    dev = _device()
     n = num_draft_tokens
     ncand = topk + (num_steps - 1) * topk * topk
     npar = 1 + (num_steps - 1) * topk
     bn = batch * n
     mbytes = batch * n * (n if mask_mode == SPEC_MASK_QLEN_U8 else max(1, spec_mask_word_bytes(n)))
     args = [
-        _ptr(scores, "scores", nbytes=batch * ncand * 4),
-        _ptr(tokens, "tokens", nbytes=batch * ncand * 4),
-        _ptr(parents, "parents", nbytes=batch * npar * 4, optional=num_steps == 1),
-        _ptr(bonus, "bonus", nbytes=batch * 4),
-        _ptr(seq_lens, "seq_lens", nbytes=batch * 4),
-        _ptr(draft_tokens, "draft_tokens", nbytes=bn * 4),
-        _ptr(positions, "positions", nbytes=bn * 4),
-        _ptr(tree_mask, "tree_mask", nbytes=mbytes),
-        _ptr(retrieve_index, "retrieve_index", nbytes=bn * 4),
-        _ptr(retrieve_next_token, "retrieve_next_token", nbytes=bn * 4),
-        _ptr(retrieve_next_sibling, "retrieve_next_sibling", nbytes=bn * 4),
-        _ptr(selected, "selected", nbytes=batch * (n - 1) * 4, optional=True),
-        _ptr(dev_status, "dev_status", nbytes=4, optional=True),
+        _ptr(scores, "scores", dev, nbytes=batch * ncand * 4),
+        _ptr(tokens, "tokens", dev, nbytes=batch * ncand * 4),
+        _ptr(parents, "parents", dev, nbytes=batch * npar * 4, optional=num_steps == 1),
+        _ptr(bonus, "bonus", dev, nbytes=batch * 4),
+        _ptr(seq_lens, "seq_lens", dev, nbytes=batch * 4),
+        _ptr(draft_tokens, "draft_tokens", dev, nbytes=bn * 4),
+        _ptr(positions, "positions", dev, nbytes=bn * 4),
+        _ptr(tree_mask, "tree_mask", dev, nbytes=mbytes),
+        _ptr(retrieve_index, "retrieve_index", dev, nbytes=bn * 4),
+        _ptr(retrieve_next_token, "retrieve_next_token", dev, nbytes=bn * 4),
+        _ptr(retrieve_next_sibling, "retrieve_next_sibling", dev, nbytes=bn * 4),
+        _ptr(selected, "selected", dev, nbytes=batch * (n - 1) * 4, optional=True),
+        _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
     ]
     _check("spec_build_tree", _lib.spec_build_tree(batch, topk, num_steps, n, mask_mode, *args,
                                                     _stream(stream)))
@@ -168,6 +177,7 @@ def spec_verify_attention(batch, num_draft_tokens, num_q_heads, num_kv_heads, he
                           page_size, dtype, sm_scale, q, k_pool, v_pool, num_slots, page_table,
                           max_pages, seq_lens, max_seq_len, out_cache_loc, tree_mask, out,
                           workspace=None, workspace_bytes=None, dev_status=None, stream=None):
+    dev = _device()
     n = num_draft_tokens
     eb = _ELEM.get(dtype, 4)
     qbytes = batch * n * num_q_heads * head_dim * eb
@@ -177,21 +187,21 @@ def spec_verify_attention(batch, num_draft_tokens, num_q_heads, num_kv_heads, he
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [
-        _ptr(q, "q", nbytes=qbytes),
-        _ptr(k_pool, "k_pool", nbytes=pool),
-        _ptr(v_pool, "v_pool", nbytes=pool),
+        _ptr(q, "q", dev, nbytes=qbytes),
+        _ptr(k_pool, "k_pool", dev, nbytes=pool),
+        _ptr(v_pool, "v_pool", dev, nbytes=pool),
     ]
     args2 = [
-        _ptr(page_table, "page_table", nbytes=batch * max_pages * 4, optional=max_seq_len == 0),
+        _ptr(page_table, "page_table", dev, nbytes=batch * max_pages * 4, optional=max_seq_len == 0),
         max_pages,
-        _ptr(seq_lens, "seq_lens", nbytes=batch * 4),
+        _ptr(seq_lens, "seq_lens", dev, nbytes=batch * 4),
         max_seq_len,
-        _ptr(out_cache_loc, "out_cache_loc", nbytes=batch * n * 4),
-        _ptr(tree_mask, "tree_mask", nbytes=batch * n * max(1, spec_mask_word_bytes(n))),
-        _ptr(out, "out", nbytes=qbytes),
-        _ptr(workspace, "workspace", nbytes=need_ws, optional=need_ws == 0),
+        _ptr(out_cache_loc, "out_cache_loc", dev, nbytes=batch * n * 4),
+        _ptr(tree_mask, "tree_mask", dev, nbytes=batch * n * max(1, spec_mask_word_bytes(n))),
+        _ptr(out, "out", dev, nbytes=qbytes),
+        _ptr(workspace, "workspace", dev, nbytes=need_ws, optional=need_ws == 0),
         workspace_bytes,
-        _ptr(dev_status, "dev_status", nbytes=4, optional=True),
+        _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
     ]
     _check("spec_verify_attention", _lib.spec_verify_attention(
         batch, n, num_q_heads, num_kv_heads, head_dim, page_size, dtype, float(sm_scale), *args,
@@ -206,24 +216,25 @@ def spec_accept_greedy(batch, num_draft_tokens, accept_width, vocab, dtype, targ
                        candidates, retrieve_index, retrieve_next_token, retrieve_next_sibling,
                        predict, accept_index, accept_length, target_predict=None,
                        workspace=None, workspace_bytes=None, dev_status=None, stream=None):
+    dev = _device()
     n = num_draft_tokens
     bn = batch * n
     need_ws = spec_accept_workspace_size(batch, n, vocab, 0)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [
-        _ptr(target_logits, "target_logits", nbytes=bn * vocab * _ELEM.get(dtype, 4)),
-        _ptr(candidates, "candidates", nbytes=bn * 4),
-        _ptr(retrieve_index, "retrieve_index", nbytes=bn * 4),
-        _ptr(retrieve_next_token, "retrieve_next_token", nbytes=bn * 4),
-        _ptr(retrieve_next_sibling, "retrieve_next_sibling", nbytes=bn * 4),
-        _ptr(predict, "predict", nbytes=bn * 4),
-        _ptr(accept_index, "accept_index", nbytes=batch * accept_width * 4),
-        _ptr(accept_length, "accept_length", nbytes=batch * 4),
-        _ptr(target_predict, "target_predict", nbytes=bn * 4, optional=True),
-        _ptr(workspace, "workspace", nbytes=need_ws, optional=batch == 0),
+        _ptr(target_logits, "target_logits", dev, nbytes=bn * vocab * _ELEM.get(dtype, 4)),
+        _ptr(candidates, "candidates", dev, nbytes=bn * 4),
+        _ptr(retrieve_index, "retrieve_index", dev, nbytes=bn * 4),
+        _ptr(retrieve_next_token, "retrieve_next_token", dev, nbytes=bn * 4),
+        _ptr(retrieve_next_sibling, "retrieve_next_sibling", dev, nbytes=bn * 4),
+        _ptr(predict, "predict", dev, nbytes=bn * 4),
+        _ptr(accept_index, "accept_index", dev, nbytes=batch * accept_width * 4),
+        _ptr(accept_length, "accept_length", dev, nbytes=batch * 4),
+        _ptr(target_predict, "target_predict", dev, nbytes=bn * 4, optional=True),
+        _ptr(workspace, "workspace", dev, nbytes=need_ws, optional=batch == 0),
         workspace_bytes,
-        _ptr(dev_status, "dev_status", nbytes=4, optional=True),
+        _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
     ]
     _check("spec_accept_greedy", _lib.spec_accept_greedy(batch, n, accept_width, vocab, dtype,
                                                           *args, _stream(stream)))
@@ -234,6 +245,7 @@ def spec_accept_sample(batch, num_draft_tokens, accept_width, vocab, dtype, targ
                        retrieve_index, retrieve_next_token, retrieve_next_sibling, predict,
                        accept_index, accept_length, workspace=None, workspace_bytes=None,
                        dev_status=None, stream=None):
+    dev = _device()
     n = num_draft_tokens
     bn = batch * n
     lb = bn * vocab * _ELEM.get(dtype, 4)
@@ -241,21 +253,21 @@ def spec_accept_sample(batch, num_draft_tokens, accept_width, vocab, dtype, targ
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [
-        _ptr(target_logits, "target_logits", nbytes=lb),
-        _ptr(draft_logits, "draft_logits", nbytes=lb, optional=True),
-        _ptr(temperature, "temperature", nbytes=batch * 4),
-        _ptr(uniforms, "uniforms", nbytes=bn * 4),
-        _ptr(final_uniforms, "final_uniforms", nbytes=batch * 4),
-        _ptr(candidates, "candidates", nbytes=bn * 4),
-        _ptr(retrieve_index, "retrieve_index", nbytes=bn * 4),
-        _ptr(retrieve_next_token, "retrieve_next_token", nbytes=bn * 4),
-        _ptr(retrieve_next_sibling, "retrieve_next_sibling", nbytes=bn * 4),
-        _ptr(predict, "predict", nbytes=bn * 4),
-        _ptr(accept_index, "accept_index", nbytes=batch * accept_width * 4),
-        _ptr(accept_length, "accept_length", nbytes=batch * 4),
-        _ptr(workspace, "workspace", nbytes=need_ws, optional=batch == 0),
+        _ptr(target_logits, "target_logits", dev, nbytes=lb),
+        _ptr(draft_logits, "draft_logits", dev, nbytes=lb, optional=True),
+        _ptr(temperature, "temperature", dev, nbytes=batch * 4),
+        _ptr(uniforms, "uniforms", dev, nbytes=bn * 4),
+        _ptr(final_uniforms, "final_uniforms", dev, nbytes=batch * 4),
+        _ptr(candidates, "candidates", dev, nbytes=bn * 4),
+        _ptr(retrieve_index, "retrieve_index", dev, nbytes=bn * 4),
+        _ptr(retrieve_next_token, "retrieve_next_token", dev, nbytes=bn * 4),
+        _ptr(retrieve_next_sibling, "retrieve_next_sibling", dev, nbytes=bn * 4),
+        _ptr(predict, "predict", dev, nbytes=bn * 4),
+        _ptr(accept_index, "accept_index", dev, nbytes=batch * accept_width * 4),
+        _ptr(accept_length, "accept_length", dev, nbytes=batch * 4),
+        _ptr(workspace, "workspace", dev, nbytes=need_ws, optional=batch == 0),
         workspace_bytes,
-        _ptr(dev_status, "dev_status", nbytes=4, optional=True),
+        _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
     ]
     _check("spec_accept_sample", _lib.spec_accept_sample(batch, n, accept_width, vocab, dtype,
                                                           *args, _stream(stream)))
@@ -265,23 +277,24 @@ def spec_compact_kv(batch, num_draft_tokens, accept_width, num_layers, num_kv_he
                     page_size, dtype, k_pool, v_pool, num_slots, page_table, max_pages,
                     seq_lens, out_cache_loc, accept_index, accept_length, new_seq_lens,
                     free_slots, num_free, dev_status=None, stream=None):
+    dev = _device()
     n = num_draft_tokens
     pool = num_layers * num_slots * num_kv_heads * head_dim * _ELEM.get(dtype, 4)
     args = [
-        _ptr(k_pool, "k_pool", nbytes=pool),
-        _ptr(v_pool, "v_pool", nbytes=pool),
+        _ptr(k_pool, "k_pool", dev, nbytes=pool),
+        _ptr(v_pool, "v_pool", dev, nbytes=pool),
     ]
     args2 = [
-        _ptr(page_table, "page_table", nbytes=batch * max_pages * 4),
+        _ptr(page_table, "page_table", dev, nbytes=batch * max_pages * 4),
         max_pages,
-        _ptr(seq_lens, "seq_lens", nbytes=batch * 4),
-        _ptr(out_cache_loc, "out_cache_loc", nbytes=batch * n * 4),
-        _ptr(accept_index, "accept_index", nbytes=batch * accept_width * 4),
-        _ptr(accept_length, "accept_length", nbytes=batch * 4),
-        _ptr(new_seq_lens, "new_seq_lens", nbytes=batch * 4),
-        _ptr(free_slots, "free_slots", nbytes=batch * n * 4),
-        _ptr(num_free, "num_free", nbytes=batch * 4),
-        _ptr(dev_status, "dev_status", nbytes=4, optional=True),
+        _ptr(seq_lens, "seq_lens", dev, nbytes=batch * 4),
+        _ptr(out_cache_loc, "out_cache_loc", dev, nbytes=batch * n * 4),
+        _ptr(accept_index, "accept_index", dev, nbytes=batch * accept_width * 4),
+        _ptr(accept_length, "accept_length", dev, nbytes=batch * 4),
+        _ptr(new_seq_lens, "new_seq_lens", dev, nbytes=batch * 4),
+        _ptr(free_slots, "free_slots", dev, nbytes=batch * n * 4),
+        _ptr(num_free, "num_free", dev, nbytes=batch * 4),
+        _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
     ]
     _check("spec_compact_kv", _lib.spec_compact_kv(batch, n, accept_width, num_layers,
                                                     num_kv_heads, head_dim, page_size, dtype,

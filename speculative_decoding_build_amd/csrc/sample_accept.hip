@@ -21,13 +21,20 @@
 //   1. statistics sweep over every verify row (target and draft): max logit
 //      and sum of exp((x - max) / T) per 8192-entry chunk, one 256-thread
 //      workgroup per (chunk, row), each chunk read once;
-//   2. the walk.  Preferred: a cooperative launch with G workgroups per
-//      request, each owning a slice of the vocabulary; the F(c) reductions and
-//      the inverse-CDF draw are split across the G slices and combined
-//      through a per-request barrier in global memory.  Every workgroup of a
-//      request replays the same decisions from the same data, so only the
-//      slice partial sums travel.  When the grid cannot be co-resident the
-//      walk falls back to one 1024-thread workgroup per request.
+//   2. the walk.  A prologue merges the chunk statistics of every row of the
+//      request and fetches, for every node, its token's target / draft logit
+//      in its parent's row, so accepting a child needs no memory access.
+//      Only a rejection (one F(c) reduction) and the terminal draw (an
+//      inverse CDF) touch the vocabulary.  Preferred form: G co-resident
+//      workgroups per request, each owning a slice of the vocabulary; a
+//      reduction is split across the slices and the G slice sums are
+//      exchanged through write-once slots (no barrier: every workgroup
+//      publishes its sum, then polls the G slots of that exchange).  Every
+//      thread of every workgroup of a request evaluates the same decisions
+//      from the same data, so decisions need no communication.  When the
+//      grid cannot be co-resident the walk runs as one 1024-thread
+//      workgroup per request.  The last rejection's sweep at a node is
+//      reused by the terminal draw at that node (same residual).
 //
 // Per-entry probabilities are float32 exponentials of the exactly formed
 // argument (x - max) / T, normalised and accumulated in float64.
@@ -41,24 +48,24 @@ namespace {
 
 constexpr int kSoloThreads = 1024;
 constexpr int kCoopThreads = 256;
-constexpr unsigned kSpinLimit = 1u << 20;       // about a second of waiting
+constexpr unsigned kSpinLimit = 1u << 20;      // polls of one slot before giving up
 constexpr int kCoopGridTarget = 512;           // workgroups of a cooperative walk, all requests
+constexpr int kCacheEntries = 16;              // row entries a walk thread keeps in registers
+
+// Exchange slot contents: kEmpty until written.  kEmpty is a signalling-NaN
+// bit pattern that float arithmetic never produces; a written value equal to
+// it is replaced by the default quiet NaN.
+constexpr uint64_t kEmpty = 0x7FF4DEAD0BADF00Dull;
+constexpr uint64_t kQuietNaN = 0x7FF8000000000000ull;
 
 struct SamplePart {
     float mt, md;
     double st, sd;
 };
 
-// per-request barrier words, one cache line each
-struct alignas(64) GroupSync {
-    unsigned count;
-    unsigned gen;
-    unsigned pad[14];
-};
-
 // exp((x - m) / T) to about one float ulp: x - m as an exact float pair
 // (two-sum), 1/T as a float pair, the rounding of the product folded back
-// as a first-order correction.
+// as a first-order correction.  A masked entry (x = -inf) gives 0.
 struct Scale {
     float m;
     float ithi;
@@ -72,7 +79,7 @@ __device__ __forceinline__ float exp_scaled(float x, const Scale &s) {
     const float y = d * s.ithi;
     const float delta = fmaf(d, s.ithi, -y) + fmaf(d, s.itlo, derr * s.ithi);
     const float e = expf(y);
-    return fmaf(e, delta, e);
+    return x == -INFINITY ? 0.f : fmaf(e, delta, e);   // -inf: the pair above is NaN
 }
 
 struct RowDist {
@@ -93,6 +100,25 @@ __device__ __forceinline__ double resid_weight(float xt, float xd, const RowDist
     return fmax(fma(-c, q, p), 0.0);
 }
 
+// 8 consecutive entries starting at v (a multiple of 8) as floats
+template <int DT>
+__device__ __forceinline__ void load8(const void *rowp, int64_t v, float (&x)[8]) {
+    if (DT == SPEC_BF16) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(rowp) + v);
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = lo_bf16(a[j]);
+            x[2 * j + 1] = hi_bf16(a[j]);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(rowp) + v);
+        const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(rowp) + v + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+}
+
 // Sum of resid_weight over [a, b) in ascending order; 16-byte loads when the
 // rows allow them (a is a multiple of 8 then).
 template <int DT>
@@ -100,17 +126,13 @@ __device__ double range_sum(const void *trow, const void *drow, int64_t a, int64
                             bool vec_ok, const RowDist &rd, double c) {
     double s = 0.0;
     int64_t v = a;
-    if (DT == SPEC_BF16 && vec_ok) {
+    if (vec_ok) {
         for (; v + 8 <= b; v += 8) {
-            const uint4 wt = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(trow) + v);
-            const uint4 wd = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(drow) + v);
-            const uint32_t at[4] = {wt.x, wt.y, wt.z, wt.w};
-            const uint32_t ad[4] = {wd.x, wd.y, wd.z, wd.w};
+            float xt[8], xd[8];
+            load8<DT>(trow, v, xt);
+            load8<DT>(drow, v, xd);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                s += resid_weight(lo_bf16(at[j]), lo_bf16(ad[j]), rd, c);
-                s += resid_weight(hi_bf16(at[j]), hi_bf16(ad[j]), rd, c);
-            }
+            for (int j = 0; j < 8; ++j) s += resid_weight(xt[j], xd[j], rd, c);
         }
     }
     for (; v < b; ++v) s += resid_weight(load_elem<DT>(trow, v), load_elem<DT>(drow, v), rd, c);
@@ -129,19 +151,8 @@ __device__ int64_t range_find(const void *trow, const void *drow, int64_t a, int
     return -1;
 }
 
-template <int NT>
-__device__ double block_sum(double v, double *scratch) {
-    v = wave_sum_d(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double s = 0.0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) s += scratch[w];
-    return s;
-}
-
 // Exclusive prefix of v over threads in thread order; also returns the total.
+// Every workgroup that scans the same values gets the same results.
 template <int NT>
 __device__ double block_exclusive_scan(double v, double *scratch, double &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -168,16 +179,18 @@ __device__ double block_exclusive_scan(double v, double *scratch, double &total)
 // 1. statistics sweep
 // ---------------------------------------------------------------------------
 
+// Also empties the exchange slots of the walk that follows: row r of the
+// grid clears slots [r*G, r*G + G) (r = request * n + exchange).
 template <int DT>
 __global__ __launch_bounds__(kSweepThreads) void sample_stats_kernel(
     const void *__restrict__ tlogits, const void *__restrict__ dlogits, int64_t vocab, int n,
-    int batch, int nchunks, bool vec_ok, const float *__restrict__ temperature,
-    SamplePart *__restrict__ part, GroupSync *__restrict__ sync) {
+    int nchunks, bool vec_ok, const float *__restrict__ temperature,
+    SamplePart *__restrict__ part, uint64_t *__restrict__ xch, int G) {
     const int c = blockIdx.x;
     const int64_t row = blockIdx.y;
     const int tid = threadIdx.x;
-    if (sync != nullptr && c == 0 && row == 0)
-        for (int r = tid; r < batch; r += kSweepThreads) { sync[r].count = 0; sync[r].gen = 0; }
+    if (xch != nullptr && c == 0)
+        for (int j = tid; j < G; j += kSweepThreads) xch[row * G + j] = kEmpty;
     const int64_t start = (int64_t)c * kChunk;
     const int64_t end = min(vocab, start + kChunk);
     const size_t eb = DT == SPEC_BF16 ? 2 : 4;
@@ -220,7 +233,7 @@ __global__ __launch_bounds__(kSweepThreads) void sample_stats_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// walk state shared by both walk kernels
+// 2. the walk
 // ---------------------------------------------------------------------------
 
 struct WalkArgs {
@@ -232,419 +245,353 @@ struct WalkArgs {
     const float *temperature, *uniforms, *final_uniforms;
     const int32_t *cand, *r_index, *r_next, *r_sib;
     int32_t *predict, *accept_index, *accept_length, *status;
-    // cooperative walk only
-    int G;              // workgroups per request
-    int64_t slice;      // vocabulary entries per workgroup (multiple of 8 * threads)
-    GroupSync *sync;    // [batch]
-    double *red;        // [batch][2][G]
+    int G;              // workgroups per request (1: one workgroup, no exchange)
+    int64_t slice;      // vocabulary entries per workgroup, a multiple of 8 * threads
+    uint64_t *xch;      // [batch][n][G] exchange slots (G > 1)
 };
 
+template <int NT>
 struct WalkShared {
-    RowDist dist;
-    float cxt[kMaxNodes];      // target / draft logit of each child token of the current node
+    RowDist dist[kMaxNodes];   // by local verify row
+    float cxt[kMaxNodes];      // node k's token: target / draft logit in its parent's row
     float cxd[kMaxNodes];
-    int clist[kMaxNodes];      // children of the current node in sibling order
-    int nkids;
-    int cand[kMaxNodes];
-    int next[kMaxNodes];
-    int sib[kMaxNodes];
-    float unif[kMaxNodes];
-    int row[kMaxNodes];
+    int cand[kMaxNodes], next[kMaxNodes], sib[kMaxNodes], par[kMaxNodes];
+    int row[kMaxNodes];        // local verify row of node k, -1 if invalid
     int pred[kMaxNodes];
     int ai[kMaxNodes + 1];
-    double scratch[16];
+    float unif[kMaxNodes];
+    double scratch[NT / 64];
     double bcast;
-    int cur, cnt, err, dec, child, draw, flag;
+    int err, owner, draw;
 };
 
-// Thread 0 decides the test of the i-th child of the current node (its
-// token's logits were prefetched) and publishes the outcome.
-__device__ void decide_child(const WalkShared &Sc, WalkShared &S, int i, int64_t vocab,
-                             double c, double F) {
-    int dec = 0;
-    const int child = Sc.clist[i];
-    const int t = Sc.cand[child];
-    if (t >= 0 && t < vocab) {
-        const RowDist &rd = Sc.dist;
-        const double p = (double)exp_scaled(Sc.cxt[i], rd.t) * rd.inv_st;
-        const double q = (double)exp_scaled(Sc.cxd[i], rd.d) * rd.inv_sd;
-        const double r = fmax(fma(-c, q, p), 0.0) / F;
-        const double ratio = q > 0.0 ? r / q : (r > 0.0 ? INFINITY : 0.0);
-        dec = (double)Sc.unif[child] < fmin(1.0, ratio);
+// Running (max, scaled sum) of softmax chunk statistics:
+// S = sum_chunks s_k * exp((m_k - M) / T) with M the largest m_k so far.
+__device__ __forceinline__ void merge_stat(float &M, double &Sm, float m2, double s2, double it) {
+    if (m2 == -INFINITY) return;                  // an empty chunk (its sum is 0)
+    if (M == -INFINITY) { M = m2; Sm = s2; return; }
+    if (m2 > M) {
+        Sm = Sm * exp(((double)M - (double)m2) * it) + s2;
+        M = m2;
     } else {
-        S.err |= SPEC_ST_RANGE;
+        Sm += s2 * exp(((double)m2 - (double)M) * it);
     }
-    S.dec = dec;
 }
 
-// Node entry, all threads: merge the row's chunk statistics (wave 0, one
-// lane per chunk), list the children in sibling order and fetch their
-// tokens' target / draft logits (one thread per child).
-template <int DT>
-__device__ void enter_node(const WalkArgs &A, WalkShared &S, int cur, int row, double it,
-                           const void *trow, const void *drow) {
-    const int tid = threadIdx.x;
-    if (tid < 64) {
-        float mt = -INFINITY, md = -INFINITY;
-        for (int c = tid; c < A.nchunks; c += 64) {
-            const SamplePart p = A.part[(int64_t)row * A.nchunks + c];
-            mt = fmaxf(mt, p.mt);
-            md = fmaxf(md, p.md);
-        }
-        mt = wave_max(mt);
-        md = wave_max(md);
-        double st = 0.0, sd = 0.0;
-        for (int c = tid; c < A.nchunks; c += 64) {
-            const SamplePart p = A.part[(int64_t)row * A.nchunks + c];
-            st += p.st * exp(((double)p.mt - (double)mt) * it);
-            sd += p.sd * exp(((double)p.md - (double)md) * it);
-        }
-        st = wave_sum_d(st);
-        sd = wave_sum_d(sd);
-        if (tid == 0) {
-            const float ithi = (float)it;
-            const float itlo = (float)(it - (double)ithi);
-            S.dist.t = Scale{mt, ithi, itlo};
-            S.dist.d = Scale{md, ithi, itlo};
-            S.dist.inv_st = st > 0.0 ? 1.0 / st : 0.0;
-            S.dist.inv_sd = sd > 0.0 ? 1.0 / sd : 0.0;
-            int k = 0;
-            int c = S.next[cur];
-            for (int steps = 0; steps < A.n && c != -1; ++steps) {
-                if (c < 0 || c >= A.n) { S.err |= SPEC_ST_RANGE; break; }
-                S.clist[k++] = c;
-                c = S.sib[c];
-            }
-            S.nkids = k;
-        }
+// Poll one exchange slot until it is written (bounded); false on timeout.
+__device__ __forceinline__ bool read_slot(uint64_t *slot, double &v) {
+    unsigned spins = 0;
+    uint64_t bits;
+    while ((bits = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == kEmpty) {
+        if (++spins > kSpinLimit) { v = 0.0; return false; }
+        __builtin_amdgcn_s_sleep(1);
     }
-    __syncthreads();
-    if (tid < S.nkids) {
-        const int t = S.cand[S.clist[tid]];
-        const bool ok = t >= 0 && t < A.vocab;
-        S.cxt[tid] = ok ? load_elem<DT>(trow, t) : 0.f;
-        S.cxd[tid] = ok ? load_elem<DT>(drow, t) : 0.f;
-    }
-    __syncthreads();
+    v = __builtin_bit_cast(double, bits);
+    return true;
 }
 
-// Per-request barrier among the G workgroups of a cooperative launch.  The
-// launch guarantees co-residency; the wait is still bounded, and a timeout
-// is reported instead of hanging.  Returns false after a timeout.
-__device__ bool group_barrier(GroupSync *gs, unsigned G, unsigned &epoch, WalkShared &S) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int ok = 1;
-        __threadfence();
-        const unsigned old = __hip_atomic_fetch_add(&gs->count, 1u, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        if (old == G - 1) {
-            __hip_atomic_store(&gs->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(&gs->gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            // poll with relaxed loads and exponential back-off (polls go to the
-            // memory side; hundreds of spinning workgroups would congest it)
-            unsigned spins = 0, nap = 1;
-            while (__hip_atomic_load(&gs->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) {
-                for (unsigned z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(4);
-                nap = nap < 16 ? nap * 2 : 16;
-                if (++spins > kSpinLimit) { ok = 0; break; }
-            }
-        }
-        __threadfence();
-        epoch += 1;
-        S.flag = ok;
-    }
-    __syncthreads();
-    return S.flag != 0;
-}
-
-// ---------------------------------------------------------------------------
-// 2a. cooperative walk: G workgroups per request
-// ---------------------------------------------------------------------------
-
-// Sum over the G slice partials of round `parity` (thread j < G loads entry
-// j); the reduction order is fixed, so every workgroup of the request gets
-// the bitwise same value.
-__device__ double group_total(const double *red, int G, WalkShared &S) {
-    double v = 0.0;
-    if ((int)threadIdx.x < G)
-        v = __hip_atomic_load(&red[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return block_sum<kCoopThreads>(v, S.scratch);
-}
-
-template <int DT>
-__global__ __launch_bounds__(kCoopThreads) void sample_walk_coop_kernel(WalkArgs A) {
-    __shared__ WalkShared S;
-    const int G = A.G;
-    const int req = blockIdx.x / G;
-    const int g = blockIdx.x % G;
+template <int DT, int NT, bool COOP>
+__global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
+    static_assert(NT % 64 == 0 && 64 % (NT / 64) == 0, "lanes per row must divide a wave");
+    __shared__ WalkShared<NT> S;
+    const int G = COOP ? A.G : 1;
+    const int req = COOP ? blockIdx.x / G : blockIdx.x;
+    const int g = COOP ? blockIdx.x % G : 0;
     const int tid = threadIdx.x;
     const int n = A.n;
     const int base = req * n;
     const size_t eb = DT == SPEC_BF16 ? 2 : 4;
     const double it = 1.0 / (double)A.temperature[req];
-    GroupSync *gs = A.sync + req;
-    double *red = A.red + (int64_t)req * 2 * G;
-    unsigned epoch = 0;
-    int parity = 0;
-    bool alive = true;
 
     // my slice of the vocabulary and, inside it, my contiguous segment
     const int64_t v0 = min(A.vocab, (int64_t)g * A.slice);
     const int64_t v1 = min(A.vocab, v0 + A.slice);
-    const int64_t seg = A.slice / kCoopThreads;
+    const int64_t seg = A.slice / NT;
     const int64_t sa = min(v1, v0 + tid * seg);
     const int64_t sb = min(v1, sa + seg);
 
+    // ---- prologue: links, uniforms and the statistics of every row -------
     if (tid < n) {
         int row = A.r_index[base + tid];
-        if (row < base || row >= base + n) row = -1;
+        row = (row >= base && row < base + n) ? row - base : -1;
         S.row[tid] = row;
         S.pred[tid] = 0;
+        S.par[tid] = -1;
         S.cand[tid] = A.cand[base + tid];
         S.next[tid] = A.r_next[base + tid];
         S.sib[tid] = A.r_sib[base + tid];
         S.unif[tid] = A.uniforms[base + tid];
     }
-    if (tid == 0) { S.cur = 0; S.cnt = 0; S.err = 0; }
-    __syncthreads();
-    if (tid == 0) {
-        for (int k = 0; k < n; ++k)
-            if (S.row[k] < 0) S.err |= SPEC_ST_RANGE;
-        S.ai[0] = S.row[0];
+    if (tid == 0) S.err = 0;
+    {
+        constexpr int LPR = NT / 64;                  // lanes per row (n <= 64)
+        const int k = tid / LPR, sub = tid % LPR;
+        float mt = -INFINITY, md = -INFINITY;
+        double st = 0.0, sd = 0.0;
+        if (k < n) {
+            for (int c = sub; c < A.nchunks; c += LPR) {
+                const SamplePart p = A.part[(int64_t)(base + k) * A.nchunks + c];
+                merge_stat(mt, st, p.mt, p.st, it);
+                merge_stat(md, sd, p.md, p.sd, it);
+            }
+        }
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) {
+            const float omt = __shfl_xor(mt, o, 64), omd = __shfl_xor(md, o, 64);
+            const double ost = __shfl_xor(st, o, 64), osd = __shfl_xor(sd, o, 64);
+            merge_stat(mt, st, omt, ost, it);
+            merge_stat(md, sd, omd, osd, it);
+        }
+        if (k < n && sub == 0) {
+            const float ithi = (float)it;
+            const float itlo = (float)(it - (double)ithi);
+            RowDist rd;
+            rd.t = Scale{mt, ithi, itlo};
+            rd.d = Scale{md, ithi, itlo};
+            rd.inv_st = st > 0.0 ? 1.0 / st : 0.0;
+            rd.inv_sd = sd > 0.0 ? 1.0 / sd : 0.0;
+            S.dist[k] = rd;
+        }
     }
+    __syncthreads();
+    if (tid < n) {
+        if (S.row[tid] < 0) atomicOr(&S.err, SPEC_ST_RANGE);
+        int c = S.next[tid];
+        for (int steps = 0; steps < n && c != -1; ++steps) {
+            if (c < 0 || c >= n) { atomicOr(&S.err, SPEC_ST_RANGE); break; }
+            S.par[c] = tid;
+            c = S.sib[c];
+        }
+    }
+    __syncthreads();
+    if (tid < n) {
+        const int p = S.par[tid];
+        const int t = S.cand[tid];
+        float xt = 0.f, xd = 0.f;
+        if (p >= 0 && S.row[p] >= 0 && t >= 0 && t < A.vocab) {
+            const int64_t grow = base + S.row[p];
+            xt = load_elem<DT>(static_cast<const char *>(A.tlogits) + grow * A.vocab * eb, t);
+            xd = load_elem<DT>(static_cast<const char *>(A.dlogits) + grow * A.vocab * eb, t);
+        }
+        S.cxt[tid] = xt;
+        S.cxd[tid] = xd;
+    }
+    __syncthreads();
+
+    // ---- the walk (every thread takes the same decisions) --------------------
+    int e = 0;                         // exchanges used so far (slots of this request)
+    bool alive = true;
+    double mine = 0.0, before = 0.0;   // my segment's sum and its prefix in my slice
+    double sj = 0.0, pre = 0.0;        // thread j < G: slice j's sum and its prefix
+    // The current node's row segment, as the exponentials exp_scaled gives
+    // (target, draft; 0 past the segment), kept in registers when the segment
+    // fits: later rejections at the node and its terminal draw then read no
+    // memory.
+    const bool use_cache = COOP && seg <= kCacheEntries;   // the solo walk's segments are longer
+    float cet[kCacheEntries], ced[kCacheEntries];
+    int cached_row = -1;
+    auto fill_cache = [&](const void *trow, const void *drow, const RowDist &rd) {
+#pragma unroll
+        for (int i0 = 0; i0 < kCacheEntries; i0 += 8) {
+            float xt[8], xd[8];
+            const int64_t v = sa + i0;
+            if (A.vec_ok && v + 8 <= sb) {
+                load8<DT>(trow, v, xt);
+                load8<DT>(drow, v, xd);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const bool in = v + j < sb;
+                    xt[j] = in ? load_elem<DT>(trow, v + j) : -INFINITY;
+                    xd[j] = in ? load_elem<DT>(drow, v + j) : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                cet[i0 + j] = exp_scaled(xt[j], rd.t);
+                ced[i0 + j] = exp_scaled(xd[j], rd.d);
+            }
+        }
+    };
+    auto cached_weight = [&](int i, const RowDist &rd, double cc) -> double {
+        const double p = (double)cet[i] * rd.inv_st;
+        const double q = (double)ced[i] * rd.inv_sd;
+        return fmax(fma(-cc, q, p), 0.0);
+    };
+    // sweep of the current node's row (local row lr) with multiplier cc;
+    // returns F(cc)
+    auto sweep = [&](const void *trow, const void *drow, const RowDist &rd, int lr,
+                     double cc) -> double {
+        if (use_cache) {
+            if (cached_row != lr) {
+                fill_cache(trow, drow, rd);
+                cached_row = lr;
+            }
+            double m = 0.0;
+#pragma unroll
+            for (int i = 0; i < kCacheEntries; ++i) m += cached_weight(i, rd, cc);
+            mine = m;
+        } else {
+            mine = range_sum<DT>(trow, drow, sa, sb, A.vec_ok, rd, cc);
+        }
+        double slice_tot;
+        before = block_exclusive_scan<NT>(mine, S.scratch, slice_tot);
+        if (!COOP) {
+            sj = slice_tot;
+            pre = 0.0;
+            return slice_tot;
+        }
+        if (e >= n) {                      // more exchanges than a tree of n nodes needs
+            if (tid == 0) atomicOr(&S.err, SPEC_ST_RANGE | SPEC_ST_SYNC);
+            __syncthreads();
+            alive = false;
+            return 0.0;
+        }
+        uint64_t *slots = A.xch + ((int64_t)base + e) * G;
+        ++e;
+        if (tid == 0) {
+            uint64_t bits = __builtin_bit_cast(uint64_t, slice_tot);
+            if (bits == kEmpty) bits = kQuietNaN;
+            __hip_atomic_store(slots + g, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        sj = 0.0;
+        if (tid < G && !read_slot(slots + tid, sj)) atomicOr(&S.err, SPEC_ST_SYNC);
+        double tot;
+        pre = block_exclusive_scan<NT>(sj, S.scratch, tot);   // also publishes the err bit
+        if (S.err & SPEC_ST_SYNC) alive = false;
+        return tot;
+    };
+    // first entry of my segment where the running sum from `before` exceeds tgt
+    auto find = [&](const void *trow, const void *drow, const RowDist &rd, double cc,
+                    double tgt) -> int64_t {
+        if (!use_cache) return range_find<DT>(trow, drow, sa, sb, rd, cc, before, tgt);
+        double run = before;
+        int64_t x = -1;
+#pragma unroll
+        for (int i = 0; i < kCacheEntries; ++i) {
+            run += cached_weight(i, rd, cc);
+            if (x < 0 && run > tgt) x = sa + i;
+        }
+        return x < sb ? x : -1;
+    };
+
+    int cur = 0, cnt = 0;
+    if (tid == 0) S.ai[0] = base + max(S.row[0], 0);
     double c = 0.0, F = 1.0;
-    int cur = 0;
+    bool swept = false;        // the last sweep was of the current node with multiplier c
     for (int level = 0; level < n && alive; ++level) {
-        __syncthreads();
-        cur = S.cur;
-        const int row = S.row[cur];
-        if (row < 0) break;
-        const void *trow = static_cast<const char *>(A.tlogits) + (int64_t)row * A.vocab * eb;
-        const void *drow = static_cast<const char *>(A.dlogits) + (int64_t)row * A.vocab * eb;
-        enter_node<DT>(A, S, cur, row, it, trow, drow);
-        const RowDist rd = S.dist;
-        const int nk = S.nkids;
+        const int lr = S.row[cur];
+        if (lr < 0) break;
+        const RowDist rd = S.dist[lr];
+        const void *trow = static_cast<const char *>(A.tlogits) + (int64_t)(base + lr) * A.vocab * eb;
+        const void *drow = static_cast<const char *>(A.dlogits) + (int64_t)(base + lr) * A.vocab * eb;
         c = 0.0;
         F = 1.0;
+        swept = false;
         int hit = -1;
-        for (int i = 0; i < nk; ++i) {
-            if (tid == 0) decide_child(S, S, i, A.vocab, c, F);
-            __syncthreads();
-            const int dec = S.dec;
-            __syncthreads();
-            if (dec) { hit = S.clist[i]; break; }
-            // rejected: F(c + F) over the vocabulary, split across the group
+        int k = S.next[cur];
+        for (int steps = 0; steps < n && k != -1 && alive; ++steps) {
+            if (k < 0 || k >= n) break;                 // reported by the prologue
+            const int t = S.cand[k];
+            bool dec = false;
+            if (t >= 0 && t < A.vocab) {
+                const double p = (double)exp_scaled(S.cxt[k], rd.t) * rd.inv_st;
+                const double q = (double)exp_scaled(S.cxd[k], rd.d) * rd.inv_sd;
+                const double r = fmax(fma(-c, q, p), 0.0) / F;
+                const double ratio = q > 0.0 ? r / q : (r > 0.0 ? INFINITY : 0.0);
+                dec = (double)S.unif[k] < fmin(1.0, ratio);
+            } else if (tid == 0) {
+                atomicOr(&S.err, SPEC_ST_RANGE);
+            }
+            if (dec) { hit = k; break; }
+            // rejected: F(c + F)
             const double cn = c + F;
-            const double mine = range_sum<DT>(trow, drow, sa, sb, A.vec_ok, rd, cn);
-            const double slice_sum = block_sum<kCoopThreads>(mine, S.scratch);
-            if (tid == 0)
-                __hip_atomic_store(&red[parity * G + g], slice_sum, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            if (!group_barrier(gs, G, epoch, S)) { alive = false; break; }
-            const double Fn = group_total(red + parity * G, G, S);
-            parity ^= 1;
+            const double Fn = sweep(trow, drow, rd, lr, cn);
+            if (!alive) break;
             if (Fn > 0.0) {
                 c = cn;
                 F = Fn;
-            } else if (tid == 0) {
-                S.err |= SPEC_ST_ZERO_RESIDUAL;
+                swept = true;
+            } else {
+                if (tid == 0) atomicOr(&S.err, SPEC_ST_ZERO_RESIDUAL);
+                swept = false;
             }
+            k = S.sib[k];
         }
         if (!alive || hit < 0) break;
-        if (tid == 0) {
-            if (S.cnt + 1 >= A.s1) {
-                S.err |= SPEC_ST_DEPTH;
-                S.dec = 0;
-            } else {
-                S.pred[cur] = S.cand[hit];
-                S.cnt = S.cnt + 1;
-                S.ai[S.cnt] = S.row[hit];
-                S.cur = hit;
-                S.dec = 1;
-            }
+        if (cnt + 1 >= A.s1) {
+            if (tid == 0) atomicOr(&S.err, SPEC_ST_DEPTH);
+            break;
         }
-        __syncthreads();
-        const int moved = S.dec;
-        __syncthreads();
-        if (!moved) break;
+        if (tid == 0) {
+            S.pred[cur] = S.cand[hit];
+            S.ai[cnt + 1] = base + max(S.row[hit], 0);
+        }
+        ++cnt;
+        cur = hit;
     }
 
-    // terminal draw: inverse CDF of max(0, p - c q) in vocabulary order
-    const int row = S.row[cur];
-    if (alive && row >= 0) {
-        const RowDist rd = S.dist;
-        const void *trow = static_cast<const char *>(A.tlogits) + (int64_t)row * A.vocab * eb;
-        const void *drow = static_cast<const char *>(A.dlogits) + (int64_t)row * A.vocab * eb;
-        const double mine = range_sum<DT>(trow, drow, sa, sb, A.vec_ok, rd, c);
-        double slice_total;
-        const double before = block_exclusive_scan<kCoopThreads>(mine, S.scratch, slice_total);
-        if (tid == 0)
-            __hip_atomic_store(&red[parity * G + g], slice_total, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        if (group_barrier(gs, G, epoch, S)) {
-            // slice sums in slice order -> owner of the crossing, my slice's offset
-            double sj = 0.0;
-            if (tid < G)
-                sj = __hip_atomic_load(&red[parity * G + tid], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            double total;
-            const double pre = block_exclusive_scan<kCoopThreads>(sj, S.scratch, total);
-            const double target = (double)A.final_uniforms[req] * total;
-            if (tid == 0) { S.dec = G - 1; S.draw = INT_MAX; }
+    // ---- terminal draw: inverse CDF of max(0, p - c q) in vocabulary order ----
+    const int lr = S.row[cur];
+    bool terminal_written = false;
+    if (alive && lr >= 0) {
+        const RowDist rd = S.dist[lr];
+        const void *trow = static_cast<const char *>(A.tlogits) + (int64_t)(base + lr) * A.vocab * eb;
+        const void *drow = static_cast<const char *>(A.dlogits) + (int64_t)(base + lr) * A.vocab * eb;
+        // after a rejection at this node the last sweep's sums are this residual's
+        const double tot = swept ? F : sweep(trow, drow, rd, lr, c);
+        if (alive) {
+            const double target = (double)A.final_uniforms[req] * tot;
+            if (tid == 0) { S.owner = INT_MAX; S.draw = INT_MAX; }
             __syncthreads();
-            if (tid < G && sj > 0.0 && pre <= target && target < pre + sj) atomicMin(&S.dec, tid);
-            if (tid == g) S.bcast = target - pre;          // target measured from my slice
+            if (COOP) {
+                if (tid < G && sj > 0.0 && pre <= target && target < pre + sj) atomicMin(&S.owner, tid);
+            } else if (tid == 0 && target < tot) {
+                S.owner = 0;
+            }
             __syncthreads();
-            if (S.dec == g) {
-                const double tgt = S.bcast;
+            const int owner = S.owner;
+            if (COOP && tid == owner) S.bcast = target - pre;   // target measured from its slice
+            __syncthreads();
+            if (owner == INT_MAX) {
+                // no crossing: the target sits at the very end of the mass
+                if (g == 0 && tid == 0) A.predict[base + lr] = (int)(A.vocab - 1);
+            } else if (owner == g) {
+                const double tgt = COOP ? S.bcast : target;
                 if (sa < sb && before <= tgt && tgt < before + mine) {
-                    const int64_t x = range_find<DT>(trow, drow, sa, sb, rd, c, before, tgt);
+                    const int64_t x = find(trow, drow, rd, c, tgt);
                     if (x >= 0) atomicMin(&S.draw, (int)x);
                 }
                 __syncthreads();
                 if (tid == 0) {
-                    // no crossing inside the slice (rounding, or a target at the
-                    // very end of the mass): its last entry
                     int x = S.draw;
                     if (x == INT_MAX) x = (int)(v1 > v0 ? v1 - 1 : A.vocab - 1);
-                    A.predict[row] = x;
+                    A.predict[base + lr] = x;
                 }
             }
-        } else {
-            alive = false;
+            terminal_written = true;
         }
     }
-
-    if (!alive && tid == 0) S.err |= SPEC_ST_SYNC;
     __syncthreads();
     if (g == 0) {
-        const int terminal = (alive && row >= 0) ? cur : -1;
-        if (tid < n && S.row[tid] >= 0 && tid != terminal) A.predict[S.row[tid]] = S.pred[tid];
-        for (int j = tid; j < A.s1; j += kCoopThreads)
-            A.accept_index[(int64_t)req * A.s1 + j] = (j <= S.cnt) ? S.ai[j] : -1;
-        if (tid == 0) A.accept_length[req] = S.cnt + 1;
+        const int terminal = terminal_written ? cur : -1;
+        if (tid < n && S.row[tid] >= 0 && tid != terminal) A.predict[base + S.row[tid]] = S.pred[tid];
+        for (int j = tid; j < A.s1; j += NT)
+            A.accept_index[(int64_t)req * A.s1 + j] = (j <= cnt) ? S.ai[j] : -1;
+        if (tid == 0) A.accept_length[req] = cnt + 1;
     }
     if (tid == 0) raise_status(A.status, S.err);
 }
 
 // ---------------------------------------------------------------------------
-// 2b. one workgroup per request (fallback)
-// ---------------------------------------------------------------------------
-
-template <int DT>
-__global__ __launch_bounds__(kSoloThreads) void sample_walk_solo_kernel(WalkArgs A) {
-    __shared__ WalkShared S;
-    const int req = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int n = A.n;
-    const int base = req * n;
-    const size_t eb = DT == SPEC_BF16 ? 2 : 4;
-    const double it = 1.0 / (double)A.temperature[req];
-    // contiguous segment per thread, a multiple of 8 entries
-    const int64_t seg = ((A.vocab + kSoloThreads - 1) / kSoloThreads + 7) / 8 * 8;
-    const int64_t sa = min(A.vocab, (int64_t)tid * seg);
-    const int64_t sb = min(A.vocab, sa + seg);
-
-    if (tid < n) {
-        int row = A.r_index[base + tid];
-        if (row < base || row >= base + n) row = -1;
-        S.row[tid] = row;
-        S.pred[tid] = 0;
-        S.cand[tid] = A.cand[base + tid];
-        S.next[tid] = A.r_next[base + tid];
-        S.sib[tid] = A.r_sib[base + tid];
-        S.unif[tid] = A.uniforms[base + tid];
-    }
-    if (tid == 0) { S.cur = 0; S.cnt = 0; S.err = 0; }
-    __syncthreads();
-    if (tid == 0) {
-        for (int k = 0; k < n; ++k)
-            if (S.row[k] < 0) S.err |= SPEC_ST_RANGE;
-        S.ai[0] = S.row[0];
-    }
-    double c = 0.0, F = 1.0;
-    int cur = 0;
-    for (int level = 0; level < n; ++level) {
-        __syncthreads();
-        cur = S.cur;
-        const int row = S.row[cur];
-        if (row < 0) break;
-        const void *trow = static_cast<const char *>(A.tlogits) + (int64_t)row * A.vocab * eb;
-        const void *drow = static_cast<const char *>(A.dlogits) + (int64_t)row * A.vocab * eb;
-        enter_node<DT>(A, S, cur, row, it, trow, drow);
-        const RowDist rd = S.dist;
-        const int nk = S.nkids;
-        c = 0.0;
-        F = 1.0;
-        int hit = -1;
-        for (int i = 0; i < nk; ++i) {
-            if (tid == 0) decide_child(S, S, i, A.vocab, c, F);
-            __syncthreads();
-            const int dec = S.dec;
-            __syncthreads();
-            if (dec) { hit = S.clist[i]; break; }
-            const double cn = c + F;
-            const double Fn = block_sum<kSoloThreads>(
-                range_sum<DT>(trow, drow, sa, sb, A.vec_ok, rd, cn), S.scratch);
-            if (Fn > 0.0) {
-                c = cn;
-                F = Fn;
-            } else if (tid == 0) {
-                S.err |= SPEC_ST_ZERO_RESIDUAL;
-            }
-        }
-        if (hit < 0) break;
-        if (tid == 0) {
-            if (S.cnt + 1 >= A.s1) {
-                S.err |= SPEC_ST_DEPTH;
-                S.dec = 0;
-            } else {
-                S.pred[cur] = S.cand[hit];
-                S.cnt = S.cnt + 1;
-                S.ai[S.cnt] = S.row[hit];
-                S.cur = hit;
-                S.dec = 1;
-            }
-        }
-        __syncthreads();
-        const int moved = S.dec;
-        __syncthreads();
-        if (!moved) break;
-    }
-
-    const int row = S.row[cur];
-    if (row >= 0) {
-        const RowDist rd = S.dist;
-        const void *trow = static_cast<const char *>(A.tlogits) + (int64_t)row * A.vocab * eb;
-        const void *drow = static_cast<const char *>(A.dlogits) + (int64_t)row * A.vocab * eb;
-        const double mine = range_sum<DT>(trow, drow, sa, sb, A.vec_ok, rd, c);
-        double total;
-        const double before = block_exclusive_scan<kSoloThreads>(mine, S.scratch, total);
-        const double target = (double)A.final_uniforms[req] * total;
-        if (tid == 0) S.draw = INT_MAX;
-        __syncthreads();
-        if (sa < sb && before <= target && target < before + mine) {
-            const int64_t x = range_find<DT>(trow, drow, sa, sb, rd, c, before, target);
-            if (x >= 0) atomicMin(&S.draw, (int)x);
-        }
-        __syncthreads();
-        if (tid == 0) S.pred[cur] = (S.draw == INT_MAX) ? (int)(A.vocab - 1) : S.draw;
-    }
-    __syncthreads();
-    if (tid < n && S.row[tid] >= 0) A.predict[S.row[tid]] = S.pred[tid];
-    for (int j = tid; j < A.s1; j += kSoloThreads)
-        A.accept_index[(int64_t)req * A.s1 + j] = (j <= S.cnt) ? S.ai[j] : -1;
-    if (tid == 0) {
-        A.accept_length[req] = S.cnt + 1;
-        raise_status(A.status, S.err);
-    }
-}
-
-// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+
+constexpr int64_t kMinSlice = (int64_t)kCoopThreads * 8;
+
+int max_groups(int64_t vocab) {
+    return (int)std::min<int64_t>((vocab + kMinSlice - 1) / kMinSlice, kCoopThreads);
+}
 
 struct CoopPlan {
     int G;
@@ -663,32 +610,27 @@ CoopPlan coop_plan(int batch, int64_t vocab) {
         bool ok = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess;
         ok = ok && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
         ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                       &per, reinterpret_cast<const void *>(sample_walk_coop_kernel<DT>),
+                       &per, reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true>),
                        kCoopThreads, 0) == hipSuccess;
         cap = (ok && coop) ? cus * per : 0;
         cached_device = dev;
     }
-    const int64_t min_slice = (int64_t)kCoopThreads * 8;
-    int64_t G = (vocab + min_slice - 1) / min_slice;
+    int64_t G = max_groups(vocab);
     G = std::min<int64_t>(G, cap / std::max(batch, 1));
     G = std::min<int64_t>(G, std::max(2, kCoopGridTarget / std::max(batch, 1)));
-    G = std::min<int64_t>(G, kCoopThreads);      // one partial per thread of a workgroup
     if (G < 2) return CoopPlan{0, 0};
     int64_t slice = (vocab + G - 1) / G;
-    slice = (slice + min_slice - 1) / min_slice * min_slice;
+    slice = (slice + kMinSlice - 1) / kMinSlice * kMinSlice;
     G = (vocab + slice - 1) / slice;
+    if (G < 2) return CoopPlan{0, 0};
     return CoopPlan{(int)G, slice};
 }
 
-size_t sample_workspace_layout(int batch, int n, int64_t vocab, size_t *off_sync, size_t *off_red) {
+size_t sample_workspace_layout(int batch, int n, int64_t vocab, size_t *off_xch) {
     const size_t parts = spec::align_up((size_t)batch * n * num_chunks(vocab) * sizeof(SamplePart), 256);
-    const size_t syncs = spec::align_up((size_t)batch * sizeof(GroupSync), 256);
-    const int64_t gmax = std::min<int64_t>((vocab + kCoopThreads * 8 - 1) / (kCoopThreads * 8),
-                                           kCoopThreads);
-    const size_t reds = spec::align_up((size_t)batch * 2 * gmax * sizeof(double), 256);
-    if (off_sync) *off_sync = parts;
-    if (off_red) *off_red = parts + syncs;
-    return parts + syncs + reds;
+    const size_t xch = spec::align_up((size_t)batch * n * max_groups(vocab) * sizeof(uint64_t), 256);
+    if (off_xch) *off_xch = parts;
+    return parts + xch;
 }
 
 template <int DT>
@@ -697,37 +639,44 @@ int launch_sample(int batch, int n, int s1, int64_t vocab, const void *tl, const
                   const int32_t *cand, const int32_t *ri, const int32_t *rn, const int32_t *rs,
                   int32_t *predict, int32_t *ai, int32_t *al, void *workspace,
                   int32_t *dev_status, hipStream_t st) {
-    size_t off_sync = 0, off_red = 0;
-    sample_workspace_layout(batch, n, vocab, &off_sync, &off_red);
+    size_t off_xch = 0;
+    sample_workspace_layout(batch, n, vocab, &off_xch);
     const int nch = num_chunks(vocab);
     const size_t eb = DT == SPEC_BF16 ? 2 : 4;
     const bool vec_ok = (vocab * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(tl) % 16 == 0 &&
                         reinterpret_cast<uintptr_t>(dl) % 16 == 0;
     SamplePart *part = static_cast<SamplePart *>(workspace);
-    GroupSync *sync = reinterpret_cast<GroupSync *>(static_cast<char *>(workspace) + off_sync);
-    double *red = reinterpret_cast<double *>(static_cast<char *>(workspace) + off_red);
+    uint64_t *xch = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + off_xch);
+    const CoopPlan pl = coop_plan<DT>(batch, vocab);
     hipLaunchKernelGGL(sample_stats_kernel<DT>, dim3(nch, batch * n), dim3(kSweepThreads), 0, st,
-                       tl, dl, vocab, n, batch, nch, vec_ok, temperature, part, sync);
+                       tl, dl, vocab, n, nch, vec_ok, temperature, part,
+                       pl.G >= 2 ? xch : nullptr, pl.G);
     WalkArgs A{};
     A.n = n; A.s1 = s1; A.nchunks = nch; A.vocab = vocab; A.vec_ok = vec_ok; A.part = part;
     A.tlogits = tl; A.dlogits = dl; A.temperature = temperature; A.uniforms = uniforms;
     A.final_uniforms = final_uniforms; A.cand = cand; A.r_index = ri; A.r_next = rn;
     A.r_sib = rs; A.predict = predict; A.accept_index = ai; A.accept_length = al;
-    A.status = dev_status; A.sync = sync; A.red = red;
-    const CoopPlan pl = coop_plan<DT>(batch, vocab);
+    A.status = dev_status; A.xch = xch;
     if (pl.G >= 2) {
         A.G = pl.G;
         A.slice = pl.slice;
+        const dim3 grid((unsigned)(batch * pl.G)), block(kCoopThreads);
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive) {
+            // recorded into a graph: an ordinary launch of a grid sized to
+            // what the device holds at once
+            hipLaunchKernelGGL((sample_walk_kernel<DT, kCoopThreads, true>), grid, block, 0, st, A);
+            return launch_status();
+        }
         void *args[] = {&A};
-        const hipError_t e = hipLaunchCooperativeKernel(
-            reinterpret_cast<const void *>(sample_walk_coop_kernel<DT>),
-            dim3((unsigned)(batch * pl.G)), dim3(kCoopThreads), args, 0, st);
-        if (e == hipSuccess) return SPEC_OK;
-        (void)hipGetLastError();   // fall back below
+        const void *fn = reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true>);
+        if (hipLaunchCooperativeKernel(fn, grid, block, args, 0, st) == hipSuccess) return SPEC_OK;
+        (void)hipGetLastError();   // fall back below; the emptied slots go unused
     }
     A.G = 1;
-    A.slice = vocab;
-    hipLaunchKernelGGL(sample_walk_solo_kernel<DT>, dim3(batch), dim3(kSoloThreads), 0, st, A);
+    A.slice = ((vocab + kSoloThreads - 1) / kSoloThreads + 7) / 8 * 8 * kSoloThreads;
+    hipLaunchKernelGGL((sample_walk_kernel<DT, kSoloThreads, false>), dim3(batch),
+                       dim3(kSoloThreads), 0, st, A);
     return launch_status();
 }
 
@@ -736,7 +685,7 @@ int launch_sample(int batch, int n, int s1, int64_t vocab, const void *tl, const
 extern "C" size_t spec_accept_workspace_size(int batch, int n, int64_t vocab, int sampled) {
     if (batch <= 0 || n <= 0 || vocab <= 0) return 0;
     if (!sampled) return spec_greedy_workspace_bytes(batch, n, vocab);
-    return sample_workspace_layout(batch, n, vocab, nullptr, nullptr);
+    return sample_workspace_layout(batch, n, vocab, nullptr);
 }
 
 extern "C" int spec_accept_sample(int batch, int n, int s1, int64_t vocab, int dtype,

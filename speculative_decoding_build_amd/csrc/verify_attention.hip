@@ -139,7 +139,8 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams P, int xcd_remap) {
     static_assert(D == 64 || D == 128, "head_dim");
     constexpr int KS = D + 8;              // K row stride (bf16), 16-byte pad
-    constexpr int VS = kTileKeys + 8;      // V^T row stride (bf16)
+    constexpr int VS = kTileKeys + 4;      // V^T row stride (bf16): 34 dwords, so the
+                                           // 8-byte reads of 32 rows hit distinct banks
     constexpr int NT = NW * 64;
     constexpr int KUNITS = kTileKeys * (D / 8);        // 16-byte K pieces per tile
     constexpr int VUNITS = (kTileKeys / 4) * (D / 8);  // 4 keys x 8 dims per V piece
@@ -493,6 +494,13 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(AttnParams P) {
 // ---------------------------------------------------------------------------
 // merge of split partials: one wavefront per (row, head) output vector
 // ---------------------------------------------------------------------------
+//
+// Lane s reads split s's (max, sum) (at most 64 splits), the weights
+// exp2(m_s - M) go to every lane by readlane, and the unnormalised outputs
+// are accumulated 8 splits at a time with all 8 loads in flight.  Lanes own
+// D/64 consecutive dims.
+
+constexpr int kMaxSplits = 64;
 
 template <int D, int DTYPE>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
@@ -511,28 +519,43 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
     const int rho = node * P.group + h % P.group;
     const int ns = min(P.nsplit, (L + P.n + P.split_len - 1) / P.split_len);
     const int64_t base = ((int64_t)b * P.hkv + kvh) * P.nsplit;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, P.part_ml[(base + s) * P.rows + rho].x);
+    const float2 ml = lane < ns ? P.part_ml[(base + lane) * P.rows + rho] : make_float2(-INFINITY, 0.f);
+    const float M = spec::wave_max(ml.x);
     const float Mu = (M == -INFINITY) ? 0.f : M;
+    const float w = lane < ns ? exp2f(ml.x - Mu) : 0.f;
+    const float lsum = spec::wave_sum(w * ml.y);
     float acc[PER] = {};
-    float lsum = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const int64_t pidx = (base + s) * P.rows + rho;
-        const float2 ml = P.part_ml[pidx];
-        const float w = exp2f(ml.x - Mu);
-        lsum = fmaf(w, ml.y, lsum);
+    const float *po = P.part_o + (base * P.rows + rho) * D + lane * PER;
+    const int64_t sstride = (int64_t)P.rows * D;
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+        float x[8][PER];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, P.part_o[pidx * D + lane + 64 * j], acc[j]);
+        for (int u = 0; u < 8; ++u) {
+            const int s = min(s0 + u, ns - 1);
+#pragma unroll
+            for (int j = 0; j < PER; ++j) x[u][j] = po[s * sstride + j];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float ws = s0 + u < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u)) : 0.f;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) acc[j] = fmaf(ws, x[u][j], acc[j]);
+        }
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     if (DTYPE == SPEC_BF16) {
-        __bf16 *op = static_cast<__bf16 *>(P.out) + vec * D;
+        uint16_t *op = static_cast<uint16_t *>(P.out) + vec * D + lane * PER;
+        uint32_t hb[PER];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) op[lane + 64 * j] = static_cast<__bf16>(acc[j] * inv);
+        for (int j = 0; j < PER; ++j) hb[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j] * inv));
+        if (PER == 2)
+            *reinterpret_cast<uint32_t *>(op) = hb[0] | (hb[PER - 1] << 16);
+        else
+            op[0] = (uint16_t)hb[0];
     } else {
-        float *op = static_cast<float *>(P.out) + vec * D;
+        float *op = static_cast<float *>(P.out) + vec * D + lane * PER;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) op[lane + 64 * j] = acc[j] * inv;
+        for (int j = 0; j < PER; ++j) op[j] = acc[j] * inv;
     }
 }
 
@@ -563,7 +586,7 @@ Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
     const int tiles = (keys + kTileKeys - 1) / kTileKeys;
     const int base = batch * hkv * pl.rowgroups;
     int ns = (kTargetGroups + base - 1) / base;
-    ns = std::max(1, std::min(ns, tiles / kMinTiles));
+    ns = std::max(1, std::min({ns, tiles / kMinTiles, kMaxSplits}));
     const int tiles_per = (tiles + ns - 1) / ns;
     pl.split_len = tiles_per * kTileKeys;
     pl.nsplit = (keys + pl.split_len - 1) / pl.split_len;

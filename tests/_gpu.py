@@ -106,10 +106,14 @@ def accept_greedy(w, tl, tree):
                 accept_length=host(al), target_predict=host(tp), status=int(host(st)[0]))
 
 
-def accept_sample(w, tl, dl, tree, temperature=None, uniforms=None, final_uniforms=None):
+def accept_sample(w, tl, dl, tree, temperature=None, uniforms=None, final_uniforms=None,
+                  workspace=None):
     cfg = w.cfg
     b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
-    ws = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8, device=DEV)
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
+                         device=DEV)
     predict, ai, al, st = i32(b * n), i32(b * s1), i32(b), status()
     predict.fill_(-7)
     ai.fill_(-7)
