@@ -253,7 +253,7 @@ def main():
         dtype=torch.uint8, device="cuda")
     ws_greedy = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
                             device="cuda")
-    ws_sample = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
+    ws_sample = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
                             device="cuda")
     S.spec_build_tree(b, cfg.topk, cfg.num_steps, n, S.SPEC_MASK_QLEN_BITS, base.scores,
                       base.tokens, base.parents, base.bonus, base.seq_lens, base.draft_tokens,

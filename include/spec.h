@@ -54,8 +54,9 @@ enum spec_status_bits {
     SPEC_ST_NOT_CLOSED = 2,     /* a kept node's parent was not kept                */
     SPEC_ST_DEPTH = 4,          /* accepted path longer than accept_width           */
     SPEC_ST_ZERO_RESIDUAL = 8,  /* residual mass exactly zero (informational)       */
-    SPEC_ST_SYNC = 16           /* a workgroup group barrier timed out; that call's
-                                   sampled outputs are unspecified                  */
+    SPEC_ST_SYNC = 16           /* a wait for another workgroup's partial result
+                                   timed out; that call's sampled outputs are
+                                   unspecified                                      */
 };
 
 enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 };
@@ -213,8 +214,12 @@ int spec_accept_greedy(int batch, int num_draft_tokens, int accept_width, int64_
  * cumulative R (vocabulary order) exceeds final_uniforms[b] * sum(R).
  * Outputs as spec_accept_greedy.  Distribution statistics are fp32 sweeps
  * with fp64 reductions; a decision closer than ~1e-6 to its threshold may
- * differ from an exact evaluation.
- * workspace: spec_accept_workspace_size(batch, n, vocab, 1) bytes.
+ * differ from an exact evaluation.  Only the rows the walk visits are read.
+ * workspace: spec_accept_workspace_size(batch, n, vocab, 1) bytes, 16-byte
+ *   aligned and zero-filled before its first use; every call leaves it
+ *   zero-filled again, so one workspace serves any number of calls in
+ *   stream order (concurrent calls need one each).  After a call that
+ *   raised SPEC_ST_SYNC, zero it again before the next call.
  */
 int spec_accept_sample(int batch, int num_draft_tokens, int accept_width, int64_t vocab,
                        int dtype, const void *target_logits, const void *draft_logits,

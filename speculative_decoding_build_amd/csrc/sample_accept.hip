@@ -17,24 +17,19 @@
 // vocabulary, independent of how many rejections came before.  A level with
 // F = 0 leaves R unchanged, as the recursive form does.
 //
-// Launches
-//   1. statistics sweep over every verify row (target and draft): max logit
-//      and sum of exp((x - max) / T) per 8192-entry chunk, one 256-thread
-//      workgroup per (chunk, row), each chunk read once;
-//   2. the walk.  A prologue merges the chunk statistics of every row of the
-//      request and fetches, for every node, its token's target / draft logit
-//      in its parent's row, so accepting a child needs no memory access.
-//      Only a rejection (one F(c) reduction) and the terminal draw (an
-//      inverse CDF) touch the vocabulary.  Preferred form: G co-resident
-//      workgroups per request, each owning a slice of the vocabulary; a
-//      reduction is split across the slices and the G slice sums are
-//      exchanged through write-once slots (no barrier: every workgroup
-//      publishes its sum, then polls the G slots of that exchange).  Every
-//      thread of every workgroup of a request evaluates the same decisions
-//      from the same data, so decisions need no communication.  When the
-//      grid cannot be co-resident the walk runs as one 1024-thread
-//      workgroup per request.  The last rejection's sweep at a node is
-//      reused by the terminal draw at that node (same residual).
+// One launch.  Only the rows the walk visits are read: on arrival at a node
+// the walk computes that row's softmax statistics (max and sum of
+// exp((x - max) / T), target and draft) and fetches its children's token
+// logits; a rejection is one F(c) reduction; the terminal token an inverse
+// CDF.  Preferred form: G co-resident workgroups per request, each owning a
+// slice of the vocabulary, whose entries stay in registers for the whole
+// visit.  Slice results are exchanged through write-once slots in the
+// workspace (each workgroup publishes, then polls the G slots of that
+// exchange); the last workgroup of a request to finish clears the slots it
+// used, so the workspace is zero again after every call.  Every thread of
+// every workgroup of a request evaluates the same decisions from the same
+// data, so decisions need no communication.  When the grid cannot be
+// co-resident the walk runs as one 1024-thread workgroup per request.
 //
 // Per-entry probabilities are float32 exponentials of the exactly formed
 // argument (x - max) / T, normalised and accumulated in float64.
@@ -50,18 +45,21 @@ constexpr int kSoloThreads = 1024;
 constexpr int kCoopThreads = 256;
 constexpr unsigned kSpinLimit = 1u << 20;      // polls of one slot before giving up
 constexpr int kCoopGridTarget = 512;           // workgroups of a cooperative walk, all requests
+constexpr int kMaxGroups = 64;                 // slices per request (one wave gathers them)
 constexpr int kCacheEntries = 16;              // row entries a walk thread keeps in registers
+constexpr int kWords = 3;                      // exchange words per workgroup per exchange
 
-// Exchange slot contents: kEmpty until written.  kEmpty is a signalling-NaN
-// bit pattern that float arithmetic never produces; a written value equal to
-// it is replaced by the default quiet NaN.
-constexpr uint64_t kEmpty = 0x7FF4DEAD0BADF00Dull;
+// Exchange slot encoding: a slot holds bits(v) ^ kFlip, 0 meaning "not yet
+// written" (a zero-filled workspace is empty).  kFlip is a signalling-NaN
+// pattern that arithmetic never produces; a value equal to it is stored as
+// the default quiet NaN instead.
+constexpr uint64_t kFlip = 0x7FF4DEAD0BADF00Dull;
 constexpr uint64_t kQuietNaN = 0x7FF8000000000000ull;
 
-struct SamplePart {
-    float mt, md;
-    double st, sd;
-};
+__device__ __forceinline__ uint64_t encode_bits(uint64_t b) {
+    if (b == kFlip) b = kQuietNaN;
+    return b ^ kFlip;
+}
 
 // exp((x - m) / T) to about one float ulp: x - m as an exact float pair
 // (two-sum), 1/T as a float pair, the rounding of the product folded back
@@ -93,10 +91,11 @@ __device__ __forceinline__ float load_elem(const void *rowp, int64_t v) {
     return static_cast<const float *>(rowp)[v];
 }
 
-// weight of entry v in the residual state (c, F), without the 1/F factor
-__device__ __forceinline__ double resid_weight(float xt, float xd, const RowDist &rd, double c) {
-    const double p = (double)exp_scaled(xt, rd.t) * rd.inv_st;
-    const double q = (double)exp_scaled(xd, rd.d) * rd.inv_sd;
+// weight of an entry in the residual state (c, F), without the 1/F factor,
+// from its two exponentials
+__device__ __forceinline__ double resid_from_exp(float et, float ed, const RowDist &rd, double c) {
+    const double p = (double)et * rd.inv_st;
+    const double q = (double)ed * rd.inv_sd;
     return fmax(fma(-c, q, p), 0.0);
 }
 
@@ -119,40 +118,75 @@ __device__ __forceinline__ void load8(const void *rowp, int64_t v, float (&x)[8]
     }
 }
 
-// Sum of resid_weight over [a, b) in ascending order; 16-byte loads when the
-// rows allow them (a is a multiple of 8 then).
-template <int DT>
-__device__ double range_sum(const void *trow, const void *drow, int64_t a, int64_t b,
-                            bool vec_ok, const RowDist &rd, double c) {
-    double s = 0.0;
-    int64_t v = a;
-    if (vec_ok) {
-        for (; v + 8 <= b; v += 8) {
-            float xt[8], xd[8];
+// Calls f(v, xt, xd, cnt) for consecutive groups of up to 8 entries of
+// [a, b) of the two rows (v the group's first entry, cnt its size; entries
+// past cnt are -inf), with 16-byte loads when the rows allow them; unrolled
+// so that several groups' loads are in flight together.
+template <int DT, typename Fn>
+__device__ __forceinline__ void for_each8(const void *trow, const void *drow, int64_t a, int64_t b,
+                                          bool vec_ok, Fn &&f) {
+#pragma unroll 4
+    for (int64_t v = a; v < b; v += 8) {
+        float xt[8], xd[8];
+        const int cnt = (int)min((int64_t)8, b - v);
+        if (vec_ok && cnt == 8) {
             load8<DT>(trow, v, xt);
             load8<DT>(drow, v, xd);
+        } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s += resid_weight(xt[j], xd[j], rd, c);
+            for (int j = 0; j < 8; ++j) {
+                const bool in = j < cnt;
+                xt[j] = in ? load_elem<DT>(trow, v + j) : -INFINITY;
+                xd[j] = in ? load_elem<DT>(drow, v + j) : -INFINITY;
+            }
         }
+        f(v, xt, xd, cnt);
     }
-    for (; v < b; ++v) s += resid_weight(load_elem<DT>(trow, v), load_elem<DT>(drow, v), rd, c);
-    return s;
 }
 
-// First entry of [a, b) where the running sum, started at `run`, exceeds
-// `target`; -1 if none.  Same order of accumulation as range_sum.
-template <int DT>
-__device__ int64_t range_find(const void *trow, const void *drow, int64_t a, int64_t b,
-                              const RowDist &rd, double c, double run, double target) {
-    for (int64_t v = a; v < b; ++v) {
-        run += resid_weight(load_elem<DT>(trow, v), load_elem<DT>(drow, v), rd, c);
-        if (run > target) return v;
+// ---- block reductions -----------------------------------------------------------
+
+// s * exp((m - M) / T): a partial sum taken at max m, rescaled to max M
+__device__ __forceinline__ double rescale(float m, double s, float M, double it) {
+    return m == -INFINITY ? 0.0 : s * exp(((double)m - (double)M) * it);
+}
+
+// Max and sum of exponentials from every thread's partial (m, s), target and
+// draft at once; every thread gets the workgroup's values.
+template <int NT>
+__device__ void block_stats(float &mt, double &st, float &md, double &sd, double it,
+                            float *sm, double *ss) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float wt = wave_max(mt), wd = wave_max(md);
+    const double rt = wave_sum_d(rescale(mt, st, wt, it));
+    const double rd = wave_sum_d(rescale(md, sd, wd, it));
+    if (lane == 0) {
+        sm[2 * wave] = wt;
+        sm[2 * wave + 1] = wd;
+        ss[2 * wave] = rt;
+        ss[2 * wave + 1] = rd;
     }
-    return -1;
+    __syncthreads();
+    float Mt = -INFINITY, Md = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        Mt = fmaxf(Mt, sm[2 * w]);
+        Md = fmaxf(Md, sm[2 * w + 1]);
+    }
+    double St = 0.0, Sd = 0.0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        St += rescale(sm[2 * w], ss[2 * w], Mt, it);
+        Sd += rescale(sm[2 * w + 1], ss[2 * w + 1], Md, it);
+    }
+    __syncthreads();
+    mt = Mt;
+    st = St;
+    md = Md;
+    sd = Sd;
 }
 
 // Exclusive prefix of v over threads in thread order; also returns the total.
-// Every workgroup that scans the same values gets the same results.
 template <int NT>
 __device__ double block_exclusive_scan(double v, double *scratch, double &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -172,87 +206,43 @@ __device__ double block_exclusive_scan(double v, double *scratch, double &total)
         if (w < wave) before += scratch[w];
         total += scratch[w];
     }
+    __syncthreads();
     return before + incl - v;
 }
 
-// ---------------------------------------------------------------------------
-// 1. statistics sweep
-// ---------------------------------------------------------------------------
-
-// Also empties the exchange slots of the walk that follows: row r of the
-// grid clears slots [r*G, r*G + G) (r = request * n + exchange).
-template <int DT>
-__global__ __launch_bounds__(kSweepThreads) void sample_stats_kernel(
-    const void *__restrict__ tlogits, const void *__restrict__ dlogits, int64_t vocab, int n,
-    int nchunks, bool vec_ok, const float *__restrict__ temperature,
-    SamplePart *__restrict__ part, uint64_t *__restrict__ xch, int G) {
-    const int c = blockIdx.x;
-    const int64_t row = blockIdx.y;
-    const int tid = threadIdx.x;
-    if (xch != nullptr && c == 0)
-        for (int j = tid; j < G; j += kSweepThreads) xch[row * G + j] = kEmpty;
-    const int64_t start = (int64_t)c * kChunk;
-    const int64_t end = min(vocab, start + kChunk);
-    const size_t eb = DT == SPEC_BF16 ? 2 : 4;
-    float xt[kPerThread], xd[kPerThread];
-    load_chunk<DT>(static_cast<const char *>(tlogits) + row * vocab * eb, start, end, vec_ok, tid, xt);
-    load_chunk<DT>(static_cast<const char *>(dlogits) + row * vocab * eb, start, end, vec_ok, tid, xd);
-    float mt = -INFINITY, md = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) { mt = fmaxf(mt, xt[e]); md = fmaxf(md, xd[e]); }
-    mt = wave_max(mt);
-    md = wave_max(md);
-    __shared__ float s_m[2][kSweepThreads / SPEC_WAVE];
-    __shared__ double s_s[2][kSweepThreads / SPEC_WAVE];
-    if ((tid & 63) == 0) { s_m[0][tid >> 6] = mt; s_m[1][tid >> 6] = md; }
+template <int NT>
+__device__ double block_sum(double v, double *scratch) {
+    v = wave_sum_d(v);
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
     __syncthreads();
+    double s = 0.0;
 #pragma unroll
-    for (int w = 0; w < kSweepThreads / SPEC_WAVE; ++w) {
-        mt = fmaxf(mt, s_m[0][w]);
-        md = fmaxf(md, s_m[1][w]);
-    }
-    const double it = 1.0 / (double)temperature[row / n];
-    const Scale sct{mt, (float)it, (float)(it - (double)(float)it)};
-    const Scale scd{md, sct.ithi, sct.itlo};
-    float st = 0.f, sd = 0.f;
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-        if (xt[e] != -INFINITY) st += exp_scaled(xt[e], sct);
-        if (xd[e] != -INFINITY) sd += exp_scaled(xd[e], scd);
-    }
-    double dst = wave_sum_d((double)st);
-    double dsd = wave_sum_d((double)sd);
-    if ((tid & 63) == 0) { s_s[0][tid >> 6] = dst; s_s[1][tid >> 6] = dsd; }
+    for (int w = 0; w < NT / 64; ++w) s += scratch[w];
     __syncthreads();
-    if (tid == 0) {
-        dst = 0.0;
-        dsd = 0.0;
-        for (int w = 0; w < kSweepThreads / SPEC_WAVE; ++w) { dst += s_s[0][w]; dsd += s_s[1][w]; }
-        part[row * nchunks + c] = SamplePart{mt, md, dst, dsd};
-    }
+    return s;
 }
 
 // ---------------------------------------------------------------------------
-// 2. the walk
+// the walk
 // ---------------------------------------------------------------------------
 
 struct WalkArgs {
-    int n, s1, nchunks;
+    int n, s1;
     int64_t vocab;
     bool vec_ok;
-    const SamplePart *part;
     const void *tlogits, *dlogits;
     const float *temperature, *uniforms, *final_uniforms;
     const int32_t *cand, *r_index, *r_next, *r_sib;
     int32_t *predict, *accept_index, *accept_length, *status;
     int G;              // workgroups per request (1: one workgroup, no exchange)
     int64_t slice;      // vocabulary entries per workgroup, a multiple of 8 * threads
-    uint64_t *xch;      // [batch][n][G] exchange slots (G > 1)
+    int E;              // exchanges a request may make
+    uint64_t *xch;      // [batch][E][G][kWords] exchange slots (G > 1)
+    unsigned *done;     // [batch] workgroups finished (G > 1)
 };
 
 template <int NT>
 struct WalkShared {
-    RowDist dist[kMaxNodes];   // by local verify row
     float cxt[kMaxNodes];      // node k's token: target / draft logit in its parent's row
     float cxd[kMaxNodes];
     int cand[kMaxNodes], next[kMaxNodes], sib[kMaxNodes], par[kMaxNodes];
@@ -260,39 +250,36 @@ struct WalkShared {
     int pred[kMaxNodes];
     int ai[kMaxNodes + 1];
     float unif[kMaxNodes];
+    float sm[2 * NT / 64];
+    double ss[2 * NT / 64];
     double scratch[NT / 64];
     double bcast;
-    int err, owner, draw;
+    RowDist dist;
+    int err, owner, draw, last;
 };
 
-// Running (max, scaled sum) of softmax chunk statistics:
-// S = sum_chunks s_k * exp((m_k - M) / T) with M the largest m_k so far.
-__device__ __forceinline__ void merge_stat(float &M, double &Sm, float m2, double s2, double it) {
-    if (m2 == -INFINITY) return;                  // an empty chunk (its sum is 0)
-    if (M == -INFINITY) { M = m2; Sm = s2; return; }
-    if (m2 > M) {
-        Sm = Sm * exp(((double)M - (double)m2) * it) + s2;
-        M = m2;
-    } else {
-        Sm += s2 * exp(((double)m2 - (double)M) * it);
-    }
-}
-
-// Poll one exchange slot until it is written (bounded); false on timeout.
-__device__ __forceinline__ bool read_slot(uint64_t *slot, double &v) {
+// Poll one exchange word until it is written (bounded); false on timeout.
+__device__ __forceinline__ bool read_word(uint64_t *slot, uint64_t &bits) {
     unsigned spins = 0;
-    uint64_t bits;
-    while ((bits = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == kEmpty) {
-        if (++spins > kSpinLimit) { v = 0.0; return false; }
+    uint64_t w;
+    while ((w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+        if (++spins > kSpinLimit) {
+            bits = 0;
+            return false;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
-    v = __builtin_bit_cast(double, bits);
+    bits = w ^ kFlip;
     return true;
+}
+
+__device__ __forceinline__ void write_word(uint64_t *slot, uint64_t bits) {
+    __hip_atomic_store(slot, encode_bits(bits), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int DT, int NT, bool COOP>
 __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
-    static_assert(NT % 64 == 0 && 64 % (NT / 64) == 0, "lanes per row must divide a wave");
+    static_assert(NT % 64 == 0, "whole waves");
     __shared__ WalkShared<NT> S;
     const int G = COOP ? A.G : 1;
     const int req = COOP ? blockIdx.x / G : blockIdx.x;
@@ -302,6 +289,8 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     const int base = req * n;
     const size_t eb = DT == SPEC_BF16 ? 2 : 4;
     const double it = 1.0 / (double)A.temperature[req];
+    const float ithi = (float)it;
+    const float itlo = (float)(it - (double)ithi);
 
     // my slice of the vocabulary and, inside it, my contiguous segment
     const int64_t v0 = min(A.vocab, (int64_t)g * A.slice);
@@ -309,88 +298,18 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     const int64_t seg = A.slice / NT;
     const int64_t sa = min(v1, v0 + tid * seg);
     const int64_t sb = min(v1, sa + seg);
+    auto row_ptr = [&](const void *m, int lrow) {
+        return static_cast<const char *>(m) + (int64_t)(base + lrow) * A.vocab * eb;
+    };
 
-    // ---- prologue: links, uniforms and the statistics of every row -------
-    if (tid < n) {
-        int row = A.r_index[base + tid];
-        row = (row >= base && row < base + n) ? row - base : -1;
-        S.row[tid] = row;
-        S.pred[tid] = 0;
-        S.par[tid] = -1;
-        S.cand[tid] = A.cand[base + tid];
-        S.next[tid] = A.r_next[base + tid];
-        S.sib[tid] = A.r_sib[base + tid];
-        S.unif[tid] = A.uniforms[base + tid];
-    }
-    if (tid == 0) S.err = 0;
-    {
-        constexpr int LPR = NT / 64;                  // lanes per row (n <= 64)
-        const int k = tid / LPR, sub = tid % LPR;
-        float mt = -INFINITY, md = -INFINITY;
-        double st = 0.0, sd = 0.0;
-        if (k < n) {
-            for (int c = sub; c < A.nchunks; c += LPR) {
-                const SamplePart p = A.part[(int64_t)(base + k) * A.nchunks + c];
-                merge_stat(mt, st, p.mt, p.st, it);
-                merge_stat(md, sd, p.md, p.sd, it);
-            }
-        }
-#pragma unroll
-        for (int o = 1; o < LPR; o <<= 1) {
-            const float omt = __shfl_xor(mt, o, 64), omd = __shfl_xor(md, o, 64);
-            const double ost = __shfl_xor(st, o, 64), osd = __shfl_xor(sd, o, 64);
-            merge_stat(mt, st, omt, ost, it);
-            merge_stat(md, sd, omd, osd, it);
-        }
-        if (k < n && sub == 0) {
-            const float ithi = (float)it;
-            const float itlo = (float)(it - (double)ithi);
-            RowDist rd;
-            rd.t = Scale{mt, ithi, itlo};
-            rd.d = Scale{md, ithi, itlo};
-            rd.inv_st = st > 0.0 ? 1.0 / st : 0.0;
-            rd.inv_sd = sd > 0.0 ? 1.0 / sd : 0.0;
-            S.dist[k] = rd;
-        }
-    }
-    __syncthreads();
-    if (tid < n) {
-        if (S.row[tid] < 0) atomicOr(&S.err, SPEC_ST_RANGE);
-        int c = S.next[tid];
-        for (int steps = 0; steps < n && c != -1; ++steps) {
-            if (c < 0 || c >= n) { atomicOr(&S.err, SPEC_ST_RANGE); break; }
-            S.par[c] = tid;
-            c = S.sib[c];
-        }
-    }
-    __syncthreads();
-    if (tid < n) {
-        const int p = S.par[tid];
-        const int t = S.cand[tid];
-        float xt = 0.f, xd = 0.f;
-        if (p >= 0 && S.row[p] >= 0 && t >= 0 && t < A.vocab) {
-            const int64_t grow = base + S.row[p];
-            xt = load_elem<DT>(static_cast<const char *>(A.tlogits) + grow * A.vocab * eb, t);
-            xd = load_elem<DT>(static_cast<const char *>(A.dlogits) + grow * A.vocab * eb, t);
-        }
-        S.cxt[tid] = xt;
-        S.cxd[tid] = xd;
-    }
-    __syncthreads();
-
-    // ---- the walk (every thread takes the same decisions) --------------------
-    int e = 0;                         // exchanges used so far (slots of this request)
-    bool alive = true;
-    double mine = 0.0, before = 0.0;   // my segment's sum and its prefix in my slice
-    double sj = 0.0, pre = 0.0;        // thread j < G: slice j's sum and its prefix
-    // The current node's row segment, as the exponentials exp_scaled gives
-    // (target, draft; 0 past the segment), kept in registers when the segment
-    // fits: later rejections at the node and its terminal draw then read no
-    // memory.
+    // The current row's segment in registers when it fits: raw logits on
+    // arrival, their exponentials once the row statistics are known.
     const bool use_cache = COOP && seg <= kCacheEntries;   // the solo walk's segments are longer
-    float cet[kCacheEntries], ced[kCacheEntries];
-    int cached_row = -1;
-    auto fill_cache = [&](const void *trow, const void *drow, const RowDist &rd) {
+    float ct[kCacheEntries], cd[kCacheEntries];
+    int cached_row = -1;               // local row whose raw logits ct / cd hold
+    auto load_cache = [&](int lrow) {
+        const void *trow = row_ptr(A.tlogits, lrow);
+        const void *drow = row_ptr(A.dlogits, lrow);
 #pragma unroll
         for (int i0 = 0; i0 < kCacheEntries; i0 += 8) {
             float xt[8], xd[8];
@@ -408,83 +327,228 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                cet[i0 + j] = exp_scaled(xt[j], rd.t);
-                ced[i0 + j] = exp_scaled(xd[j], rd.d);
+                ct[i0 + j] = xt[j];
+                cd[i0 + j] = xd[j];
             }
         }
+        cached_row = lrow;
     };
-    auto cached_weight = [&](int i, const RowDist &rd, double cc) -> double {
-        const double p = (double)cet[i] * rd.inv_st;
-        const double q = (double)ced[i] * rd.inv_sd;
-        return fmax(fma(-cc, q, p), 0.0);
-    };
-    // sweep of the current node's row (local row lr) with multiplier cc;
-    // returns F(cc)
-    auto sweep = [&](const void *trow, const void *drow, const RowDist &rd, int lr,
-                     double cc) -> double {
-        if (use_cache) {
-            if (cached_row != lr) {
-                fill_cache(trow, drow, rd);
-                cached_row = lr;
+
+    // ---- prologue: links and uniforms; the root's slice is fetched meanwhile
+    // (local row 0, the usual layout; fetched again on arrival if the root
+    // names another row) --------------------------------------------------------
+    if (tid < n) {
+        int row = A.r_index[base + tid];
+        row = (row >= base && row < base + n) ? row - base : -1;
+        S.row[tid] = row;
+        S.pred[tid] = 0;
+        S.par[tid] = -1;
+        S.cand[tid] = A.cand[base + tid];
+        S.next[tid] = A.r_next[base + tid];
+        S.sib[tid] = A.r_sib[base + tid];
+        S.unif[tid] = A.uniforms[base + tid];
+    }
+    if (tid == 0) S.err = 0;
+    if (use_cache) load_cache(0);
+    __syncthreads();
+    if (tid < n) {
+        if (S.row[tid] < 0) atomicOr(&S.err, SPEC_ST_RANGE);
+        int c = S.next[tid];
+        for (int steps = 0; steps < n && c != -1; ++steps) {
+            if (c < 0 || c >= n) {
+                atomicOr(&S.err, SPEC_ST_RANGE);
+                break;
             }
-            double m = 0.0;
-#pragma unroll
-            for (int i = 0; i < kCacheEntries; ++i) m += cached_weight(i, rd, cc);
-            mine = m;
-        } else {
-            mine = range_sum<DT>(trow, drow, sa, sb, A.vec_ok, rd, cc);
+            S.par[c] = tid;
+            c = S.sib[c];
         }
-        double slice_tot;
-        before = block_exclusive_scan<NT>(mine, S.scratch, slice_tot);
+    }
+    __syncthreads();
+
+    // ---- exchanges (uniform across the request's workgroups) -----------------
+    int e = 0;                         // exchanges used so far
+    bool alive = true;
+    auto slot = [&](int ex, int wg) -> uint64_t * {
+        return A.xch + (((int64_t)req * A.E + ex) * G + wg) * kWords;
+    };
+    // row statistics from every workgroup's slice statistics
+    auto exchange_stats = [&](float mt, double st, float md, double sd) -> RowDist {
+        if (COOP) {
+            if (e >= A.E) {
+                if (tid == 0) atomicOr(&S.err, SPEC_ST_RANGE | SPEC_ST_SYNC);
+            } else {
+                if (tid == 0) {
+                    const uint64_t mm = (uint64_t)__float_as_uint(mt) |
+                                        ((uint64_t)__float_as_uint(md) << 32);
+                    write_word(slot(e, g) + 0, mm);
+                    write_word(slot(e, g) + 1, __builtin_bit_cast(uint64_t, st));
+                    write_word(slot(e, g) + 2, __builtin_bit_cast(uint64_t, sd));
+                }
+                if (tid < 64) {
+                    float jmt = -INFINITY, jmd = -INFINITY;
+                    double jst = 0.0, jsd = 0.0;
+                    if (tid < G) {
+                        uint64_t w0 = 0, w1 = 0, w2 = 0;
+                        const bool ok = read_word(slot(e, tid) + 0, w0) &&
+                                        read_word(slot(e, tid) + 1, w1) &&
+                                        read_word(slot(e, tid) + 2, w2);
+                        if (!ok) {
+                            atomicOr(&S.err, SPEC_ST_SYNC);
+                        } else {
+                            jmt = __uint_as_float((uint32_t)w0);
+                            jmd = __uint_as_float((uint32_t)(w0 >> 32));
+                            jst = __builtin_bit_cast(double, w1);
+                            jsd = __builtin_bit_cast(double, w2);
+                        }
+                    }
+                    mt = wave_max(jmt);
+                    md = wave_max(jmd);
+                    st = wave_sum_d(rescale(jmt, jst, mt, it));
+                    sd = wave_sum_d(rescale(jmd, jsd, md, it));
+                }
+                ++e;
+            }
+        }
+        if (tid == 0) {
+            RowDist r;
+            r.t = Scale{mt, ithi, itlo};
+            r.d = Scale{md, ithi, itlo};
+            r.inv_st = st > 0.0 ? 1.0 / st : 0.0;
+            r.inv_sd = sd > 0.0 ? 1.0 / sd : 0.0;
+            S.dist = r;
+        }
+        __syncthreads();
+        if (S.err & SPEC_ST_SYNC) alive = false;
+        const RowDist r = S.dist;
+        __syncthreads();
+        return r;
+    };
+    double sj = 0.0;                   // wave 0, lane j < G: slice j's sum in the last sweep
+    // total over the slices of a per-workgroup sum
+    auto exchange_sum = [&](double slice_sum) -> double {
         if (!COOP) {
-            sj = slice_tot;
-            pre = 0.0;
-            return slice_tot;
+            sj = slice_sum;
+            return slice_sum;
         }
-        if (e >= n) {                      // more exchanges than a tree of n nodes needs
+        if (e >= A.E) {
             if (tid == 0) atomicOr(&S.err, SPEC_ST_RANGE | SPEC_ST_SYNC);
             __syncthreads();
             alive = false;
             return 0.0;
         }
-        uint64_t *slots = A.xch + ((int64_t)base + e) * G;
-        ++e;
-        if (tid == 0) {
-            uint64_t bits = __builtin_bit_cast(uint64_t, slice_tot);
-            if (bits == kEmpty) bits = kQuietNaN;
-            __hip_atomic_store(slots + g, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) write_word(slot(e, g), __builtin_bit_cast(uint64_t, slice_sum));
+        if (tid < 64) {
+            sj = 0.0;
+            uint64_t w = 0;
+            if (tid < G) {
+                if (read_word(slot(e, tid), w)) sj = __builtin_bit_cast(double, w);
+                else atomicOr(&S.err, SPEC_ST_SYNC);
+            }
+            const double tot = wave_sum_d(sj);
+            if (tid == 0) S.bcast = tot;
         }
-        sj = 0.0;
-        if (tid < G && !read_slot(slots + tid, sj)) atomicOr(&S.err, SPEC_ST_SYNC);
-        double tot;
-        pre = block_exclusive_scan<NT>(sj, S.scratch, tot);   // also publishes the err bit
+        ++e;
+        __syncthreads();
         if (S.err & SPEC_ST_SYNC) alive = false;
+        const double tot = S.bcast;
+        __syncthreads();
         return tot;
     };
-    // first entry of my segment where the running sum from `before` exceeds tgt
-    auto find = [&](const void *trow, const void *drow, const RowDist &rd, double cc,
-                    double tgt) -> int64_t {
-        if (!use_cache) return range_find<DT>(trow, drow, sa, sb, rd, cc, before, tgt);
-        double run = before;
-        int64_t x = -1;
-#pragma unroll
-        for (int i = 0; i < kCacheEntries; ++i) {
-            run += cached_weight(i, rd, cc);
-            if (x < 0 && run > tgt) x = sa + i;
-        }
-        return x < sb ? x : -1;
-    };
 
+    // ---- the walk (every thread takes the same decisions) --------------------
+    double mine = 0.0;                 // my segment's sum in the last sweep
     int cur = 0, cnt = 0;
     if (tid == 0) S.ai[0] = base + max(S.row[0], 0);
     double c = 0.0, F = 1.0;
-    bool swept = false;        // the last sweep was of the current node with multiplier c
+    bool swept = false;                // the last sweep was of the current node with multiplier c
+    RowDist rd{};
+    int lr = -1;
+    // sum of my segment's residual weights with multiplier cc
+    auto segment_sum = [&](double cc) -> double {
+        double m = 0.0;
+        if (use_cache) {
+#pragma unroll
+            for (int i = 0; i < kCacheEntries; ++i) m += resid_from_exp(ct[i], cd[i], rd, cc);
+        } else {
+            for_each8<DT>(row_ptr(A.tlogits, lr), row_ptr(A.dlogits, lr), sa, sb, A.vec_ok,
+                          [&](int64_t, const float (&xt)[8], const float (&xd)[8], int) {
+#pragma unroll
+                              for (int j = 0; j < 8; ++j)
+                                  m += resid_from_exp(exp_scaled(xt[j], rd.t),
+                                                      exp_scaled(xd[j], rd.d), rd, cc);
+                          });
+        }
+        return m;
+    };
+    auto sweep = [&](double cc) -> double {
+        mine = segment_sum(cc);
+        return exchange_sum(block_sum<NT>(mine, S.scratch));
+    };
+
     for (int level = 0; level < n && alive; ++level) {
-        const int lr = S.row[cur];
+        lr = S.row[cur];
         if (lr < 0) break;
-        const RowDist rd = S.dist[lr];
-        const void *trow = static_cast<const char *>(A.tlogits) + (int64_t)(base + lr) * A.vocab * eb;
-        const void *drow = static_cast<const char *>(A.dlogits) + (int64_t)(base + lr) * A.vocab * eb;
+        // arrival: the children's token logits, this row's slice, its statistics
+        if (tid < n && S.par[tid] == cur) {
+            const int t = S.cand[tid];
+            const bool ok = t >= 0 && t < A.vocab;
+            S.cxt[tid] = ok ? load_elem<DT>(row_ptr(A.tlogits, lr), t) : 0.f;
+            S.cxd[tid] = ok ? load_elem<DT>(row_ptr(A.dlogits, lr), t) : 0.f;
+        }
+        float mt = -INFINITY, md = -INFINITY;
+        double st = 0.0, sd = 0.0;
+        if (use_cache) {
+            if (cached_row != lr) load_cache(lr);
+#pragma unroll
+            for (int i = 0; i < kCacheEntries; ++i) {
+                mt = fmaxf(mt, ct[i]);
+                md = fmaxf(md, cd[i]);
+            }
+            const Scale sct{mt, ithi, itlo}, scd{md, ithi, itlo};
+            float ft = 0.f, fd = 0.f;
+#pragma unroll
+            for (int i = 0; i < kCacheEntries; ++i) {
+                ft += exp_scaled(ct[i], sct);
+                fd += exp_scaled(cd[i], scd);
+            }
+            st = ft;
+            sd = fd;
+        } else {
+            const void *trow = row_ptr(A.tlogits, lr);
+            const void *drow = row_ptr(A.dlogits, lr);
+            for_each8<DT>(trow, drow, sa, sb, A.vec_ok,
+                          [&](int64_t, const float (&xt)[8], const float (&xd)[8], int) {
+#pragma unroll
+                              for (int j = 0; j < 8; ++j) {
+                                  mt = fmaxf(mt, xt[j]);
+                                  md = fmaxf(md, xd[j]);
+                              }
+                          });
+            const Scale sct{mt, ithi, itlo}, scd{md, ithi, itlo};
+            float ft = 0.f, fd = 0.f;
+            for_each8<DT>(trow, drow, sa, sb, A.vec_ok,
+                          [&](int64_t, const float (&xt)[8], const float (&xd)[8], int) {
+#pragma unroll
+                              for (int j = 0; j < 8; ++j) {
+                                  ft += exp_scaled(xt[j], sct);
+                                  fd += exp_scaled(xd[j], scd);
+                              }
+                          });
+            st = ft;
+            sd = fd;
+        }
+        block_stats<NT>(mt, st, md, sd, it, S.sm, S.ss);
+        rd = exchange_stats(mt, st, md, sd);
+        if (!alive) break;
+        if (use_cache) {
+#pragma unroll
+            for (int i = 0; i < kCacheEntries; ++i) {
+                ct[i] = exp_scaled(ct[i], rd.t);
+                cd[i] = exp_scaled(cd[i], rd.d);
+            }
+            cached_row = -1;           // the registers now hold exponentials
+        }
+
         c = 0.0;
         F = 1.0;
         swept = false;
@@ -503,10 +567,13 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             } else if (tid == 0) {
                 atomicOr(&S.err, SPEC_ST_RANGE);
             }
-            if (dec) { hit = k; break; }
+            if (dec) {
+                hit = k;
+                break;
+            }
             // rejected: F(c + F)
             const double cn = c + F;
-            const double Fn = sweep(trow, drow, rd, lr, cn);
+            const double Fn = sweep(cn);
             if (!alive) break;
             if (Fn > 0.0) {
                 c = cn;
@@ -532,35 +599,72 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     }
 
     // ---- terminal draw: inverse CDF of max(0, p - c q) in vocabulary order ----
-    const int lr = S.row[cur];
     bool terminal_written = false;
-    if (alive && lr >= 0) {
-        const RowDist rd = S.dist[lr];
-        const void *trow = static_cast<const char *>(A.tlogits) + (int64_t)(base + lr) * A.vocab * eb;
-        const void *drow = static_cast<const char *>(A.dlogits) + (int64_t)(base + lr) * A.vocab * eb;
+    if (alive && lr >= 0 && lr == S.row[cur]) {
         // after a rejection at this node the last sweep's sums are this residual's
-        const double tot = swept ? F : sweep(trow, drow, rd, lr, c);
+        const double tot = swept ? F : sweep(c);
         if (alive) {
             const double target = (double)A.final_uniforms[req] * tot;
-            if (tid == 0) { S.owner = INT_MAX; S.draw = INT_MAX; }
+            if (tid == 0) {
+                S.owner = INT_MAX;
+                S.draw = INT_MAX;
+            }
             __syncthreads();
             if (COOP) {
-                if (tid < G && sj > 0.0 && pre <= target && target < pre + sj) atomicMin(&S.owner, tid);
+                if (tid < 64) {
+                    // slice prefix sums in slice order; the owner holds the crossing
+                    double incl = sj;
+#pragma unroll
+                    for (int o = 1; o < 64; o <<= 1) {
+                        const double x = __shfl_up(incl, o, 64);
+                        if (tid >= o) incl += x;
+                    }
+                    const double pre = incl - sj;
+                    const bool here = tid < G && sj > 0.0 && pre <= target && target < pre + sj;
+                    const uint64_t bal = __ballot(here);
+                    if (bal != 0 && tid == __builtin_ctzll(bal)) {
+                        S.owner = tid;
+                        S.bcast = target - pre;
+                    }
+                }
             } else if (tid == 0 && target < tot) {
                 S.owner = 0;
+                S.bcast = target;
             }
             __syncthreads();
             const int owner = S.owner;
-            if (COOP && tid == owner) S.bcast = target - pre;   // target measured from its slice
-            __syncthreads();
+            const double tgt = S.bcast;
             if (owner == INT_MAX) {
                 // no crossing: the target sits at the very end of the mass
                 if (g == 0 && tid == 0) A.predict[base + lr] = (int)(A.vocab - 1);
             } else if (owner == g) {
-                const double tgt = COOP ? S.bcast : target;
+                double slice_tot;
+                const double before = block_exclusive_scan<NT>(mine, S.scratch, slice_tot);
                 if (sa < sb && before <= tgt && tgt < before + mine) {
-                    const int64_t x = find(trow, drow, rd, c, tgt);
-                    if (x >= 0) atomicMin(&S.draw, (int)x);
+                    // first entry of my segment where the running sum crosses tgt
+                    double run = before;
+                    int64_t x = -1;
+                    if (use_cache) {
+#pragma unroll
+                        for (int i = 0; i < kCacheEntries; ++i) {
+                            run += resid_from_exp(ct[i], cd[i], rd, c);
+                            if (x < 0 && run > tgt) x = sa + i;
+                        }
+                    } else {
+                        for_each8<DT>(row_ptr(A.tlogits, lr), row_ptr(A.dlogits, lr), sa, sb,
+                                      A.vec_ok,
+                                      [&](int64_t v, const float (&xt)[8], const float (&xd)[8],
+                                          int cnt) {
+                                          if (x >= 0) return;
+#pragma unroll
+                                          for (int j = 0; j < 8; ++j) {
+                                              run += resid_from_exp(exp_scaled(xt[j], rd.t),
+                                                                    exp_scaled(xd[j], rd.d), rd, c);
+                                              if (x < 0 && j < cnt && run > tgt) x = v + j;
+                                          }
+                                      });
+                    }
+                    if (x >= 0 && x < sb) atomicMin(&S.draw, (int)x);
                 }
                 __syncthreads();
                 if (tid == 0) {
@@ -581,6 +685,25 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
         if (tid == 0) A.accept_length[req] = cnt + 1;
     }
     if (tid == 0) raise_status(A.status, S.err);
+
+    // the last workgroup of the request to get here clears the request's
+    // slots: every other one has read all it will read
+    if (COOP) {
+        if (tid == 0) {
+            const unsigned old = __hip_atomic_fetch_add(A.done + req, 1u, __ATOMIC_ACQ_REL,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            S.last = old == (unsigned)G - 1;
+        }
+        __syncthreads();
+        if (S.last) {
+            const int used = (S.err & SPEC_ST_SYNC) ? A.E : e;
+            uint64_t *x = A.xch + (int64_t)req * A.E * G * kWords;
+            for (int i = tid; i < used * G * kWords; i += NT)
+                __hip_atomic_store(x + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0)
+                __hip_atomic_store(A.done + req, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -589,9 +712,14 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
 
 constexpr int64_t kMinSlice = (int64_t)kCoopThreads * 8;
 
-int max_groups(int64_t vocab) {
-    return (int)std::min<int64_t>((vocab + kMinSlice - 1) / kMinSlice, kCoopThreads);
+// upper bound of the workgroups per request the plan can pick
+int group_cap(int batch, int64_t vocab) {
+    int64_t G = std::min<int64_t>((vocab + kMinSlice - 1) / kMinSlice, kMaxGroups);
+    G = std::min<int64_t>(G, std::max(2, kCoopGridTarget / std::max(batch, 1)));
+    return (int)std::max<int64_t>(G, 1);
 }
+
+int exchanges_per_request(int n) { return 2 * n + 2; }
 
 struct CoopPlan {
     int G;
@@ -615,9 +743,8 @@ CoopPlan coop_plan(int batch, int64_t vocab) {
         cap = (ok && coop) ? cus * per : 0;
         cached_device = dev;
     }
-    int64_t G = max_groups(vocab);
+    int64_t G = group_cap(batch, vocab);
     G = std::min<int64_t>(G, cap / std::max(batch, 1));
-    G = std::min<int64_t>(G, std::max(2, kCoopGridTarget / std::max(batch, 1)));
     if (G < 2) return CoopPlan{0, 0};
     int64_t slice = (vocab + G - 1) / G;
     slice = (slice + kMinSlice - 1) / kMinSlice * kMinSlice;
@@ -626,11 +753,12 @@ CoopPlan coop_plan(int batch, int64_t vocab) {
     return CoopPlan{(int)G, slice};
 }
 
-size_t sample_workspace_layout(int batch, int n, int64_t vocab, size_t *off_xch) {
-    const size_t parts = spec::align_up((size_t)batch * n * num_chunks(vocab) * sizeof(SamplePart), 256);
-    const size_t xch = spec::align_up((size_t)batch * n * max_groups(vocab) * sizeof(uint64_t), 256);
-    if (off_xch) *off_xch = parts;
-    return parts + xch;
+size_t sample_workspace_layout(int batch, int n, int64_t vocab, size_t *off_done) {
+    const size_t xch = spec::align_up((size_t)batch * exchanges_per_request(n) *
+                                          group_cap(batch, vocab) * kWords * sizeof(uint64_t),
+                                      256);
+    if (off_done) *off_done = xch;
+    return xch + spec::align_up((size_t)batch * sizeof(unsigned), 256);
 }
 
 template <int DT>
@@ -639,24 +767,32 @@ int launch_sample(int batch, int n, int s1, int64_t vocab, const void *tl, const
                   const int32_t *cand, const int32_t *ri, const int32_t *rn, const int32_t *rs,
                   int32_t *predict, int32_t *ai, int32_t *al, void *workspace,
                   int32_t *dev_status, hipStream_t st) {
-    size_t off_xch = 0;
-    sample_workspace_layout(batch, n, vocab, &off_xch);
-    const int nch = num_chunks(vocab);
+    size_t off_done = 0;
+    sample_workspace_layout(batch, n, vocab, &off_done);
     const size_t eb = DT == SPEC_BF16 ? 2 : 4;
-    const bool vec_ok = (vocab * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(tl) % 16 == 0 &&
-                        reinterpret_cast<uintptr_t>(dl) % 16 == 0;
-    SamplePart *part = static_cast<SamplePart *>(workspace);
-    uint64_t *xch = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + off_xch);
-    const CoopPlan pl = coop_plan<DT>(batch, vocab);
-    hipLaunchKernelGGL(sample_stats_kernel<DT>, dim3(nch, batch * n), dim3(kSweepThreads), 0, st,
-                       tl, dl, vocab, n, nch, vec_ok, temperature, part,
-                       pl.G >= 2 ? xch : nullptr, pl.G);
     WalkArgs A{};
-    A.n = n; A.s1 = s1; A.nchunks = nch; A.vocab = vocab; A.vec_ok = vec_ok; A.part = part;
-    A.tlogits = tl; A.dlogits = dl; A.temperature = temperature; A.uniforms = uniforms;
-    A.final_uniforms = final_uniforms; A.cand = cand; A.r_index = ri; A.r_next = rn;
-    A.r_sib = rs; A.predict = predict; A.accept_index = ai; A.accept_length = al;
-    A.status = dev_status; A.xch = xch;
+    A.n = n;
+    A.s1 = s1;
+    A.vocab = vocab;
+    A.vec_ok = (vocab * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(tl) % 16 == 0 &&
+               reinterpret_cast<uintptr_t>(dl) % 16 == 0;
+    A.tlogits = tl;
+    A.dlogits = dl;
+    A.temperature = temperature;
+    A.uniforms = uniforms;
+    A.final_uniforms = final_uniforms;
+    A.cand = cand;
+    A.r_index = ri;
+    A.r_next = rn;
+    A.r_sib = rs;
+    A.predict = predict;
+    A.accept_index = ai;
+    A.accept_length = al;
+    A.status = dev_status;
+    A.E = exchanges_per_request(n);
+    A.xch = static_cast<uint64_t *>(workspace);
+    A.done = reinterpret_cast<unsigned *>(static_cast<char *>(workspace) + off_done);
+    const CoopPlan pl = coop_plan<DT>(batch, vocab);
     if (pl.G >= 2) {
         A.G = pl.G;
         A.slice = pl.slice;
@@ -671,7 +807,7 @@ int launch_sample(int batch, int n, int s1, int64_t vocab, const void *tl, const
         void *args[] = {&A};
         const void *fn = reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true>);
         if (hipLaunchCooperativeKernel(fn, grid, block, args, 0, st) == hipSuccess) return SPEC_OK;
-        (void)hipGetLastError();   // fall back below; the emptied slots go unused
+        (void)hipGetLastError();   // fall back below
     }
     A.G = 1;
     A.slice = ((vocab + kSoloThreads - 1) / kSoloThreads + 7) / 8 * 8 * kSoloThreads;
@@ -707,6 +843,7 @@ extern "C" int spec_accept_sample(int batch, int n, int s1, int64_t vocab, int d
         return SPEC_ERR_NULL;
     if (!workspace || workspace_bytes < spec_accept_workspace_size(batch, n, vocab, 1))
         return SPEC_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return SPEC_ERR_WORKSPACE;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (dtype == SPEC_BF16)
         return launch_sample<SPEC_BF16>(batch, n, s1, vocab, target_logits, draft_logits,

@@ -112,7 +112,7 @@ def accept_sample(w, tl, dl, tree, temperature=None, uniforms=None, final_unifor
     b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
     ws = workspace
     if ws is None:
-        ws = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
+        ws = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
                          device=DEV)
     predict, ai, al, st = i32(b * n), i32(b * s1), i32(b), status()
     predict.fill_(-7)

@@ -73,7 +73,7 @@ def test_graph_replay_matches_eager(name, cfg):
         dtype=torch.uint8, device="cuda")
     ws_g = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
                        device="cuda")
-    ws_s = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
+    ws_s = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
                        device="cuda")
 
     def step():

@@ -10,8 +10,8 @@ the walk into its less common branches.
 * a one-hot draft distribution (every other draft logit -inf): q(t) = 0 for
   the other children, whose ratio is then infinite, and a residual that
   drops exactly one token;
-* two calls in a row on one workspace: the exchange slots of the first call
-  must not leak into the second.
+* three calls in a row on one workspace: each call must leave the workspace
+  zero-filled, as the next call expects it.
 
 Same bar as the other sampled tests: bit-exact outputs except for requests
 the oracle marks exempt (a decision within 1e-6 of its threshold, or a
@@ -121,10 +121,12 @@ def test_sample_one_hot_draft(dtype):
 def test_sample_workspace_reused():
     cfg = W.shrink(W.CONFIGS[3], batch=3, hist=H8, vocab=30000, draft_noise=2.0)
     b, n = cfg.batch, cfg.num_draft_tokens
-    ws = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
+    ws = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
                      device="cuda")
     for seed in (31, 32, 33):
         say(f"[sample reuse] seed {seed}")
         w, t, tl, dl = _setup(cfg, seed)
         g = G.accept_sample(w, tl, dl, _tree(t), workspace=ws)
         _check(w, t, tl, dl, g, f"seed {seed}")
+        # the call leaves the workspace as it found it: zero
+        assert int(torch.count_nonzero(ws)) == 0
