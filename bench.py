@@ -219,12 +219,24 @@ def _cpu_baseline(cfg, w, tl, dl, budget_s):
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"whole step except verify attention, which ran {done} of {pairs_total} "
+        "sample": ("whole step, float64 numpy, one thread" if done >= pairs_total else
+                   f"whole step except verify attention, which ran {done} of {pairs_total} "
                    f"(row, head) vectors and was scaled up; float64 numpy, one thread"),
         "op_seconds": {"build_tree": t_build, "verify_attention": t_attn,
                        "accept_greedy": t_greedy, "accept_sample": t_sample,
                        "compact_kv": t_compact},
     }
+
+
+def _traffic(cfg):
+    """HBM bytes per verify-attention call (both launches) from the committed
+    counter summary of this workload, or None when there is none or it was
+    taken on another version of the kernel source."""
+    from speculative_decoding_build_amd.profile_summary import read_traffic
+    root = os.path.dirname(os.path.abspath(__file__))
+    return read_traffic(os.path.join(root, "profiles", f"verify_attention_{cfg.name}_hbm.md"),
+                        os.path.join(root, "speculative_decoding_build_amd", "csrc",
+                                     "verify_attention.hip"))
 
 
 def main():
@@ -281,27 +293,42 @@ def main():
         run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample)
     torch.cuda.synchronize()
 
-    # per-operation GPU times: one graph per operation holding that operation
-    # for every input copy back to back, replayed between two events, so no
-    # host time falls between the launches
     calls = [op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample) for x in xs]
-    reps = max(2, math.ceil(64 / copies))
     op_ms = {}
-    for j, op in enumerate(OPS):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for c in calls:
-                c[j]()
-        g.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
+    if args.mode == "graph":
+        # per-operation GPU times: one graph per operation holding that
+        # operation for every input copy back to back, replayed between two
+        # events, so no host time falls between the launches
+        reps = max(2, math.ceil(64 / copies))
+        for j, op in enumerate(OPS):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in calls:
+                    c[j]()
             g.replay()
-        e1.record()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            op_ms[op] = e0.elapsed_time(e1) / (reps * copies)
+            del g
+    else:
+        # eager: events around every operation of eager steps (host launch
+        # time between operations is included)
+        k_ev = max(5, min(args.steps, 20))
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(k_ev)]
+        for i in range(k_ev):
+            c = calls[i % copies]
+            for j in range(5):
+                ev[i][j].record()
+                c[j]()
+            ev[i][5].record()
         torch.cuda.synchronize()
-        op_ms[op] = e0.elapsed_time(e1) / (reps * copies)
-        del g
+        for j, op in enumerate(OPS):
+            op_ms[op] = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
 
     # eager steps (every launch from Python)
     k_e = max(5, min(args.steps, 20))
@@ -356,7 +383,6 @@ def main():
     sweep_g = b * n * cfg.vocab * (2 if cfg.dtype == "bf16" else 4)
     attn_gbs = attn_bytes / (op_ms["verify_attention"] * 1e-3) / 1e9
     greedy_gbs = sweep_g / (op_ms["accept_greedy"] * 1e-3) / 1e9
-    sample_gbs = 2 * sweep_g / (op_ms["accept_sample"] * 1e-3) / 1e9
     accept_op = "accept_greedy" if "greedy" in cfg.accept else "accept_sample"
 
     line = {
@@ -379,19 +405,21 @@ def main():
                    "cached_tokens": int(w.seq_lens.sum()), "temperature": cfg.temperature,
                    "input_copies_rotated": copies},
         "mode": args.mode,
+        "op_timing": ("graph of the operation alone, events around the replays"
+                      if args.mode == "graph" else "events around eager launches"),
         "graph_replay_matches_eager": graph_check,
         "ms_per_step_eager": eager_ms,
         "accept_steps_per_s": b / (op_ms[accept_op] * 1e-3),
         "op_ms": op_ms,
         "verify_attn_gbs": attn_gbs,
         "verify_attn_frac_hbm": attn_gbs / HBM_PEAK_GBS,
-        "accept_sweep_gbs": {"greedy": greedy_gbs, "sample": sample_gbs},
+        "accept_greedy_sweep_gbs": greedy_gbs,
         "mean_accept_length": float(acc_len.mean()),
         "dev_status": status,
         "roofline": {"kernel": "spec_verify_attention (split-KV MFMA + merge launches)",
                      "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes": attn_bytes},
+                     "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
+                     "traffic": _traffic(cfg), "algorithmic_bytes": attn_bytes},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, w, tl, dl, args.cpu_budget_s)
