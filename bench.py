@@ -263,7 +263,7 @@ def main():
     ws_attn = torch.empty(max(1, S.spec_verify_attention_workspace_size(
         b, n, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, _MAXLEN[cfg.name], code)),
         dtype=torch.uint8, device="cuda")
-    ws_greedy = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
+    ws_greedy = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
                             device="cuda")
     ws_sample = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
                             device="cuda")

@@ -35,6 +35,9 @@ __global__ __launch_bounds__(kThreads) void compact_kv_kernel(
     const int b = blockIdx.x;
     const int layer = blockIdx.y;
     const int tid = threadIdx.x;
+    // the accepted row of move tid is read without waiting for the length,
+    // so both loads (and the sequence length) are in flight together
+    const int row_j = tid < s1 ? accept_index[(int64_t)b * s1 + tid] : -1;
     const int L = seq_lens[b];
     int acc = accept_length[b];
     int err = 0;
@@ -48,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void compact_kv_kernel(
         int64_t src = -1, tgt = -1;
         const int j = tid;
         if (j < acc) {
-            const int row = accept_index[(int64_t)b * s1 + j];
+            const int row = row_j;
             if (row >= 0) {
                 if (row >= total_rows) {
                     err |= SPEC_ST_RANGE;

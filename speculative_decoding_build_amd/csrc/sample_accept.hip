@@ -125,7 +125,7 @@ __device__ __forceinline__ void load8(const void *rowp, int64_t v, float (&x)[8]
 template <int DT, typename Fn>
 __device__ __forceinline__ void for_each8(const void *trow, const void *drow, int64_t a, int64_t b,
                                           bool vec_ok, Fn &&f) {
-#pragma unroll 4
+#pragma unroll 2
     for (int64_t v = a; v < b; v += 8) {
         float xt[8], xd[8];
         const int cnt = (int)min((int64_t)8, b - v);
@@ -147,19 +147,20 @@ __device__ __forceinline__ void for_each8(const void *trow, const void *drow, in
 // ---- block reductions -----------------------------------------------------------
 
 // s * exp((m - M) / T): a partial sum taken at max m, rescaled to max M
-__device__ __forceinline__ double rescale(float m, double s, float M, double it) {
-    return m == -INFINITY ? 0.0 : s * exp(((double)m - (double)M) * it);
+// (float exponential of the exactly formed argument; 0 for an empty part)
+__device__ __forceinline__ double rescale(float m, double s, float M, float ithi, float itlo) {
+    return m == -INFINITY ? 0.0 : s * (double)exp_scaled(m, Scale{M, ithi, itlo});
 }
 
 // Max and sum of exponentials from every thread's partial (m, s), target and
 // draft at once; every thread gets the workgroup's values.
 template <int NT>
-__device__ void block_stats(float &mt, double &st, float &md, double &sd, double it,
+__device__ void block_stats(float &mt, double &st, float &md, double &sd, float ithi, float itlo,
                             float *sm, double *ss) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float wt = wave_max(mt), wd = wave_max(md);
-    const double rt = wave_sum_d(rescale(mt, st, wt, it));
-    const double rd = wave_sum_d(rescale(md, sd, wd, it));
+    const double rt = wave_sum_d(rescale(mt, st, wt, ithi, itlo));
+    const double rd = wave_sum_d(rescale(md, sd, wd, ithi, itlo));
     if (lane == 0) {
         sm[2 * wave] = wt;
         sm[2 * wave + 1] = wd;
@@ -176,8 +177,8 @@ __device__ void block_stats(float &mt, double &st, float &md, double &sd, double
     double St = 0.0, Sd = 0.0;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) {
-        St += rescale(sm[2 * w], ss[2 * w], Mt, it);
-        Sd += rescale(sm[2 * w + 1], ss[2 * w + 1], Md, it);
+        St += rescale(sm[2 * w], ss[2 * w], Mt, ithi, itlo);
+        Sd += rescale(sm[2 * w + 1], ss[2 * w + 1], Md, ithi, itlo);
     }
     __syncthreads();
     mt = Mt;
@@ -403,8 +404,8 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                     }
                     mt = wave_max(jmt);
                     md = wave_max(jmd);
-                    st = wave_sum_d(rescale(jmt, jst, mt, it));
-                    sd = wave_sum_d(rescale(jmd, jsd, md, it));
+                    st = wave_sum_d(rescale(jmt, jst, mt, ithi, itlo));
+                    sd = wave_sum_d(rescale(jmd, jsd, md, ithi, itlo));
                 }
                 ++e;
             }
@@ -488,12 +489,17 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     for (int level = 0; level < n && alive; ++level) {
         lr = S.row[cur];
         if (lr < 0) break;
-        // arrival: the children's token logits, this row's slice, its statistics
-        if (tid < n && S.par[tid] == cur) {
+        // arrival: the children's token logits (kept in registers until the
+        // statistics are exchanged, so their loads overlap that work), this
+        // row's slice, its statistics
+        const bool is_child = tid < n && S.par[tid] == cur;
+        float kid_t = 0.f, kid_d = 0.f;
+        if (is_child) {
             const int t = S.cand[tid];
-            const bool ok = t >= 0 && t < A.vocab;
-            S.cxt[tid] = ok ? load_elem<DT>(row_ptr(A.tlogits, lr), t) : 0.f;
-            S.cxd[tid] = ok ? load_elem<DT>(row_ptr(A.dlogits, lr), t) : 0.f;
+            if (t >= 0 && t < A.vocab) {
+                kid_t = load_elem<DT>(row_ptr(A.tlogits, lr), t);
+                kid_d = load_elem<DT>(row_ptr(A.dlogits, lr), t);
+            }
         }
         float mt = -INFINITY, md = -INFINITY;
         double st = 0.0, sd = 0.0;
@@ -504,13 +510,18 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                 mt = fmaxf(mt, ct[i]);
                 md = fmaxf(md, cd[i]);
             }
+            // the registers now take the exponentials relative to this
+            // thread's max; one factor per row moves them to the row's max
             const Scale sct{mt, ithi, itlo}, scd{md, ithi, itlo};
             float ft = 0.f, fd = 0.f;
 #pragma unroll
             for (int i = 0; i < kCacheEntries; ++i) {
-                ft += exp_scaled(ct[i], sct);
-                fd += exp_scaled(cd[i], scd);
+                ct[i] = exp_scaled(ct[i], sct);
+                cd[i] = exp_scaled(cd[i], scd);
+                ft += ct[i];
+                fd += cd[i];
             }
+            cached_row = -1;
             st = ft;
             sd = fd;
         } else {
@@ -537,16 +548,23 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             st = ft;
             sd = fd;
         }
-        block_stats<NT>(mt, st, md, sd, it, S.sm, S.ss);
+        const float thr_mt = mt, thr_md = md;
+        block_stats<NT>(mt, st, md, sd, ithi, itlo, S.sm, S.ss);
         rd = exchange_stats(mt, st, md, sd);
+        if (is_child) {
+            S.cxt[tid] = kid_t;
+            S.cxd[tid] = kid_d;
+        }
+        __syncthreads();
         if (!alive) break;
         if (use_cache) {
+            const float ft = thr_mt == -INFINITY ? 0.f : exp_scaled(thr_mt, rd.t);
+            const float fd = thr_md == -INFINITY ? 0.f : exp_scaled(thr_md, rd.d);
 #pragma unroll
             for (int i = 0; i < kCacheEntries; ++i) {
-                ct[i] = exp_scaled(ct[i], rd.t);
-                cd[i] = exp_scaled(cd[i], rd.d);
+                ct[i] *= ft;
+                cd[i] *= fd;
             }
-            cached_row = -1;           // the registers now hold exponentials
         }
 
         c = 0.0;
@@ -559,11 +577,12 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             const int t = S.cand[k];
             bool dec = false;
             if (t >= 0 && t < A.vocab) {
+                // u < min(1, (max(0, p - c q) / F) / q), without the divisions
                 const double p = (double)exp_scaled(S.cxt[k], rd.t) * rd.inv_st;
                 const double q = (double)exp_scaled(S.cxd[k], rd.d) * rd.inv_sd;
-                const double r = fmax(fma(-c, q, p), 0.0) / F;
-                const double ratio = q > 0.0 ? r / q : (r > 0.0 ? INFINITY : 0.0);
-                dec = (double)S.unif[k] < fmin(1.0, ratio);
+                const double r = fmax(fma(-c, q, p), 0.0);
+                const double u = (double)S.unif[k];
+                dec = q > 0.0 ? (u < 1.0 && u * q * F < r) : (r > 0.0 ? u < 1.0 : u < 0.0);
             } else if (tid == 0) {
                 atomicOr(&S.err, SPEC_ST_RANGE);
             }
@@ -690,7 +709,11 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     // slots: every other one has read all it will read
     if (COOP) {
         if (tid == 0) {
-            const unsigned old = __hip_atomic_fetch_add(A.done + req, 1u, __ATOMIC_ACQ_REL,
+            // relaxed: this workgroup's slot reads have returned their values
+            // before the increment is issued, and the clearing needs nothing
+            // else from the others (an acquire / release here would write back
+            // the L2 on every workgroup)
+            const unsigned old = __hip_atomic_fetch_add(A.done + req, 1u, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
             S.last = old == (unsigned)G - 1;
         }

@@ -5,7 +5,10 @@
 // mask:build_tree_kernel_efficient; 邻接表:retrieve_* 三兄弟) and
 // "把投机采样讲透:以 SGLang 中的 EAGLE-2 为例" (4.3 tree mask, positions).
 //
-// One 256-thread workgroup per request.  Selection needs no sort: a
+// One 1024-thread workgroup per request.  Every input of the request
+// (scores, tokens, parent list, bonus token, sequence length) is read into
+// LDS in one round of loads at the start, so the rest of the kernel waits
+// on memory once.  Selection needs no sort: a
 // candidate is kept iff fewer than n-1 candidates beat it under
 // (score desc, flat index asc), and its node index is one plus the number of
 // kept candidates with a smaller flat index (a block prefix count), which is
@@ -40,10 +43,14 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     int32_t *__restrict__ r_index, int32_t *__restrict__ r_next, int32_t *__restrict__ r_sib,
     int32_t *__restrict__ selected, int32_t *__restrict__ status) {
     __shared__ __attribute__((aligned(16))) uint64_t s_key[kMaxCand];
+    __shared__ int32_t s_tok[kMaxCand];        // candidate tokens
+    __shared__ int32_t s_plist[kMaxCand];      // parent list (npar <= ncand entries)
     __shared__ int16_t s_node[kMaxCand];       // flat index -> node (0 = not kept)
     __shared__ int32_t s_flat[kMaxNodes];      // node -> flat index
     __shared__ int32_t s_parent[kMaxNodes];
+    __shared__ uint64_t s_kids[kMaxNodes];     // children of each node as a bit set
     __shared__ int32_t s_wave_cnt[kThreads / SPEC_WAVE];
+    __shared__ int32_t s_bonus, s_len;
 
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
@@ -52,7 +59,16 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     const int keep = n - 1;
     const float *sc = scores + (size_t)r * ncand;
 
-    for (int f = tid; f < ncand; f += kThreads) s_key[f] = order_key(sc[f], f);
+    for (int f = tid; f < ncand; f += kThreads) {
+        s_key[f] = order_key(sc[f], f);
+        s_tok[f] = tokens[(size_t)r * ncand + f];
+    }
+    if (parents != nullptr)
+        for (int i = tid; i < npar; i += kThreads) s_plist[i] = parents[(size_t)r * npar + i];
+    if (tid == 0) {
+        s_bonus = bonus[r];
+        s_len = seq_lens[r];
+    }
     if (tid < kMaxNodes) s_flat[tid] = 0;
     __syncthreads();
 
@@ -66,13 +82,24 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
         bool kept = false;
         if (f < ncand && keep > 0) {
             const uint64_t mine = s_key[f];
-            int beats = 0;
-            for (int g = 0; g < ncand2; g += 2) {
-                const uint4 w = *reinterpret_cast<const uint4 *>(&s_key[g]);
-                const uint64_t k0 = ((uint64_t)w.y << 32) | w.x;
-                const uint64_t k1 = ((uint64_t)w.w << 32) | w.z;
-                beats += (k0 > mine) + (k1 > mine);
+            // four independent counts, so several LDS reads are in flight
+            int b0 = 0, b1 = 0, b2 = 0, b3 = 0;
+            int g = 0;
+            for (; g + 8 <= ncand2; g += 8) {
+                const uint4 w0 = *reinterpret_cast<const uint4 *>(&s_key[g]);
+                const uint4 w1 = *reinterpret_cast<const uint4 *>(&s_key[g + 2]);
+                const uint4 w2 = *reinterpret_cast<const uint4 *>(&s_key[g + 4]);
+                const uint4 w3 = *reinterpret_cast<const uint4 *>(&s_key[g + 6]);
+                b0 += (((uint64_t)w0.y << 32 | w0.x) > mine) + (((uint64_t)w0.w << 32 | w0.z) > mine);
+                b1 += (((uint64_t)w1.y << 32 | w1.x) > mine) + (((uint64_t)w1.w << 32 | w1.z) > mine);
+                b2 += (((uint64_t)w2.y << 32 | w2.x) > mine) + (((uint64_t)w2.w << 32 | w2.z) > mine);
+                b3 += (((uint64_t)w3.y << 32 | w3.x) > mine) + (((uint64_t)w3.w << 32 | w3.z) > mine);
             }
+            for (; g < ncand2; g += 2) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(&s_key[g]);
+                b0 += (((uint64_t)w.y << 32 | w.x) > mine) + (((uint64_t)w.w << 32 | w.z) > mine);
+            }
+            int beats = b0 + b1 + b2 + b3;
             if (ncand2 != ncand) beats += s_key[ncand - 1] > mine;
             kept = beats < keep;
         }
@@ -108,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
         if (f < topk) {
             par = 0;
         } else {
-            const int g = parents[(size_t)r * npar + f / topk];
+            const int g = s_plist[f / topk];
             if (g < 0 || g >= ncand) {
                 err |= SPEC_ST_RANGE;
                 par = 0;
@@ -127,8 +154,18 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     __syncthreads();
     if (wave != 0) return;
 
+    // children of every node as a bit set (lane j gets the set of node j):
+    // first child = lowest set bit, next sibling = lowest bit of the
+    // parent's set above k
+    uint64_t kids = 0;
+    for (int j = 0; j < n; ++j) {
+        const uint64_t m = __ballot(k >= 1 && k < n && par == j);
+        if (k == j) kids = m;
+    }
+    if (k < n) s_kids[k] = kids;
+    // only wave 0 is left, and one wave's LDS accesses complete in order
+    __builtin_amdgcn_wave_barrier();
     if (k < n) {
-        // depth and ancestor-or-self bits by walking up the parent chain
         uint64_t bits = 1ull << k;
         int depth = 0;
         int j = k;
@@ -137,17 +174,15 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
             bits |= 1ull << j;
             ++depth;
         }
-        // first child: smallest c with parent c == k; next sibling: smallest
-        // c > k sharing k's parent
-        int first = -1, sib = -1;
-        for (int c = n - 1; c >= 1; --c) {
-            const int pc = s_parent[c];
-            if (pc == k) first = c;
-            if (k >= 1 && c > k && pc == par) sib = c;
+        const int first = kids ? __builtin_ctzll(kids) : -1;
+        int sib = -1;
+        if (k >= 1) {
+            const uint64_t later = s_kids[par] & ~((2ull << k) - 1ull);   // siblings above k
+            sib = later ? __builtin_ctzll(later) : -1;
         }
         const size_t row = (size_t)r * n + k;
-        draft_tokens[row] = (k == 0) ? bonus[r] : tokens[(size_t)r * ncand + s_flat[k]];
-        positions[row] = seq_lens[r] + depth;
+        draft_tokens[row] = (k == 0) ? s_bonus : s_tok[s_flat[k]];
+        positions[row] = s_len + depth;
         r_index[row] = static_cast<int32_t>(row);
         r_next[row] = first;
         r_sib[row] = sib;

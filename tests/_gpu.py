@@ -90,10 +90,13 @@ def verify_attention(w, mask_words, layer=0, sm_scale=0.0):
     return o.reshape(b * n, cfg.num_q_heads, cfg.head_dim), int(host(st)[0])
 
 
-def accept_greedy(w, tl, tree):
+def accept_greedy(w, tl, tree, workspace=None):
     cfg = w.cfg
     b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
-    ws = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8, device=DEV)
+    ws = workspace
+    if ws is None:
+        ws = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
+                         device=DEV)
     predict, ai, al, tp, st = i32(b * n), i32(b * s1), i32(b), i32(b * n), status()
     predict.fill_(-7)
     ai.fill_(-7)

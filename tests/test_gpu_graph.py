@@ -71,7 +71,7 @@ def test_graph_replay_matches_eager(name, cfg):
     ws_a = torch.empty(max(1, S.spec_verify_attention_workspace_size(
         b, n, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, maxlen, code)),
         dtype=torch.uint8, device="cuda")
-    ws_g = torch.empty(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
+    ws_g = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
                        device="cuda")
     ws_s = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
                        device="cuda")

@@ -130,3 +130,24 @@ def test_sample_workspace_reused():
         _check(w, t, tl, dl, g, f"seed {seed}")
         # the call leaves the workspace as it found it: zero
         assert int(torch.count_nonzero(ws)) == 0
+
+
+def test_greedy_workspace_reused():
+    """Three greedy accepts in a row on one workspace, each bit-exact against
+    the oracle (partials of one call must not leak into the next)."""
+    cfg = W.shrink(W.CONFIGS[5], batch=3, hist=H8, vocab=30000)
+    b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
+    ws = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
+                     device="cuda")
+    for seed in (41, 42, 43):
+        say(f"[greedy reuse] seed {seed}")
+        w, t, tl, dl = _setup(cfg, seed)
+        o = oracle.accept_greedy(tl, t["draft_tokens"], t["retrieve_index"],
+                                 t["retrieve_next_token"], t["retrieve_next_sibling"], b, n, s1,
+                                 cfg.dtype)
+        g = G.accept_greedy(w, tl, _tree(t), workspace=ws)
+        assert g["status"] == 0
+        np.testing.assert_array_equal(g["target_predict"], o["target_predict"])
+        np.testing.assert_array_equal(g["predict"], o["predict"])
+        np.testing.assert_array_equal(g["accept_index"], o["accept_index"])
+        np.testing.assert_array_equal(g["accept_length"], o["accept_length"])
