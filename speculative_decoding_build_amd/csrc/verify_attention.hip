@@ -39,8 +39,11 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTileKeys = 64;
-constexpr int kTargetGroups = 1024;     // workgroups a launch aims for
+constexpr int kTargetGroups = 512;      // workgroups a launch aims for (one co-resident round)
 constexpr int kMinTiles = 4;            // 64-key tiles per split at least
+constexpr int kPreTiles = 4;            // tiles whose page entries the prologue fetches
+constexpr int kMaxTreeNodes = 64;
+constexpr int kSmallGrid = 512;         // fewer 8-wave workgroups than this: use 4-wave ones
 
 struct AttnParams {
     int batch, n, hq, hkv, group, rows;   // rows = n * group
@@ -161,16 +164,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
 
     const Work wk = decode_work(P, blockIdx.x, xcd_remap != 0);
     const int b = wk.b, kvh = wk.kvh, split = wk.split, rg = wk.rg;
+    const int kb = split * P.split_len;
+    // Loads that do not depend on the sequence length go out with it: the
+    // page-table entries of the split's first kPreTiles tiles and the
+    // request's tree slots.
+    int pre_page = -1, pre_tree = -1;
+    if (tid < kPreTiles * kTileKeys) {
+        const int p = kb + tid;
+        if (P.page_table != nullptr && p < P.max_pages * P.page_size)
+            pre_page = P.page_table[(int64_t)b * P.max_pages + p / P.page_size];
+    }
+    if (tid < P.n) pre_tree = P.out_cache_loc[(int64_t)b * P.n + tid];
     const int L = P.seq_lens[b];
     int err = 0;
     if (L < 0 || L > P.max_seq_len) {
         if (tid == 0 && split == 0 && rg == 0) spec::raise_status(P.status, SPEC_ST_RANGE);
         return;
     }
-    const int kb = split * P.split_len;
     const int ke = min(L + P.n, kb + P.split_len);
     if (kb >= ke) return;
     const int ntiles = (ke - kb + kTileKeys - 1) / kTileKeys;
+    __shared__ int32_t s_pre[kPreTiles * kTileKeys];
+    __shared__ int32_t s_tree[kMaxTreeNodes];
+    if (tid < kPreTiles * kTileKeys) s_pre[tid] = pre_page;
+    if (tid < P.n) s_tree[tid] = pre_tree;
 
     // ---- query fragments (B operand of S^T = K Q^T) -----------------------
     const int rho = rg * P.rows_per_group + wave * 32 + col;
@@ -201,9 +218,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
     const __bf16 *vpool = static_cast<const __bf16 *>(P.v_pool);
 
     // slot of key position p of this request, -1 past the split or invalid
+    // (the first kPreTiles tiles' page entries and the tree slots come from
+    // LDS)
     auto lookup = [&](int p) -> int64_t {
         if (p >= ke) return -1;
-        return key_slot(P, b, L, p, err);
+        int64_t slot;
+        if (p < L) {
+            const int rel = p - kb;
+            const int page = rel < kPreTiles * kTileKeys
+                                 ? s_pre[rel]
+                                 : P.page_table[(int64_t)b * P.max_pages + p / P.page_size];
+            slot = page < 0 ? -1 : (int64_t)page * P.page_size + p % P.page_size;
+        } else {
+            slot = s_tree[p - L];
+        }
+        if (slot < 0 || slot >= P.num_slots) {
+            err |= SPEC_ST_RANGE;
+            return -1;
+        }
+        return slot;
     };
 
     // ---- register staging: two tiles in flight, in two statically named sets
@@ -274,6 +307,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
 
     // ---- prologue: tiles 0 and 1 loading, tile 0 in LDS, slots of tiles 2
     // and 3 in the slot stages, tile 2 loading --------------------------------
+    __syncthreads();                       // s_pre, s_tree
     if (tid < kTileKeys) {
         s_slot[0][tid] = lookup(kb + tid);
         s_slot[1][tid] = lookup(kb + kTileKeys + tid);
@@ -573,7 +607,16 @@ Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
     Plan pl{};
     const int rows = n * (hq / hkv);
     if (dtype == SPEC_BF16) {
+        // 8-wave workgroups (one row group of up to 256 rows) unless that
+        // leaves the device short of workgroups; then 4-wave ones, whose row
+        // groups read the same K/V (from L2) in parallel
         pl.nw = rows <= 128 ? 4 : 8;
+        if (pl.nw == 8) {
+            const int tiles8 = (max_seq_len + n + kTileKeys - 1) / kTileKeys;
+            const int groups8 = batch * hkv * ((rows + 255) / 256) *
+                                std::max(1, std::min(tiles8 / kMinTiles, kMaxSplits));
+            if (groups8 < kSmallGrid) pl.nw = 4;
+        }
         pl.rows_per_group = pl.nw * 32;
     } else {
         pl.nw = 4;

@@ -224,6 +224,38 @@ def full(cid, attention):
     return _full[key]
 
 
+# Split-KV plans whose last key split holds 1, 2, 3 or 4 tiles, or ends in a
+# part tile, or whose splits are 4 tiles long: every output vector against
+# the oracle.
+SPLIT_CASES = {
+    "L4160_last1": W.shrink(W.CONFIGS[2], hist=("fixed", 4160), vocab=1000),
+    "L4224_last2": W.shrink(W.CONFIGS[2], hist=("fixed", 4224), vocab=1000),
+    "L4288_last3": W.shrink(W.CONFIGS[2], hist=("fixed", 4288), vocab=1000),
+    "L4100_part": W.shrink(W.CONFIGS[2], hist=("fixed", 4100), vocab=1000),
+    "L4032_4tile": W.shrink(W.CONFIGS[2], hist=("fixed", 4032), vocab=1000),
+    "L2048": W.shrink(W.CONFIGS[2], hist=("fixed", 2048), vocab=1000),
+    "b4_Lu": W.shrink(W.CONFIGS[3], batch=4, hist=("uniform", 1000, 3000), vocab=1000),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_verify_attention_split_remainders(name):
+    cfg = SPLIT_CASES[name]
+    w = W.make_workload(cfg, 17)
+    t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                          cfg.num_steps, cfg.num_draft_tokens)
+    say(f"[attention splits] {name} b={cfg.batch} L={w.seq_lens.tolist()}")
+    words = oracle.pack_mask(t["mask"], oracle.MASK_QLEN_BITS)
+    got, st = G.verify_attention(w, words)
+    assert st == 0
+    ref = oracle.verify_attention(w.q, w.k_pool[0], w.v_pool[0], w.page_table, w.seq_lens,
+                                  w.out_cache_loc, t["mask"], cfg.num_q_heads, cfg.num_kv_heads,
+                                  cfg.page_size, cfg.dtype)
+    err = _attn_err(got, ref.reshape(got.shape))
+    say(f"    max rel err {err:.3e} over all {got.shape[0] * got.shape[1]} vectors")
+    assert err <= ATTN_TOL[cfg.dtype]
+
+
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
 def test_full_tree_and_accept(cid):
     w, t = full(cid, False)
