@@ -48,6 +48,7 @@ constexpr int kCoopGridTarget = 512;           // workgroups of a cooperative wa
 constexpr int kMaxGroups = 64;                 // slices per request (one wave gathers them)
 constexpr int kCacheEntries = 16;              // row entries a walk thread keeps in registers
 constexpr int kWords = 3;                      // exchange words per workgroup per exchange
+constexpr int kSlotWords = 8;                  // one 64-byte slot per workgroup and exchange
 
 // Exchange slot encoding: a slot holds bits(v) ^ kFlip, 0 meaning "not yet
 // written" (a zero-filled workspace is empty).  kFlip is a signalling-NaN
@@ -238,7 +239,7 @@ struct WalkArgs {
     int G;              // workgroups per request (1: one workgroup, no exchange)
     int64_t slice;      // vocabulary entries per workgroup, a multiple of 8 * threads
     int E;              // exchanges a request may make
-    uint64_t *xch;      // [batch][E][G][kWords] exchange slots (G > 1)
+    uint64_t *xch;      // [batch][E][G][kSlotWords] exchange slots (G > 1)
     unsigned *done;     // [batch] workgroups finished (G > 1)
 };
 
@@ -259,27 +260,47 @@ struct WalkShared {
     int err, owner, draw, last;
 };
 
-// Poll one exchange word until it is written (bounded); false on timeout.
-__device__ __forceinline__ bool read_word(uint64_t *slot, uint64_t &bits) {
-    unsigned spins = 0;
-    uint64_t w;
-    while ((w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
-        if (++spins > kSpinLimit) {
-            bits = 0;
-            return false;
+template <int W>
+__device__ __forceinline__ void load_words(const uint64_t *slot, uint64_t (&w)[W]) {
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+        w[i] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll the W words of one exchange slot until all are written (bounded);
+// false on timeout.  The words are read together; one read is in flight at
+// a time (more polls in flight only add traffic to the lines every
+// workgroup is polling, and arrive later).
+template <int W>
+__device__ __forceinline__ bool read_slot(const uint64_t *slot, uint64_t (&bits)[W]) {
+    for (unsigned spins = 0; spins < kSpinLimit; ++spins) {
+        uint64_t w[W];
+        load_words<W>(slot, w);
+        bool all = true;
+#pragma unroll
+        for (int i = 0; i < W; ++i) all = all && w[i] != 0;
+        if (all) {
+#pragma unroll
+            for (int i = 0; i < W; ++i) bits[i] = w[i] ^ kFlip;
+            return true;
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    bits = w ^ kFlip;
-    return true;
+#pragma unroll
+    for (int i = 0; i < W; ++i) bits[i] = 0;
+    return false;
 }
 
 __device__ __forceinline__ void write_word(uint64_t *slot, uint64_t bits) {
     __hip_atomic_store(slot, encode_bits(bits), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int DT, int NT, bool COOP>
+// CACHE: the segments fit in registers (COOP only).  Each launch runs one of
+// the two segment paths, so each kernel holds only that one's code (the
+// instruction cache is smaller than both together).
+template <int DT, int NT, bool COOP, bool CACHE>
 __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
+    static_assert(COOP || !CACHE, "the one-workgroup walk does not cache");
     static_assert(NT % 64 == 0, "whole waves");
     __shared__ WalkShared<NT> S;
     const int G = COOP ? A.G : 1;
@@ -305,7 +326,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
 
     // The current row's segment in registers when it fits: raw logits on
     // arrival, their exponentials once the row statistics are known.
-    const bool use_cache = COOP && seg <= kCacheEntries;   // the solo walk's segments are longer
+    constexpr bool use_cache = CACHE;   // the host picks CACHE iff seg <= kCacheEntries
     float ct[kCacheEntries], cd[kCacheEntries];
     int cached_row = -1;               // local row whose raw logits ct / cd hold
     auto load_cache = [&](int lrow) {
@@ -350,7 +371,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
         S.unif[tid] = A.uniforms[base + tid];
     }
     if (tid == 0) S.err = 0;
-    if (use_cache) load_cache(0);
+    if constexpr (use_cache) load_cache(0);
     __syncthreads();
     if (tid < n) {
         if (S.row[tid] < 0) atomicOr(&S.err, SPEC_ST_RANGE);
@@ -370,7 +391,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     int e = 0;                         // exchanges used so far
     bool alive = true;
     auto slot = [&](int ex, int wg) -> uint64_t * {
-        return A.xch + (((int64_t)req * A.E + ex) * G + wg) * kWords;
+        return A.xch + (((int64_t)req * A.E + ex) * G + wg) * kSlotWords;
     };
     // row statistics from every workgroup's slice statistics
     auto exchange_stats = [&](float mt, double st, float md, double sd) -> RowDist {
@@ -389,17 +410,14 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                     float jmt = -INFINITY, jmd = -INFINITY;
                     double jst = 0.0, jsd = 0.0;
                     if (tid < G) {
-                        uint64_t w0 = 0, w1 = 0, w2 = 0;
-                        const bool ok = read_word(slot(e, tid) + 0, w0) &&
-                                        read_word(slot(e, tid) + 1, w1) &&
-                                        read_word(slot(e, tid) + 2, w2);
-                        if (!ok) {
+                        uint64_t w[kWords];
+                        if (!read_slot<kWords>(slot(e, tid), w)) {
                             atomicOr(&S.err, SPEC_ST_SYNC);
                         } else {
-                            jmt = __uint_as_float((uint32_t)w0);
-                            jmd = __uint_as_float((uint32_t)(w0 >> 32));
-                            jst = __builtin_bit_cast(double, w1);
-                            jsd = __builtin_bit_cast(double, w2);
+                            jmt = __uint_as_float((uint32_t)w[0]);
+                            jmd = __uint_as_float((uint32_t)(w[0] >> 32));
+                            jst = __builtin_bit_cast(double, w[1]);
+                            jsd = __builtin_bit_cast(double, w[2]);
                         }
                     }
                     mt = wave_max(jmt);
@@ -440,9 +458,9 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
         if (tid == 0) write_word(slot(e, g), __builtin_bit_cast(uint64_t, slice_sum));
         if (tid < 64) {
             sj = 0.0;
-            uint64_t w = 0;
+            uint64_t w[1];
             if (tid < G) {
-                if (read_word(slot(e, tid), w)) sj = __builtin_bit_cast(double, w);
+                if (read_slot<1>(slot(e, tid), w)) sj = __builtin_bit_cast(double, w[0]);
                 else atomicOr(&S.err, SPEC_ST_SYNC);
             }
             const double tot = wave_sum_d(sj);
@@ -467,7 +485,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     // sum of my segment's residual weights with multiplier cc
     auto segment_sum = [&](double cc) -> double {
         double m = 0.0;
-        if (use_cache) {
+        if constexpr (use_cache) {
 #pragma unroll
             for (int i = 0; i < kCacheEntries; ++i) m += resid_from_exp(ct[i], cd[i], rd, cc);
         } else {
@@ -503,7 +521,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
         }
         float mt = -INFINITY, md = -INFINITY;
         double st = 0.0, sd = 0.0;
-        if (use_cache) {
+        if constexpr (use_cache) {
             if (cached_row != lr) load_cache(lr);
 #pragma unroll
             for (int i = 0; i < kCacheEntries; ++i) {
@@ -557,7 +575,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
         }
         __syncthreads();
         if (!alive) break;
-        if (use_cache) {
+        if constexpr (use_cache) {
             const float ft = thr_mt == -INFINITY ? 0.f : exp_scaled(thr_mt, rd.t);
             const float fd = thr_md == -INFINITY ? 0.f : exp_scaled(thr_md, rd.d);
 #pragma unroll
@@ -663,7 +681,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                     // first entry of my segment where the running sum crosses tgt
                     double run = before;
                     int64_t x = -1;
-                    if (use_cache) {
+                    if constexpr (use_cache) {
 #pragma unroll
                         for (int i = 0; i < kCacheEntries; ++i) {
                             run += resid_from_exp(ct[i], cd[i], rd, c);
@@ -720,9 +738,10 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
         __syncthreads();
         if (S.last) {
             const int used = (S.err & SPEC_ST_SYNC) ? A.E : e;
-            uint64_t *x = A.xch + (int64_t)req * A.E * G * kWords;
+            uint64_t *x = A.xch + (int64_t)req * A.E * G * kSlotWords;
             for (int i = tid; i < used * G * kWords; i += NT)
-                __hip_atomic_store(x + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(x + (i / kWords) * kSlotWords + i % kWords, (uint64_t)0,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (tid == 0)
                 __hip_atomic_store(A.done + req, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -747,38 +766,47 @@ int exchanges_per_request(int n) { return 2 * n + 2; }
 struct CoopPlan {
     int G;
     int64_t slice;
+    bool cache;         // segments of at most kCacheEntries entries
 };
 
-// Workgroups per request for the cooperative walk, or G = 0 when the grid
-// cannot be co-resident (or cooperative launch is unavailable).
-template <int DT>
-CoopPlan coop_plan(int batch, int64_t vocab) {
+// Workgroups of one cooperative-walk kernel that fit on the device at once
+// (0 if cooperative launch is unavailable).
+template <int DT, bool CACHE>
+int coop_capacity(int dev) {
     static int cached_device = -1, cap = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return CoopPlan{0, 0};
     if (dev != cached_device) {
         int coop = 0, cus = 0, per = 0;
         bool ok = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess;
         ok = ok && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
         ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                       &per, reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true>),
+                       &per, reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true, CACHE>),
                        kCoopThreads, 0) == hipSuccess;
         cap = (ok && coop) ? cus * per : 0;
         cached_device = dev;
     }
+    return cap;
+}
+
+// Workgroups per request for the cooperative walk, or G = 0 when the grid
+// cannot be co-resident (or cooperative launch is unavailable).
+template <int DT>
+CoopPlan coop_plan(int batch, int64_t vocab) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CoopPlan{0, 0, false};
+    const int cap = std::min(coop_capacity<DT, true>(dev), coop_capacity<DT, false>(dev));
     int64_t G = group_cap(batch, vocab);
     G = std::min<int64_t>(G, cap / std::max(batch, 1));
-    if (G < 2) return CoopPlan{0, 0};
+    if (G < 2) return CoopPlan{0, 0, false};
     int64_t slice = (vocab + G - 1) / G;
     slice = (slice + kMinSlice - 1) / kMinSlice * kMinSlice;
     G = (vocab + slice - 1) / slice;
-    if (G < 2) return CoopPlan{0, 0};
-    return CoopPlan{(int)G, slice};
+    if (G < 2) return CoopPlan{0, 0, false};
+    return CoopPlan{(int)G, slice, slice / kCoopThreads <= kCacheEntries};
 }
 
 size_t sample_workspace_layout(int batch, int n, int64_t vocab, size_t *off_done) {
     const size_t xch = spec::align_up((size_t)batch * exchanges_per_request(n) *
-                                          group_cap(batch, vocab) * kWords * sizeof(uint64_t),
+                                          group_cap(batch, vocab) * kSlotWords * sizeof(uint64_t),
                                       256);
     if (off_done) *off_done = xch;
     return xch + spec::align_up((size_t)batch * sizeof(unsigned), 256);
@@ -820,21 +848,28 @@ int launch_sample(int batch, int n, int s1, int64_t vocab, const void *tl, const
         A.G = pl.G;
         A.slice = pl.slice;
         const dim3 grid((unsigned)(batch * pl.G)), block(kCoopThreads);
+        const void *fn = pl.cache
+            ? reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true, true>)
+            : reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true, false>);
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive) {
             // recorded into a graph: an ordinary launch of a grid sized to
             // what the device holds at once
-            hipLaunchKernelGGL((sample_walk_kernel<DT, kCoopThreads, true>), grid, block, 0, st, A);
+            if (pl.cache)
+                hipLaunchKernelGGL((sample_walk_kernel<DT, kCoopThreads, true, true>), grid, block,
+                                   0, st, A);
+            else
+                hipLaunchKernelGGL((sample_walk_kernel<DT, kCoopThreads, true, false>), grid, block,
+                                   0, st, A);
             return launch_status();
         }
         void *args[] = {&A};
-        const void *fn = reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true>);
         if (hipLaunchCooperativeKernel(fn, grid, block, args, 0, st) == hipSuccess) return SPEC_OK;
         (void)hipGetLastError();   // fall back below
     }
     A.G = 1;
     A.slice = ((vocab + kSoloThreads - 1) / kSoloThreads + 7) / 8 * 8 * kSoloThreads;
-    hipLaunchKernelGGL((sample_walk_kernel<DT, kSoloThreads, false>), dim3(batch),
+    hipLaunchKernelGGL((sample_walk_kernel<DT, kSoloThreads, false, false>), dim3(batch),
                        dim3(kSoloThreads), 0, st, A);
     return launch_status();
 }
