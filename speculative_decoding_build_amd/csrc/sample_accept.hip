@@ -145,7 +145,63 @@ __device__ __forceinline__ void for_each8(const void *trow, const void *drow, in
     }
 }
 
-// ---- block reductions -----------------------------------------------------------
+// ---- wave and block reductions ---------------------------------------------------
+//
+// Full-wave reductions (every lane active at the call) kept in registers:
+// DPP moves combine lanes inside each 16-lane row (quad xor 1, quad xor 2,
+// half-row mirror, row mirror: after each step all lanes of a group hold the
+// same value, addition and max being commutative), then the four row results
+// are read out as scalars.  Every lane returns the same value, and equal
+// inputs give equal results in every workgroup.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v, float old) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,
+                                                      0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v, double old) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v), o = __builtin_bit_cast(uint64_t, old);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)o, (int)(uint32_t)b, CTRL,
+                                                             0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(o >> 32),
+                                                             (int)(uint32_t)(b >> 32), CTRL, 0xF,
+                                                             0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double full_wave_sum_d(double v) {
+    v += dpp_f64<kDppQuadXor1>(v, 0.0);
+    v += dpp_f64<kDppQuadXor2>(v, 0.0);
+    v += dpp_f64<kDppRowHalfMirror>(v, 0.0);
+    v += dpp_f64<kDppRowMirror>(v, 0.0);
+    return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+
+__device__ __forceinline__ float full_wave_max(float v) {
+    v = fmaxf(v, dpp_f32<kDppQuadXor1>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppQuadXor2>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppRowMirror>(v, -INFINITY));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
 
 // s * exp((m - M) / T): a partial sum taken at max m, rescaled to max M
 // (float exponential of the exactly formed argument; 0 for an empty part)
@@ -159,9 +215,9 @@ template <int NT>
 __device__ void block_stats(float &mt, double &st, float &md, double &sd, float ithi, float itlo,
                             float *sm, double *ss) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const float wt = wave_max(mt), wd = wave_max(md);
-    const double rt = wave_sum_d(rescale(mt, st, wt, ithi, itlo));
-    const double rd = wave_sum_d(rescale(md, sd, wd, ithi, itlo));
+    const float wt = full_wave_max(mt), wd = full_wave_max(md);
+    const double rt = full_wave_sum_d(rescale(mt, st, wt, ithi, itlo));
+    const double rd = full_wave_sum_d(rescale(md, sd, wd, ithi, itlo));
     if (lane == 0) {
         sm[2 * wave] = wt;
         sm[2 * wave + 1] = wd;
@@ -214,7 +270,7 @@ __device__ double block_exclusive_scan(double v, double *scratch, double &total)
 
 template <int NT>
 __device__ double block_sum(double v, double *scratch) {
-    v = wave_sum_d(v);
+    v = full_wave_sum_d(v);
     if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
     __syncthreads();
     double s = 0.0;
@@ -245,8 +301,8 @@ struct WalkArgs {
 
 template <int NT>
 struct WalkShared {
-    float cxt[kMaxNodes];      // node k's token: target / draft logit in its parent's row
-    float cxd[kMaxNodes];
+    double cp[kMaxNodes];      // node k's token: target / draft probability in its parent's row
+    double cq[kMaxNodes];
     int cand[kMaxNodes], next[kMaxNodes], sib[kMaxNodes], par[kMaxNodes];
     int row[kMaxNodes];        // local verify row of node k, -1 if invalid
     int pred[kMaxNodes];
@@ -255,8 +311,9 @@ struct WalkShared {
     float sm[2 * NT / 64];
     double ss[2 * NT / 64];
     double scratch[NT / 64];
-    double bcast;
-    RowDist dist;
+    double bcast[2];           // exchange results, alternating buffers (one barrier each)
+    RowDist dist[2];
+    double tgt;
     int err, owner, draw, last;
 };
 
@@ -327,13 +384,18 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     // The current row's segment in registers when it fits: raw logits on
     // arrival, their exponentials once the row statistics are known.
     constexpr bool use_cache = CACHE;   // the host picks CACHE iff seg <= kCacheEntries
+    static_assert(kCacheEntries == 16, "two groups of 8 cached entries");
     float ct[kCacheEntries], cd[kCacheEntries];
+    // seg is a multiple of 8: the second group of 8 registers is used only
+    // when seg is 16 (a uniform branch around the work on it otherwise)
+    const bool wide = seg > 8;
     int cached_row = -1;               // local row whose raw logits ct / cd hold
     auto load_cache = [&](int lrow) {
         const void *trow = row_ptr(A.tlogits, lrow);
         const void *drow = row_ptr(A.dlogits, lrow);
 #pragma unroll
         for (int i0 = 0; i0 < kCacheEntries; i0 += 8) {
+            if (i0 == 8 && !wide) break;
             float xt[8], xd[8];
             const int64_t v = sa + i0;
             if (A.vec_ok && v + 8 <= sb) {
@@ -389,6 +451,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
 
     // ---- exchanges (uniform across the request's workgroups) -----------------
     int e = 0;                         // exchanges used so far
+    int xb = 0;                        // exchange calls so far (result buffer parity)
     bool alive = true;
     auto slot = [&](int ex, int wg) -> uint64_t * {
         return A.xch + (((int64_t)req * A.E + ex) * G + wg) * kSlotWords;
@@ -420,10 +483,10 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                             jsd = __builtin_bit_cast(double, w[2]);
                         }
                     }
-                    mt = wave_max(jmt);
-                    md = wave_max(jmd);
-                    st = wave_sum_d(rescale(jmt, jst, mt, ithi, itlo));
-                    sd = wave_sum_d(rescale(jmd, jsd, md, ithi, itlo));
+                    mt = full_wave_max(jmt);
+                    md = full_wave_max(jmd);
+                    st = full_wave_sum_d(rescale(jmt, jst, mt, ithi, itlo));
+                    sd = full_wave_sum_d(rescale(jmd, jsd, md, ithi, itlo));
                 }
                 ++e;
             }
@@ -434,12 +497,14 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             r.d = Scale{md, ithi, itlo};
             r.inv_st = st > 0.0 ? 1.0 / st : 0.0;
             r.inv_sd = sd > 0.0 ? 1.0 / sd : 0.0;
-            S.dist = r;
+            S.dist[xb & 1] = r;
         }
         __syncthreads();
         if (S.err & SPEC_ST_SYNC) alive = false;
-        const RowDist r = S.dist;
-        __syncthreads();
+        // the other buffer is written next; this one not before every thread
+        // has passed the next exchange's barrier
+        const RowDist r = S.dist[xb & 1];
+        ++xb;
         return r;
     };
     double sj = 0.0;                   // wave 0, lane j < G: slice j's sum in the last sweep
@@ -463,14 +528,14 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                 if (read_slot<1>(slot(e, tid), w)) sj = __builtin_bit_cast(double, w[0]);
                 else atomicOr(&S.err, SPEC_ST_SYNC);
             }
-            const double tot = wave_sum_d(sj);
-            if (tid == 0) S.bcast = tot;
+            const double tot = full_wave_sum_d(sj);
+            if (tid == 0) S.bcast[xb & 1] = tot;
         }
         ++e;
         __syncthreads();
         if (S.err & SPEC_ST_SYNC) alive = false;
-        const double tot = S.bcast;
-        __syncthreads();
+        const double tot = S.bcast[xb & 1];
+        ++xb;
         return tot;
     };
 
@@ -487,7 +552,10 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
         double m = 0.0;
         if constexpr (use_cache) {
 #pragma unroll
-            for (int i = 0; i < kCacheEntries; ++i) m += resid_from_exp(ct[i], cd[i], rd, cc);
+            for (int i = 0; i < kCacheEntries; ++i) {
+                if (i == 8 && !wide) break;
+                m += resid_from_exp(ct[i], cd[i], rd, cc);
+            }
         } else {
             for_each8<DT>(row_ptr(A.tlogits, lr), row_ptr(A.dlogits, lr), sa, sb, A.vec_ok,
                           [&](int64_t, const float (&xt)[8], const float (&xd)[8], int) {
@@ -525,6 +593,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             if (cached_row != lr) load_cache(lr);
 #pragma unroll
             for (int i = 0; i < kCacheEntries; ++i) {
+                if (i == 8 && !wide) break;
                 mt = fmaxf(mt, ct[i]);
                 md = fmaxf(md, cd[i]);
             }
@@ -534,6 +603,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             float ft = 0.f, fd = 0.f;
 #pragma unroll
             for (int i = 0; i < kCacheEntries; ++i) {
+                if (i == 8 && !wide) break;
                 ct[i] = exp_scaled(ct[i], sct);
                 cd[i] = exp_scaled(cd[i], scd);
                 ft += ct[i];
@@ -570,8 +640,8 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
         block_stats<NT>(mt, st, md, sd, ithi, itlo, S.sm, S.ss);
         rd = exchange_stats(mt, st, md, sd);
         if (is_child) {
-            S.cxt[tid] = kid_t;
-            S.cxd[tid] = kid_d;
+            S.cp[tid] = (double)exp_scaled(kid_t, rd.t) * rd.inv_st;
+            S.cq[tid] = (double)exp_scaled(kid_d, rd.d) * rd.inv_sd;
         }
         __syncthreads();
         if (!alive) break;
@@ -580,6 +650,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             const float fd = thr_md == -INFINITY ? 0.f : exp_scaled(thr_md, rd.d);
 #pragma unroll
             for (int i = 0; i < kCacheEntries; ++i) {
+                if (i == 8 && !wide) break;
                 ct[i] *= ft;
                 cd[i] *= fd;
             }
@@ -596,8 +667,8 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             bool dec = false;
             if (t >= 0 && t < A.vocab) {
                 // u < min(1, (max(0, p - c q) / F) / q), without the divisions
-                const double p = (double)exp_scaled(S.cxt[k], rd.t) * rd.inv_st;
-                const double q = (double)exp_scaled(S.cxd[k], rd.d) * rd.inv_sd;
+                const double p = S.cp[k];
+                const double q = S.cq[k];
                 const double r = fmax(fma(-c, q, p), 0.0);
                 const double u = (double)S.unif[k];
                 dec = q > 0.0 ? (u < 1.0 && u * q * F < r) : (r > 0.0 ? u < 1.0 : u < 0.0);
@@ -661,16 +732,16 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                     const uint64_t bal = __ballot(here);
                     if (bal != 0 && tid == __builtin_ctzll(bal)) {
                         S.owner = tid;
-                        S.bcast = target - pre;
+                        S.tgt = target - pre;
                     }
                 }
             } else if (tid == 0 && target < tot) {
                 S.owner = 0;
-                S.bcast = target;
+                S.tgt = target;
             }
             __syncthreads();
             const int owner = S.owner;
-            const double tgt = S.bcast;
+            const double tgt = S.tgt;
             if (owner == INT_MAX) {
                 // no crossing: the target sits at the very end of the mass
                 if (g == 0 && tid == 0) A.predict[base + lr] = (int)(A.vocab - 1);
@@ -684,6 +755,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                     if constexpr (use_cache) {
 #pragma unroll
                         for (int i = 0; i < kCacheEntries; ++i) {
+                            if (i == 8 && !wide) break;
                             run += resid_from_exp(ct[i], cd[i], rd, c);
                             if (x < 0 && run > tgt) x = sa + i;
                         }
