@@ -184,7 +184,12 @@ int spec_verify_attention(int batch, int num_draft_tokens, int num_q_heads, int 
  *   accept_length [batch] i32    accepted drafts + 1
  *   target_predict [batch*n] i32 (optional, NULL to skip) every row's choice
  * A path that would exceed accept_width raises SPEC_ST_DEPTH and stops there.
- * workspace: spec_accept_workspace_size(batch, n, vocab, 0) bytes.
+ * workspace: spec_accept_workspace_size(batch, n, vocab, 0) bytes (a 64-bit
+ *   key per verify row and 8192-entry chunk), 8-byte
+ *   aligned and zero-filled before its first use; every call leaves it
+ *   zero-filled again, so one workspace serves any number of calls in stream
+ *   order (concurrent calls need one each).  After a call that raised
+ *   SPEC_ST_SYNC, zero it again before the next call.
  * Logits must not be NaN.
  */
 size_t spec_accept_workspace_size(int batch, int num_draft_tokens, int64_t vocab, int sampled);

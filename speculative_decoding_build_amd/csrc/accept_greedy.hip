@@ -5,35 +5,62 @@
 // 行到最终输出路径" (三: accept_index holds verify rows; the last row's target
 // choice is the terminal token).
 //
-// Two launches: a chunked argmax sweep over every verify row (one 256-thread
-// workgroup per (8192-entry chunk, row), the chunk loaded once with 16-byte
-// loads), then one wavefront per request that merges its rows' chunk
-// partials and walks the tree.
+// Work item t (verify row t / nchunks, 8192-entry chunk t % nchunks) is
+// workgroup t of the grid: the chunk is loaded once with 16-byte loads and
+// its best entry is written, as one 64-bit key, to write-once slot t.  A slot
+// is 0 until written (a key is never 0), so the walker that reads a
+// request's slots needs no fence: it polls until all are non-zero, then
+// clears them for the next call (the workspace is zero after every call).
+//
+// One launch when the requests' walkers fit on the device at once: the last
+// `batch` workgroups of the grid walk a request each after their own chunk.
+// A walker waits only for chunk work, which never waits, and fewer walkers
+// than the device holds at once always leave room for the chunk workgroups
+// still to run, in whatever order they are dispatched.  Otherwise a second
+// launch walks (its polls find every slot written).
 #include "sweep_common.h"
 
 using namespace spec;
 
 namespace {
 
-struct ArgPart {
-    float v;
-    int32_t i;
+constexpr unsigned kSpinLimit = 1u << 20;   // polls of one slot before giving up
+
+// A row's best entry as one 64-bit key: the value's order-preserving bits
+// above, 0xFFFFFFFF - index below, so a larger key is a larger value or,
+// for equal values, a smaller index (the first index of the row maximum).
+// 0 is no entry; -0 is keyed as +0, the two comparing equal.
+__device__ __forceinline__ uint64_t arg_key(float v, int i) {
+    if (i < 0) return 0;
+    uint32_t bits = __float_as_uint(v == 0.f ? 0.f : v);
+    bits = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+    return ((uint64_t)bits << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+__device__ __forceinline__ int arg_key_index(uint64_t key) {
+    return key == 0 ? -1 : (int)(0xFFFFFFFFu - (uint32_t)key);
+}
+
+struct GreedyArgs {
+    const void *logits;
+    int64_t vocab;
+    bool vec_ok;
+    int batch, n, s1, nchunks;
+    const int32_t *cand, *r_index, *r_next, *r_sib;
+    int32_t *predict, *accept_index, *accept_length, *target_predict, *status;
+    uint64_t *slots;     // [batch * n][nchunks] chunk keys, written once per call
 };
 
-// ---- greedy: chunked argmax -----------------------------------------------
-
+// The best entry of chunk t % nchunks of verify row t / nchunks into slot t.
 template <int DT>
-__global__ __launch_bounds__(kSweepThreads) void argmax_partial_kernel(
-    const void *__restrict__ logits, int64_t vocab, int nchunks, bool vec_ok,
-    ArgPart *__restrict__ part) {
-    const int c = blockIdx.x;
-    const int64_t row = blockIdx.y;
+__device__ __forceinline__ void chunk_item(const GreedyArgs &A, int64_t t, uint64_t *s_wave) {
     const int tid = threadIdx.x;
-    const int64_t start = (int64_t)c * kChunk;
-    const int64_t end = min(vocab, start + kChunk);
-    const char *rowp = static_cast<const char *>(logits) + row * vocab * (DT == SPEC_BF16 ? 2 : 4);
+    const int64_t row = t / A.nchunks;
+    const int64_t start = (t % A.nchunks) * kChunk;
+    const int64_t end = min(A.vocab, start + kChunk);
+    const char *rowp = static_cast<const char *>(A.logits) + row * A.vocab * (DT == SPEC_BF16 ? 2 : 4);
     float x[kPerThread];
-    load_chunk<DT>(rowp, start, end, vec_ok, tid, x);
+    load_chunk<DT>(rowp, start, end, A.vec_ok, tid, x);
     float bv = -INFINITY;
     int bi = -1;
 #pragma unroll
@@ -44,64 +71,82 @@ __global__ __launch_bounds__(kSweepThreads) void argmax_partial_kernel(
             bi = (int)idx;
         }
     }
+    uint64_t key = arg_key(bv, bi);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, SPEC_WAVE);
-        const int oi = __shfl_xor(bi, o, SPEC_WAVE);
-        if (arg_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        const uint64_t other = __shfl_xor(key, o, SPEC_WAVE);
+        key = other > key ? other : key;
     }
-    __shared__ float s_v[kSweepThreads / SPEC_WAVE];
-    __shared__ int s_i[kSweepThreads / SPEC_WAVE];
-    if ((tid & 63) == 0) { s_v[tid >> 6] = bv; s_i[tid >> 6] = bi; }
+    if ((tid & 63) == 0) s_wave[tid >> 6] = key;
     __syncthreads();
     if (tid == 0) {
-        for (int w = 1; w < kSweepThreads / SPEC_WAVE; ++w)
-            if (arg_better(s_v[w], s_i[w], bv, bi)) { bv = s_v[w]; bi = s_i[w]; }
-        part[row * nchunks + c] = ArgPart{bv, bi};
+#pragma unroll
+        for (int w = 1; w < kSweepThreads / SPEC_WAVE; ++w) key = s_wave[w] > key ? s_wave[w] : key;
+        __hip_atomic_store(A.slots + t, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-// One wavefront per request: merge the chunk partials of the request's rows,
-// then walk from the root.
-__global__ __launch_bounds__(SPEC_WAVE) void greedy_walk_kernel(
-    int n, int s1, int total_rows, int nchunks, const ArgPart *__restrict__ part,
-    const int32_t *__restrict__ cand, const int32_t *__restrict__ r_index,
-    const int32_t *__restrict__ r_next, const int32_t *__restrict__ r_sib,
-    int32_t *__restrict__ predict, int32_t *__restrict__ accept_index,
-    int32_t *__restrict__ accept_length, int32_t *__restrict__ target_predict,
-    int32_t *__restrict__ status) {
-    __shared__ int s_tp[kMaxNodes];
-    __shared__ int s_row[kMaxNodes];
-    __shared__ int s_pred[kMaxNodes];
-    __shared__ int s_cand[kMaxNodes];
-    __shared__ int s_next[kMaxNodes];
-    __shared__ int s_sib[kMaxNodes];
+// Request b: collect its rows' keys from the slots (polling, bounded), clear
+// the slots, walk from the root and write the outputs.
+__device__ void walk_request(const GreedyArgs &A, int b) {
+    __shared__ uint64_t s_key[kMaxNodes];
+    __shared__ int s_tp[kMaxNodes], s_row[kMaxNodes], s_pred[kMaxNodes];
+    __shared__ int s_cand[kMaxNodes], s_next[kMaxNodes], s_sib[kMaxNodes];
     __shared__ int s_ai[kMaxNodes + 1];
-    __shared__ int s_len;
-    const int b = blockIdx.x;
-    const int k = threadIdx.x;
+    __shared__ int s_len, s_err;
+    const int tid = threadIdx.x;
+    const int n = A.n;
     const int base = b * n;
-    int err = 0;
-    if (k < n) {
-        // every lane loads its node's links and reduces its row's chunk partials
-        int row = r_index[base + k];
-        s_cand[k] = cand[base + k];
-        s_next[k] = r_next[base + k];
-        s_sib[k] = r_sib[base + k];
-        if (row < base || row >= base + n) { err |= SPEC_ST_RANGE; row = -1; }
-        int bi = -1;
-        float bv = -INFINITY;
-        if (row >= 0)
-            for (int c = 0; c < nchunks; ++c) {
-                const ArgPart p = part[(int64_t)row * nchunks + c];
-                if (arg_better(p.v, p.i, bv, bi)) { bv = p.v; bi = p.i; }
+    if (tid < n) s_key[tid] = 0;
+    if (tid == 0) s_err = 0;
+    __syncthreads();
+    // loads of up to four slots per thread go out together, then any empty
+    // one is polled; one timed-out slot ends every poll of the walker
+    const int nslots = n * A.nchunks;
+    uint64_t *rs = A.slots + (int64_t)base * A.nchunks;
+    for (int j0 = tid; j0 < nslots; j0 += 4 * kSweepThreads) {
+        uint64_t k4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u * kSweepThreads;
+            k4[u] = j < nslots ? __hip_atomic_load(rs + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u * kSweepThreads;
+            if (j >= nslots) continue;
+            uint64_t k = k4[u];
+            for (unsigned spins = 0; k == 0; ++spins) {
+                if (spins >= kSpinLimit || (__hip_atomic_load(&s_err, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_WORKGROUP) &
+                                            SPEC_ST_SYNC)) {
+                    atomicOr(&s_err, SPEC_ST_SYNC);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                k = __hip_atomic_load(rs + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-        s_tp[k] = bi;
-        s_row[k] = row;
-        s_pred[k] = 0;
+            atomicMax(reinterpret_cast<unsigned long long *>(&s_key[j / A.nchunks]),
+                      (unsigned long long)k);
+        }
     }
     __syncthreads();
-    if (k == 0) {
+    // every slot of the request has been read: clear them for the next call
+    for (int j = tid; j < nslots; j += blockDim.x)
+        __hip_atomic_store(rs + j, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int err = 0;
+    if (tid < n) {
+        int row = A.r_index[base + tid];
+        s_cand[tid] = A.cand[base + tid];
+        s_next[tid] = A.r_next[base + tid];
+        s_sib[tid] = A.r_sib[base + tid];
+        if (row < base || row >= base + n) { err |= SPEC_ST_RANGE; row = -1; }
+        s_tp[tid] = row >= 0 ? arg_key_index(s_key[row - base]) : -1;
+        s_row[tid] = row;
+        s_pred[tid] = 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
         int cur = 0, cnt = 0;
         s_ai[0] = s_row[0];
         for (int guard = 0; guard < n; ++guard) {
@@ -114,7 +159,7 @@ __global__ __launch_bounds__(SPEC_WAVE) void greedy_walk_kernel(
                 c = s_sib[c];
             }
             if (hit < 0) break;
-            if (cnt + 1 >= s1) { err |= SPEC_ST_DEPTH; break; }
+            if (cnt + 1 >= A.s1) { err |= SPEC_ST_DEPTH; break; }
             s_pred[cur] = s_cand[hit];
             ++cnt;
             s_ai[cnt] = s_row[hit];
@@ -124,22 +169,57 @@ __global__ __launch_bounds__(SPEC_WAVE) void greedy_walk_kernel(
         s_len = cnt + 1;
     }
     __syncthreads();
-    if (k < n && s_row[k] >= 0) {
-        predict[s_row[k]] = s_pred[k];
-        if (target_predict != nullptr) target_predict[s_row[k]] = s_tp[k];
+    if (tid < n && s_row[tid] >= 0) {
+        A.predict[s_row[tid]] = s_pred[tid];
+        if (A.target_predict != nullptr) A.target_predict[s_row[tid]] = s_tp[tid];
     }
-    for (int j = k; j < s1; j += SPEC_WAVE)
-        accept_index[(int64_t)b * s1 + j] = (j < s_len) ? s_ai[j] : -1;
-    if (k == 0) accept_length[b] = s_len;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, SPEC_WAVE);
-    if (k == 0) raise_status(status, err);
+    for (int j = tid; j < A.s1; j += blockDim.x)
+        A.accept_index[(int64_t)b * A.s1 + j] = (j < s_len) ? s_ai[j] : -1;
+    if (tid == 0) A.accept_length[b] = s_len;
+    if (err) atomicOr(&s_err, err);
+    __syncthreads();
+    if (tid == 0) raise_status(A.status, s_err);
+}
+
+// Chunk work for every (row, chunk); with WALK the last `batch` workgroups
+// then walk a request each.
+template <int DT, bool WALK>
+__global__ __launch_bounds__(kSweepThreads) void greedy_kernel(GreedyArgs A) {
+    __shared__ uint64_t s_wave[kSweepThreads / SPEC_WAVE];
+    const int64_t t = blockIdx.x;
+    chunk_item<DT>(A, t, s_wave);
+    if constexpr (WALK) {
+        const int64_t first_walker = (int64_t)gridDim.x - A.batch;
+        if (t >= first_walker) walk_request(A, (int)(t - first_walker));
+    }
+}
+
+// Second launch when the walkers cannot all be resident with the chunk work.
+__global__ __launch_bounds__(kSweepThreads) void greedy_walk_kernel(GreedyArgs A) {
+    walk_request(A, blockIdx.x);
+}
+
+// Workgroups of the fused kernel the device holds at once (0 if unknown).
+template <int DT>
+int fused_capacity(int dev) {
+    static int cached_device = -1, cap = 0;
+    if (dev != cached_device) {
+        int cus = 0, per = 0;
+        const bool ok =
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per, reinterpret_cast<const void *>(greedy_kernel<DT, true>), kSweepThreads, 0) ==
+                hipSuccess;
+        cap = ok ? cus * per : 0;
+        cached_device = dev;
+    }
+    return cap;
 }
 
 }  // namespace
 
 size_t spec_greedy_workspace_bytes(int batch, int n, int64_t vocab) {
-    return spec::align_up((size_t)batch * n * num_chunks(vocab) * sizeof(ArgPart), 256);
+    return spec::align_up((size_t)batch * n * num_chunks(vocab) * sizeof(uint64_t), 256);
 }
 
 int spec_check_accept_args(int batch, int n, int s1, int64_t vocab, int dtype) {
@@ -165,24 +245,49 @@ extern "C" int spec_accept_greedy(int batch, int n, int s1, int64_t vocab, int d
     if (!target_logits || !candidates || !retrieve_index || !retrieve_next_token ||
         !retrieve_next_sibling || !predict || !accept_index || !accept_length)
         return SPEC_ERR_NULL;
-    if (!workspace || workspace_bytes < spec_greedy_workspace_bytes(batch, n, vocab))
+    if (!workspace || workspace_bytes < spec_greedy_workspace_bytes(batch, n, vocab) ||
+        reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
         return SPEC_ERR_WORKSPACE;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int nch = num_chunks(vocab);
+    const int64_t items = (int64_t)batch * n * nch;
+    if (items > INT_MAX) return SPEC_ERR_UNSUPPORTED;
     const size_t eb = dtype == SPEC_BF16 ? 2 : 4;
-    const bool vec_ok = (vocab * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(target_logits) % 16 == 0;
-    ArgPart *part = static_cast<ArgPart *>(workspace);
-    const dim3 grid(nch, batch * n);
-    if (dtype == SPEC_BF16)
-        hipLaunchKernelGGL(argmax_partial_kernel<SPEC_BF16>, grid, dim3(kSweepThreads), 0, st,
-                           target_logits, vocab, nch, vec_ok, part);
-    else
-        hipLaunchKernelGGL(argmax_partial_kernel<SPEC_F32>, grid, dim3(kSweepThreads), 0, st,
-                           target_logits, vocab, nch, vec_ok, part);
-    hipLaunchKernelGGL(greedy_walk_kernel, dim3(batch), dim3(SPEC_WAVE), 0, st, n, s1,
-                       batch * n, nch, part, candidates, retrieve_index, retrieve_next_token,
-                       retrieve_next_sibling, predict, accept_index, accept_length,
-                       target_predict, dev_status);
+    GreedyArgs A{};
+    A.logits = target_logits;
+    A.vocab = vocab;
+    A.vec_ok = (vocab * eb) % 16 == 0 && reinterpret_cast<uintptr_t>(target_logits) % 16 == 0;
+    A.batch = batch;
+    A.n = n;
+    A.s1 = s1;
+    A.nchunks = nch;
+    A.cand = candidates;
+    A.r_index = retrieve_index;
+    A.r_next = retrieve_next_token;
+    A.r_sib = retrieve_next_sibling;
+    A.predict = predict;
+    A.accept_index = accept_index;
+    A.accept_length = accept_length;
+    A.target_predict = target_predict;
+    A.status = dev_status;
+    A.slots = static_cast<uint64_t *>(workspace);
+    const dim3 grid((unsigned)items);
+    int dev = 0;
+    const bool fused = hipGetDevice(&dev) == hipSuccess &&
+                       batch < (dtype == SPEC_BF16 ? fused_capacity<SPEC_BF16>(dev)
+                                                   : fused_capacity<SPEC_F32>(dev));
+    if (fused) {
+        if (dtype == SPEC_BF16)
+            hipLaunchKernelGGL((greedy_kernel<SPEC_BF16, true>), grid, dim3(kSweepThreads), 0, st, A);
+        else
+            hipLaunchKernelGGL((greedy_kernel<SPEC_F32, true>), grid, dim3(kSweepThreads), 0, st, A);
+    } else {
+        if (dtype == SPEC_BF16)
+            hipLaunchKernelGGL((greedy_kernel<SPEC_BF16, false>), grid, dim3(kSweepThreads), 0, st, A);
+        else
+            hipLaunchKernelGGL((greedy_kernel<SPEC_F32, false>), grid, dim3(kSweepThreads), 0, st, A);
+        hipLaunchKernelGGL(greedy_walk_kernel, dim3(batch), dim3(kSweepThreads), 0, st, A);
+    }
     return spec::launch_status();
 }
 

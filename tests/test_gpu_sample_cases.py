@@ -11,7 +11,8 @@ the walk into its less common branches.
   the other children, whose ratio is then infinite, and a residual that
   drops exactly one token;
 * three calls in a row on one workspace: each call must leave the workspace
-  zero-filled, as the next call expects it.
+  zero-filled, as the next call expects it (sampled and greedy);
+* greedy accept with more requests than its one-launch form holds at once.
 
 Same bar as the other sampled tests: bit-exact outputs except for requests
 the oracle marks exempt (a decision within 1e-6 of its threshold, or a
@@ -134,7 +135,8 @@ def test_sample_workspace_reused():
 
 def test_greedy_workspace_reused():
     """Three greedy accepts in a row on one workspace, each bit-exact against
-    the oracle (partials of one call must not leak into the next)."""
+    the oracle and each leaving the workspace zero (slots and counters of one
+    call must not leak into the next)."""
     cfg = W.shrink(W.CONFIGS[5], batch=3, hist=H8, vocab=30000)
     b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
     ws = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
@@ -151,3 +153,26 @@ def test_greedy_workspace_reused():
         np.testing.assert_array_equal(g["predict"], o["predict"])
         np.testing.assert_array_equal(g["accept_index"], o["accept_index"])
         np.testing.assert_array_equal(g["accept_length"], o["accept_length"])
+        # the call leaves the workspace as it found it: zero
+        assert int(torch.count_nonzero(ws)) == 0
+
+
+def test_greedy_two_launch_path():
+    """More requests than the one-launch greedy accept keeps resident at once
+    (its walkers would crowd out the chunk work): the walk runs as a second
+    launch.  Bit-exact against the oracle; the workspace is left zero."""
+    cfg = W.shrink(W.CONFIGS[4], batch=2200, hist=H8, vocab=300)
+    b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
+    say(f"[greedy two launches] b={b} n={n} V={cfg.vocab}")
+    w, t, tl, dl = _setup(cfg, 51)
+    ws = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
+                     device="cuda")
+    o = oracle.accept_greedy(tl, t["draft_tokens"], t["retrieve_index"], t["retrieve_next_token"],
+                             t["retrieve_next_sibling"], b, n, s1, cfg.dtype)
+    g = G.accept_greedy(w, tl, _tree(t), workspace=ws)
+    assert g["status"] == 0
+    np.testing.assert_array_equal(g["target_predict"], o["target_predict"])
+    np.testing.assert_array_equal(g["predict"], o["predict"])
+    np.testing.assert_array_equal(g["accept_index"], o["accept_index"])
+    np.testing.assert_array_equal(g["accept_length"], o["accept_length"])
+    assert int(torch.count_nonzero(ws)) == 0
