@@ -297,14 +297,16 @@ def main():
     op_ms = {}
     if args.mode == "graph":
         # per-operation GPU times: one graph per operation holding that
-        # operation for every input copy back to back, replayed between two
-        # events, so no host time falls between the launches
-        reps = max(2, math.ceil(64 / copies))
+        # operation at least 16 times back to back (cycling through the input
+        # copies), replayed between two events, so neither host time nor the
+        # launch of a graph falls between the operations
+        per_graph = max(16, copies)
+        reps = max(2, math.ceil(64 / per_graph))
         for j, op in enumerate(OPS):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for c in calls:
-                    c[j]()
+                for i in range(per_graph):
+                    calls[i % copies][j]()
             g.replay()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -313,7 +315,7 @@ def main():
                 g.replay()
             e1.record()
             torch.cuda.synchronize()
-            op_ms[op] = e0.elapsed_time(e1) / (reps * copies)
+            op_ms[op] = e0.elapsed_time(e1) / (reps * per_graph)
             del g
     else:
         # eager: events around every operation of eager steps (host launch

@@ -12,9 +12,10 @@
 // candidate is kept iff fewer than n-1 candidates beat it under
 // (score desc, flat index asc), and its node index is one plus the number of
 // kept candidates with a smaller flat index (a block prefix count), which is
-// exactly "take the top n-1, then sort their indices ascending".  Structure
-// work (depth, ancestor bits, child/sibling links) runs on one wavefront with
-// a lane per node.
+// exactly "take the top n-1, then sort their indices ascending"; the
+// comparisons of each candidate are shared among all threads of the
+// workgroup.  Structure work (depth, ancestor bits, child/sibling links)
+// runs on one wavefront with a lane per node.
 #include "spec_common.h"
 
 namespace {
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     __shared__ int32_t s_parent[kMaxNodes];
     __shared__ uint64_t s_kids[kMaxNodes];     // children of each node as a bit set
     __shared__ int32_t s_wave_cnt[kThreads / SPEC_WAVE];
+    __shared__ int32_t s_beats[kThreads];      // per-candidate beat counts (one round)
     __shared__ int32_t s_bonus, s_len;
 
     const int r = blockIdx.x;
@@ -73,36 +75,47 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     __syncthreads();
 
     // ---- kept iff fewer than n-1 candidates beat it; node index = 1 + number
-    // of kept candidates with a smaller flat index (rounds of kThreads
-    // candidates keep flat order: round i holds f = i*kThreads + tid)
-    const int ncand2 = ncand & ~1;
+    // of kept candidates with a smaller flat index.  A round ranks up to
+    // `per` candidates in flat order (round i: f = i*per + c); each
+    // candidate's count is split into `parts` ranges of the keys, one per
+    // thread, so all waves share the comparisons.
+    const int per = ncand < kThreads ? (ncand + SPEC_WAVE - 1) / SPEC_WAVE * SPEC_WAVE : kThreads;
+    const int parts = kThreads / per;                  // 1 .. 16
+    const int span = ((ncand + parts - 1) / parts + 1) & ~1;   // keys per part, even
     int before_rounds = 0;
-    for (int f0 = 0; f0 < ncand; f0 += kThreads) {
-        const int f = f0 + tid;
-        bool kept = false;
-        if (f < ncand && keep > 0) {
-            const uint64_t mine = s_key[f];
-            // four independent counts, so several LDS reads are in flight
-            int b0 = 0, b1 = 0, b2 = 0, b3 = 0;
-            int g = 0;
-            for (; g + 8 <= ncand2; g += 8) {
-                const uint4 w0 = *reinterpret_cast<const uint4 *>(&s_key[g]);
-                const uint4 w1 = *reinterpret_cast<const uint4 *>(&s_key[g + 2]);
-                const uint4 w2 = *reinterpret_cast<const uint4 *>(&s_key[g + 4]);
-                const uint4 w3 = *reinterpret_cast<const uint4 *>(&s_key[g + 6]);
-                b0 += (((uint64_t)w0.y << 32 | w0.x) > mine) + (((uint64_t)w0.w << 32 | w0.z) > mine);
-                b1 += (((uint64_t)w1.y << 32 | w1.x) > mine) + (((uint64_t)w1.w << 32 | w1.z) > mine);
-                b2 += (((uint64_t)w2.y << 32 | w2.x) > mine) + (((uint64_t)w2.w << 32 | w2.z) > mine);
-                b3 += (((uint64_t)w3.y << 32 | w3.x) > mine) + (((uint64_t)w3.w << 32 | w3.z) > mine);
+    for (int f0 = 0; f0 < ncand; f0 += per) {
+        {
+            const int c = tid % per, part = tid / per;
+            const int f = f0 + c;
+            int beats = 0;
+            if (part < parts && f < ncand && keep > 0) {
+                const uint64_t mine = s_key[f];
+                const int g_lo = part * span;
+                const int g_hi = min(ncand, g_lo + span);
+                const int g_hi2 = g_lo + ((g_hi - g_lo) & ~1);
+                // two independent counts, so several LDS reads are in flight
+                int b0 = 0, b1 = 0;
+                int g = g_lo;
+                for (; g + 4 <= g_hi2; g += 4) {
+                    const uint4 w0 = *reinterpret_cast<const uint4 *>(&s_key[g]);
+                    const uint4 w1 = *reinterpret_cast<const uint4 *>(&s_key[g + 2]);
+                    b0 += (((uint64_t)w0.y << 32 | w0.x) > mine) + (((uint64_t)w0.w << 32 | w0.z) > mine);
+                    b1 += (((uint64_t)w1.y << 32 | w1.x) > mine) + (((uint64_t)w1.w << 32 | w1.z) > mine);
+                }
+                for (; g < g_hi2; g += 2) {
+                    const uint4 w = *reinterpret_cast<const uint4 *>(&s_key[g]);
+                    b0 += (((uint64_t)w.y << 32 | w.x) > mine) + (((uint64_t)w.w << 32 | w.z) > mine);
+                }
+                if (g_hi2 < g_hi) b0 += s_key[g_hi2] > mine;
+                beats = b0 + b1;
             }
-            for (; g < ncand2; g += 2) {
-                const uint4 w = *reinterpret_cast<const uint4 *>(&s_key[g]);
-                b0 += (((uint64_t)w.y << 32 | w.x) > mine) + (((uint64_t)w.w << 32 | w.z) > mine);
-            }
-            int beats = b0 + b1 + b2 + b3;
-            if (ncand2 != ncand) beats += s_key[ncand - 1] > mine;
-            kept = beats < keep;
+            if (part == 0) s_beats[c] = beats;
+            __syncthreads();
+            if (part > 0 && part < parts && f < ncand) atomicAdd(&s_beats[c], beats);
+            __syncthreads();
         }
+        const int f = f0 + tid;
+        const bool kept = tid < per && f < ncand && keep > 0 && s_beats[tid] < keep;
         // block prefix count of kept flags in thread order
         const uint64_t ball = __ballot(kept);
         const int in_wave = __popcll(ball & ((1ull << lane) - 1ull));
@@ -114,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
             if (w < wave) before += s_wave_cnt[w];
             round_total += s_wave_cnt[w];
         }
-        if (f < ncand) {
+        if (tid < per && f < ncand) {
             int node = 0;
             if (kept && before < keep) {
                 node = before + 1;               // node index 1 .. n-1
@@ -150,21 +163,19 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
             }
         }
     }
-    if (wave == 0 && k < n) s_parent[k] = par;
+    if (wave == 0 && k < n) {
+        s_parent[k] = par;
+        s_kids[k] = 0;
+    }
     __syncthreads();
     if (wave != 0) return;
 
-    // children of every node as a bit set (lane j gets the set of node j):
-    // first child = lowest set bit, next sibling = lowest bit of the
-    // parent's set above k
-    uint64_t kids = 0;
-    for (int j = 0; j < n; ++j) {
-        const uint64_t m = __ballot(k >= 1 && k < n && par == j);
-        if (k == j) kids = m;
-    }
-    if (k < n) s_kids[k] = kids;
+    // children of every node as a bit set: first child = lowest set bit,
+    // next sibling = lowest bit of the parent's set above k
+    if (k >= 1 && k < n) atomicOr(reinterpret_cast<unsigned long long *>(&s_kids[par]), 1ull << k);
     // only wave 0 is left, and one wave's LDS accesses complete in order
     __builtin_amdgcn_wave_barrier();
+    const uint64_t kids = k < n ? s_kids[k] : 0;
     if (k < n) {
         uint64_t bits = 1ull << k;
         int depth = 0;
