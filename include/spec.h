@@ -254,7 +254,8 @@ int spec_accept_sample(int batch, int num_draft_tokens, int accept_width, int64_
  *   num_free     [batch] i32
  * Entries of accept_index that are -1 are skipped; rows, slots or pages out
  * of range raise SPEC_ST_RANGE and that row is not moved.  Requests must
- * own disjoint slots.
+ * own disjoint slots.  num_draft_tokens <= 64 (else SPEC_ERR_UNSUPPORTED),
+ * accept_width <= 65.
  */
 int spec_compact_kv(int batch, int num_draft_tokens, int accept_width, int num_layers,
                     int num_kv_heads, int head_dim, int page_size, int dtype, void *k_pool,
