@@ -91,6 +91,19 @@ __device__ __forceinline__ int64_t key_slot(const AttnParams &P, int b, int L, i
     return slot;
 }
 
+// A split with no keys (past the sequence, or a sequence length out of
+// range) still writes (max, sum) = (-inf, 0) for its rows, so the merge can
+// take every split's partial without reading the sequence length.
+__device__ __forceinline__ void mark_empty_split(const AttnParams &P, int b, int kvh, int split,
+                                                 int rg) {
+    if (P.nsplit == 1) return;
+    const int r0 = rg * P.rows_per_group;
+    const int r1 = min(P.rows, r0 + P.rows_per_group);
+    const int64_t base = (((int64_t)b * P.hkv + kvh) * P.nsplit + split) * P.rows;
+    for (int rho = r0 + (int)threadIdx.x; rho < r1; rho += blockDim.x)
+        P.part_ml[base + rho] = make_float2(-INFINITY, 0.f);
+}
+
 // ---------------------------------------------------------------------------
 // work decomposition shared by the split kernels
 // ---------------------------------------------------------------------------
@@ -179,10 +192,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
     int err = 0;
     if (L < 0 || L > P.max_seq_len) {
         if (tid == 0 && split == 0 && rg == 0) spec::raise_status(P.status, SPEC_ST_RANGE);
+        mark_empty_split(P, b, kvh, split, rg);
         return;
     }
     const int ke = min(L + P.n, kb + P.split_len);
-    if (kb >= ke) return;
+    if (kb >= ke) {
+        mark_empty_split(P, b, kvh, split, rg);
+        return;
+    }
     const int ntiles = (ke - kb + kTileKeys - 1) / kTileKeys;
     __shared__ int32_t s_pre[kPreTiles * kTileKeys];
     __shared__ int32_t s_tree[kMaxTreeNodes];
@@ -470,11 +487,15 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(AttnParams P) {
     int err = 0;
     if (L < 0 || L > P.max_seq_len) {
         if (tid == 0 && split == 0 && rg == 0) spec::raise_status(P.status, SPEC_ST_RANGE);
+        mark_empty_split(P, b, kvh, split, rg);
         return;
     }
     const int kb = split * P.split_len;
     const int ke = min(L + P.n, kb + P.split_len);
-    if (kb >= ke) return;
+    if (kb >= ke) {
+        mark_empty_split(P, b, kvh, split, rg);
+        return;
+    }
     const float *kpool = static_cast<const float *>(P.k_pool);
     const float *vpool = static_cast<const float *>(P.v_pool);
     const int r0 = rg * P.rows_per_group;
@@ -547,33 +568,46 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
     const int64_t row = vec / P.hq;
     const int node = row % P.n;
     const int b = row / P.n;
-    const int L = P.seq_lens[b];
-    if (L < 0 || L > P.max_seq_len) return;
     const int kvh = h / P.group;
     const int rho = node * P.group + h % P.group;
-    const int ns = min(P.nsplit, (L + P.n + P.split_len - 1) / P.split_len);
-    const int64_t base = ((int64_t)b * P.hkv + kvh) * P.nsplit;
+    // every split wrote its (max, sum), empty ones (-inf, 0), so the
+    // partials' loads go out with these (one round, no sequence length);
+    // an empty split's O is never read into the sum (weight 0, and its
+    // memory was not written)
+    const int ns = P.nsplit;
+    const int64_t base = ((int64_t)b * P.hkv + kvh) * ns;
     const float2 ml = lane < ns ? P.part_ml[(base + lane) * P.rows + rho] : make_float2(-INFINITY, 0.f);
-    const float M = spec::wave_max(ml.x);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    const float w = lane < ns ? exp2f(ml.x - Mu) : 0.f;
-    const float lsum = spec::wave_sum(w * ml.y);
-    float acc[PER] = {};
     const float *po = P.part_o + (base * P.rows + rho) * D + lane * PER;
     const int64_t sstride = (int64_t)P.rows * D;
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-        float x[8][PER];
+    constexpr int kBatch = 16;
+    float x[kBatch][PER];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int s = min(s0 + u, ns - 1);
+    for (int u = 0; u < kBatch; ++u) {
+        const int s = min(u, ns - 1);
 #pragma unroll
-            for (int j = 0; j < PER; ++j) x[u][j] = po[s * sstride + j];
+        for (int j = 0; j < PER; ++j) x[u][j] = po[s * sstride + j];
+    }
+    const float M = spec::wave_max(ml.x);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    const float w = (lane < ns && ml.x != -INFINITY) ? exp2f(ml.x - Mu) : 0.f;
+    const float lsum = spec::wave_sum(w * ml.y);
+    float acc[PER] = {};
+    for (int s0 = 0; s0 < ns; s0 += kBatch) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int s = min(s0 + u, ns - 1);
+#pragma unroll
+                for (int j = 0; j < PER; ++j) x[u][j] = po[s * sstride + j];
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kBatch; ++u) {
             const float ws = s0 + u < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u)) : 0.f;
+            if (ws > 0.f) {
 #pragma unroll
-            for (int j = 0; j < PER; ++j) acc[j] = fmaf(ws, x[u][j], acc[j]);
+                for (int j = 0; j < PER; ++j) acc[j] = fmaf(ws, x[u][j], acc[j]);
+            }
         }
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
