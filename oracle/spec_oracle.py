@@ -30,6 +30,9 @@ Readings where the pages are silent (each also listed in the design notes):
   * Sampled accept: one uniform per tree node tests that node; one final
     uniform per request draws the terminal token by inverse CDF in vocabulary
     order; rejected siblings update the residual recursively.
+  * Target-only sampled accept: the siblings under node k share the coin
+    u[k] (the root's first, then each accepted node's); the terminal token
+    is drawn like the sampled accept's, from relu(p - buffer).
   * Malformed trees: a node whose parent is not selected (or whose parent
     index is out of range) hangs off the root and raises a status bit.
 
@@ -370,6 +373,91 @@ def accept_sample(target_logits, draft_logits, temperature, uniforms, final_unif
         x = int(np.argmax(cdf > target)) if cdf[-1] > target else int(R.size - 1)
         lo = cdf[x - 1] if x > 0 else 0.0
         draw_margin[r] = min((target - lo) / total, (cdf[x] - target) / total)
+        predict[row] = x
+        accept_length[r] = cnt + 1
+    return dict(predict=predict, accept_index=accept_index, accept_length=accept_length,
+                margin=margin, draw_margin=draw_margin,
+                exempt=(margin < band) | (draw_margin < draw_band), status=status)
+
+
+def accept_target_only(target_logits, temperature, threshold_single, threshold_acc, uniforms,
+                       final_uniforms, candidates, retrieve_index, retrieve_next_token,
+                       retrieve_next_sibling, b, n, s1, dtype, band=1e-6, draw_band=2e-8,
+                       tiny=1e-30):
+    """[P2] 四 (Target-only Tree Sampling), with the two thresholds of [P1]
+    三条判定路径: at node cur, p is the target distribution of row(cur) and the
+    sibling accumulator starts at 0.  Each child c (sibling order) with token
+    t adds p(t) to the accumulator and is accepted iff p(t) > 0 and (coin <
+    accumulator / threshold_acc or p(t) >= threshold_single).  The coin of the
+    siblings under cur is u[cur]: the pages switch to the accepted node's
+    random number together with its distribution, starting from the root's.
+    A rejected child's p(t) is written at token t into row(cur) of a work
+    buffer that starts at zero (no draft distribution is used).  With no child
+    accepted, or at a leaf, the terminal token is drawn from relu(p - buffer)
+    of row(cur) by inverse CDF in vocabulary order with the request's final
+    uniform (the draw of accept_sample).  [P5] 5.6: the walk is the greedy
+    walk's.
+
+    ``margin`` is the smallest distance of a test to its boundary: |coin -
+    accumulator / threshold_acc|, |p(t) - threshold_single|, and p(t) itself
+    when 0 < p(t) < ``tiny`` (a probability a float32 exponential may
+    flush to zero); ``exempt`` as in accept_sample.
+    """
+    tl = widen(target_logits, dtype)
+    cand = np.asarray(candidates).reshape(b, n)
+    ts, ta = float(threshold_single), float(threshold_acc)
+    predict = np.zeros(b * n, np.int64)
+    accept_index = np.full((b, s1), -1, np.int64)
+    accept_length = np.zeros(b, np.int64)
+    margin = np.full(b, np.inf)
+    draw_margin = np.full(b, np.inf)
+    status = 0
+    for r in range(b):
+        T = float(temperature[r])
+        cur = 0
+        cnt = 0
+        accept_index[r, 0] = retrieve_index[r, 0]
+        while True:
+            row = int(retrieve_index[r, cur])
+            p = softmax_t(tl[row], T)
+            buf = np.zeros_like(p)
+            coin = float(uniforms[r, cur])
+            acc = 0.0
+            c = int(retrieve_next_token[r, cur])
+            hit = -1
+            while c != -1:
+                t = int(cand[r, c])
+                pt = p[t]
+                acc += pt
+                margin[r] = min(margin[r], abs(coin - acc / ta), abs(pt - ts))
+                if 0.0 < pt < tiny:
+                    margin[r] = min(margin[r], pt)
+                if pt > 0.0 and (coin < acc / ta or pt >= ts):
+                    hit = c
+                    break
+                buf[t] = pt
+                c = int(retrieve_next_sibling[r, c])
+            if hit < 0:
+                break
+            if cnt + 1 >= s1:
+                status |= ST_DEPTH
+                break
+            predict[row] = cand[r, hit]
+            cnt += 1
+            accept_index[r, cnt] = retrieve_index[r, hit]
+            cur = hit
+        # terminal token: inverse CDF of relu(p - buffer) in vocabulary order
+        row = int(retrieve_index[r, cur])
+        R = np.maximum(p - buf, 0.0)
+        total = R.sum()
+        if total <= 0.0:
+            status |= ST_ZERO_RESIDUAL
+        target = float(final_uniforms[r]) * total
+        cdf = np.cumsum(R)
+        x = int(np.argmax(cdf > target)) if cdf[-1] > target else int(R.size - 1)
+        lo = cdf[x - 1] if x > 0 else 0.0
+        if total > 0.0:
+            draw_margin[r] = min((target - lo) / total, (cdf[x] - target) / total)
         predict[row] = x
         accept_length[r] = cnt + 1
     return dict(predict=predict, accept_index=accept_index, accept_length=accept_length,

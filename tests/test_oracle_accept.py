@@ -369,3 +369,138 @@ def test_compact_separate_verify_slots_all_freed():
     assert res["free_slots"].tolist() == [10, 11, 12] and res["num_free"].tolist() == [3]
     np.testing.assert_array_equal(res["k_pool"][:, 2], kp[:, 10])
     np.testing.assert_array_equal(res["k_pool"][:, 3], kp[:, 12])
+
+
+# ---------------------------------------------------------------------------
+# target-only sampled accept
+# ---------------------------------------------------------------------------
+
+def _links(parent, b):
+    """retrieve arrays of b copies of the tree given by ``parent`` (node 0 the
+    root, children in ascending node order)."""
+    n = len(parent)
+    rn = np.full((b, n), -1)
+    rs = np.full((b, n), -1)
+    for k in range(n):
+        kids = [c for c in range(n) if parent[c] == k]
+        if kids:
+            rn[:, k] = kids[0]
+            for a, c in zip(kids, kids[1:]):
+                rs[:, a] = c
+    return np.arange(b * n).reshape(b, n), rn, rs
+
+
+def _target_only(rows_p, parent, tokens, u, uf, ts=1.0, ta=1.0, T=1.0):
+    """One request per entry of ``uf``: tree ``parent``, node tokens
+    ``tokens``, row k's target law rows_p[k] (given as logits log p), coins
+    u[request, node]."""
+    b = len(uf)
+    n = len(parent)
+    with np.errstate(divide="ignore"):
+        logit = np.log(np.asarray(rows_p, np.float64))
+    logit[~np.isfinite(logit)] = -np.inf
+    tl = np.tile(logit, (b, 1)).astype(np.float32)
+    cand = np.tile(np.asarray(tokens), b)
+    ri, rn, rs = _links(parent, b)
+    return oracle.accept_target_only(tl, np.full(b, T, np.float32), ts, ta,
+                                     np.asarray(u, np.float32).reshape(b, n),
+                                     np.asarray(uf, np.float32), cand, ri, rn, rs, b, n, n, "f32")
+
+
+def test_target_only_thresholds_one_give_the_target_law():
+    """Thresholds 1: child j is accepted iff the coin lies below the mass of
+    children 1..j, and the terminal draw excludes the tried children, so the
+    output law is exactly p (the children's tokens first, then the rest)."""
+    rng = np.random.default_rng(7)
+    V = 7
+    p = rng.dirichlet(np.ones(V))
+    kids = [4, 1, 6]
+    parent = [-1, 0, 0, 0]
+    tokens = [0] + kids
+    m = 4000
+    g = _grid(m)
+    acc = _target_only([p] * 4, parent, tokens, np.stack([g] + [np.zeros(m)] * 3, 1),
+                       np.full(m, 0.5))
+    law = np.zeros(V)
+    took = acc["accept_length"] == 2
+    for r in np.nonzero(took)[0]:
+        law[acc["predict"][4 * r]] += 1.0 / m
+    rate = took.mean()
+    assert abs(rate - p[kids].sum()) <= 1 / m
+    rej = _target_only([p] * 4, parent, tokens, np.stack([np.full(m, 0.9999999)] + [np.zeros(m)] * 3, 1), g)
+    assert (rej["accept_length"] == 1).all()
+    hist = np.bincount(rej["predict"][0::4], minlength=V) / m
+    assert hist[kids].sum() == 0
+    law += (1 - rate) * hist
+    np.testing.assert_allclose(law, p, atol=3 / m)
+
+
+def test_target_only_two_level_chi_square():
+    """Random coins on a 2 x 2 tree: the first output follows the root row's
+    law, and after the first child is accepted the second output follows
+    that child's row law (the accumulator and the coin are per level)."""
+    rng = np.random.default_rng(11)
+    V = 24
+    parent = [-1, 0, 0, 1, 1, 2, 2]
+    n = len(parent)
+    logits = rng.normal(0, 1.2, (n, V))
+    rows_p = [oracle.softmax_t(logits[k].astype(np.float32), 1.0) for k in range(n)]
+    tokens = [0, 3, 9, 5, 7, 1, 2]
+    trials = 60000
+    res = _target_only(rows_p, parent, tokens, rng.random((trials, n)), rng.random(trials))
+    first = res["predict"][res["accept_index"][:, 0]]
+    counts = np.bincount(first, minlength=V)
+    p0 = rows_p[0]
+    chi2 = ((counts - trials * p0) ** 2 / (trials * p0)).sum()
+    assert chi2 < stats.chi2.ppf(1 - 1e-3, V - 1), chi2
+    via1 = res["accept_index"][:, 1] == np.arange(trials) * n + 1
+    second = res["predict"][res["accept_index"][via1, 1]]
+    c2 = np.bincount(second, minlength=V)
+    m1 = int(via1.sum())
+    p1 = rows_p[1]
+    chi2 = ((c2 - m1 * p1) ** 2 / (m1 * p1)).sum()
+    assert chi2 < stats.chi2.ppf(1 - 1e-3, V - 1), chi2
+
+
+def test_target_only_accumulator_and_coin_per_level():
+    """Root child (p = 0.6) accepted by the root's coin 0.5; its child
+    (p = 0.2) is then tested against its own coin and a fresh accumulator:
+    coin 0.3 rejects (an accumulator carried over, 0.8, would accept), coin
+    0.1 accepts (the root's coin, 0.5, would reject)."""
+    V = 4
+    p = np.array([0.1, 0.6, 0.2, 0.1])
+    parent = [-1, 0, 1]
+    tokens = [0, 1, 2]
+    for coin2, accepted in ((0.3, False), (0.1, True)):
+        res = _target_only([p] * 3, parent, tokens, [[0.5, coin2, 0.0]], [0.5])
+        assert res["accept_length"][0] == (3 if accepted else 2), coin2
+
+
+def test_target_only_threshold_single_and_zero_guard():
+    V = 5
+    p = np.array([0.3, 0.35, 0.25, 0.1, 0.0])
+    parent = [-1, 0, 0]
+    # p >= threshold_single accepts whatever the coin
+    res = _target_only([p] * 3, parent, [0, 1, 2], [[0.999, 0, 0]], [0.5], ts=0.3)
+    assert res["accept_length"][0] == 2 and res["accept_index"][0, 1] == 1
+    res = _target_only([p] * 3, parent, [0, 2, 3], [[0.999, 0, 0]], [0.5], ts=0.3)
+    assert res["accept_length"][0] == 1
+    # a zero-probability child is never accepted, not even with
+    # threshold_single 0 or a coin of 0
+    res = _target_only([p] * 3, parent, [0, 4, 3], [[0.0, 0, 0]], [0.5], ts=0.0)
+    assert res["accept_index"][0, 1] == 2
+    res = _target_only([p] * 2, [-1, 0], [0, 4], [[0.0, 0]], [0.5], ts=0.0)
+    assert res["accept_length"][0] == 1 and res["predict"][0] != 4
+
+
+def test_target_only_threshold_acc_scales_the_test():
+    """threshold_acc = 0.5: the first child is accepted with probability
+    min(1, 2 p(t))."""
+    rng = np.random.default_rng(5)
+    p = rng.dirichlet(np.ones(6))
+    t = int(np.argsort(p)[2])
+    m = 4000
+    res = _target_only([p] * 2, [-1, 0], [0, t], np.stack([_grid(m), np.zeros(m)], 1),
+                       np.full(m, 0.5), ta=0.5)
+    rate = np.mean(res["accept_length"] == 2)
+    assert abs(rate - min(1.0, 2 * p[t])) <= 1 / m
