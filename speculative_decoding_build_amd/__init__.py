@@ -7,8 +7,8 @@ arguments: it checks that every tensor lives on the current GPU, is
 contiguous and holds at least the elements the call will touch, then passes
 ``data_ptr()`` and the current HIP stream.  Every step runs in the library's
 HIP kernels; there is no other code path.  Importing this package fails if
-the library has not been built (``python -m
-speculative_decoding_build_amd.build_lib``).
+the library has not been built (``python
+speculative_decoding_build_amd/build_lib.py``).
 """
 from __future__ import annotations
 
@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libspecmi.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m speculative_decoding_build_amd.build_lib`")
+                      "`python speculative_decoding_build_amd/build_lib.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

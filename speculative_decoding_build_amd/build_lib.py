@@ -1,6 +1,9 @@
 """Builds libspecmi.so (the C-ABI library) from csrc/*.hip for gfx950.
 
-    python -m speculative_decoding_build_amd.build_lib
+    python speculative_decoding_build_amd/build_lib.py
+
+Run as a script (the package itself refuses to import before the library
+exists).
 """
 import glob
 import os
