@@ -18,9 +18,9 @@
 //     in the lane (one cross-half exchange for the max).  P^T feeds the PV
 //     product straight from the score registers: the 16 keys of one MFMA
 //     k-step are taken in the order the score layout already holds them, and
-//     V^T is read in that same key order.  K tiles sit row-major in LDS; V
-//     tiles are transposed on their way into LDS so the V^T operand is two
-//     8-byte reads.  64-key tiles are double-buffered, the next tile's global
+//     V^T is stored in that same key order.  K tiles sit row-major in LDS; V
+//     tiles are transposed on their way into LDS so the V^T operand is one
+//     16-byte read.  64-key tiles are double-buffered, the next tile's global
 //     loads in flight during the current tile's math.
 //   * f32: the same splits on the vector ALUs (one wavefront per query row,
 //     lanes across head_dim).
@@ -41,7 +41,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTileKeys = 64;
 constexpr int kTargetGroups = 512;      // workgroups a launch aims for (one co-resident round)
 constexpr int kMinTiles = 4;            // 64-key tiles per split at least
-constexpr int kPreTiles = 4;            // tiles whose page entries the prologue fetches
+constexpr int kChunkTiles = 8;          // tiles per chunk of the slot ring
+constexpr int kChunkKeys = kChunkTiles * kTileKeys;
 constexpr int kMaxTreeNodes = 64;
 constexpr int kSmallGrid = 512;         // fewer 8-wave workgroups than this: use 4-wave ones
 
@@ -137,12 +138,13 @@ __device__ __forceinline__ Work decode_work(const AttnParams &P, int w, bool xcd
 // One workgroup: NW waves, each owning 32 query rows (one 32x32 MFMA column
 // block).  Per 64-key tile the pipeline is
 //     write tile t+1 (registers -> LDS, V transposed)
-//     issue the global loads of tile t+3 (slots read from LDS)
-//     look up the slots of tile t+4 (page table / tree slots, wave 0)
+//     issue the global loads of tile t+3 (slots read from the LDS slot ring)
 //     compute tile t (S^T = K Q^T, softmax, O^T += V^T P^T)
 //     barrier
-// so two tiles of K/V are in flight while one is computed, and the page
-// table is read two tiles before the data it addresses.
+// so two tiles of K/V are in flight while one is computed.  The slot ring
+// holds two chunks of 8 tiles; a chunk's page-table entries are loaded 7
+// tiles before the first load that needs them, so no tile waits on the page
+// table.
 //
 // Softmax runs in the log2 domain on raw scores: p = exp2(s*C - m) with
 // C = scale*log2(e).  The running max m is raised (and O, l rescaled) only
@@ -155,11 +157,15 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams P, int xcd_remap) {
     static_assert(D == 64 || D == 128, "head_dim");
     constexpr int KS = D + 8;              // K row stride (bf16), 16-byte pad
-    constexpr int VS = kTileKeys + 4;      // V^T row stride (bf16): 34 dwords, so the
-                                           // 8-byte reads of 32 rows hit distinct banks
+    constexpr int VS = kTileKeys + 8;      // V^T row stride (bf16): 36 dwords, so the
+                                           // 16-byte reads of 16 rows hit distinct banks
     constexpr int NT = NW * 64;
     constexpr int KUNITS = kTileKeys * (D / 8);        // 16-byte K pieces per tile
     constexpr int VUNITS = (kTileKeys / 4) * (D / 8);  // 4 keys x 8 dims per V piece
+    static_assert(kChunkKeys % NT == 0, "chunk keys per thread");
+    // a tile's loads are issued LEAD tiles before it is computed (two
+    // register sets in flight)
+    constexpr int LEAD = 3;
     constexpr int KPER = (KUNITS + NT - 1) / NT;
     constexpr int VPER = (VUNITS + NT - 1) / NT;
     constexpr int DK = D / 16;             // MFMA k-steps over head_dim
@@ -167,7 +173,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
 
     __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kTileKeys * KS];
     __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * VS];
-    __shared__ int64_t s_slot[2][kTileKeys];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -179,14 +184,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
     const int b = wk.b, kvh = wk.kvh, split = wk.split, rg = wk.rg;
     const int kb = split * P.split_len;
     // Loads that do not depend on the sequence length go out with it: the
-    // page-table entries of the split's first kPreTiles tiles and the
+    // page-table entries of the split's first two slot chunks and the
     // request's tree slots.
-    int pre_page = -1, pre_tree = -1;
-    if (tid < kPreTiles * kTileKeys) {
-        const int p = kb + tid;
+    constexpr int KPT = kChunkKeys / NT;   // chunk keys per thread
+    int pg[2 * KPT];
+#pragma unroll
+    for (int j = 0; j < 2 * KPT; ++j) {
+        const int p = kb + tid + j * NT;
+        pg[j] = -1;
         if (P.page_table != nullptr && p < P.max_pages * P.page_size)
-            pre_page = P.page_table[(int64_t)b * P.max_pages + p / P.page_size];
+            pg[j] = P.page_table[(int64_t)b * P.max_pages + p / P.page_size];
     }
+    int pre_tree = -1;
     if (tid < P.n) pre_tree = P.out_cache_loc[(int64_t)b * P.n + tid];
     const int L = P.seq_lens[b];
     int err = 0;
@@ -201,9 +210,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
         return;
     }
     const int ntiles = (ke - kb + kTileKeys - 1) / kTileKeys;
-    __shared__ int32_t s_pre[kPreTiles * kTileKeys];
+    // Slot ring: the physical slots of two chunks of kChunkKeys keys (-1 past
+    // the split or invalid).  Chunk c lives in half c & 1; its page entries
+    // are loaded seven tiles before its first tile's K/V loads need them.
+    __shared__ int32_t s_ring[2][kChunkKeys];
     __shared__ int32_t s_tree[kMaxTreeNodes];
-    if (tid < kPreTiles * kTileKeys) s_pre[tid] = pre_page;
     if (tid < P.n) s_tree[tid] = pre_tree;
 
     // ---- query fragments (B operand of S^T = K Q^T) -----------------------
@@ -234,42 +245,36 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
     const __bf16 *kpool = static_cast<const __bf16 *>(P.k_pool);
     const __bf16 *vpool = static_cast<const __bf16 *>(P.v_pool);
 
-    // slot of key position p of this request, -1 past the split or invalid
-    // (the first kPreTiles tiles' page entries and the tree slots come from
-    // LDS)
-    auto lookup = [&](int p) -> int64_t {
+    // slot of key position p of this request from its page entry (history)
+    // or the tree slots; -1 past the split or when out of range
+    auto slot_of = [&](int p, int page) -> int32_t {
         if (p >= ke) return -1;
         int64_t slot;
-        if (p < L) {
-            const int rel = p - kb;
-            const int page = rel < kPreTiles * kTileKeys
-                                 ? s_pre[rel]
-                                 : P.page_table[(int64_t)b * P.max_pages + p / P.page_size];
+        if (p < L)
             slot = page < 0 ? -1 : (int64_t)page * P.page_size + p % P.page_size;
-        } else {
+        else
             slot = s_tree[p - L];
-        }
         if (slot < 0 || slot >= P.num_slots) {
             err |= SPEC_ST_RANGE;
             return -1;
         }
-        return slot;
+        return (int32_t)slot;
     };
 
     // ---- register staging: two tiles in flight, in two statically named sets
     uint4 kreg0[KPER], kreg1[KPER];
     uint4 vreg0[VPER][4], vreg1[VPER][4];
-    auto issue = [&](uint4 (&kr)[KPER], uint4 (&vr)[VPER][4], int stage_slot) {
-        const int64_t *sl = s_slot[stage_slot];
+    auto issue = [&](uint4 (&kr)[KPER], uint4 (&vr)[VPER][4], int t) {
+        const int32_t *sl = &s_ring[(t / kChunkTiles) & 1][(t % kChunkTiles) * kTileKeys];
 #pragma unroll
         for (int i = 0; i < KPER; ++i) {
             const int u = tid + i * NT;
             kr[i] = make_uint4(0, 0, 0, 0);
             if (u < KUNITS) {
-                const int64_t slot = sl[u / (D / 8)];
+                const int32_t slot = sl[u / (D / 8)];
                 if (slot >= 0)
                     kr[i] = *reinterpret_cast<const uint4 *>(
-                        kpool + (slot * P.hkv + kvh) * D + (u % (D / 8)) * 8);
+                        kpool + ((int64_t)slot * P.hkv + kvh) * D + (u % (D / 8)) * 8);
             }
         }
 #pragma unroll
@@ -279,10 +284,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
             for (int j = 0; j < 4; ++j) {
                 vr[i][j] = make_uint4(0, 0, 0, 0);
                 if (u < VUNITS) {
-                    const int64_t slot = sl[(u % (kTileKeys / 4)) * 4 + j];
+                    const int32_t slot = sl[(u % (kTileKeys / 4)) * 4 + j];
                     if (slot >= 0)
                         vr[i][j] = *reinterpret_cast<const uint4 *>(
-                            vpool + (slot * P.hkv + kvh) * D + (u / (kTileKeys / 4)) * 8);
+                            vpool + ((int64_t)slot * P.hkv + kvh) * D + (u / (kTileKeys / 4)) * 8);
                 }
             }
         }
@@ -304,7 +309,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
             if (u < VUNITS) {
                 const int kq = u % (kTileKeys / 4), d8 = u / (kTileKeys / 4);
                 // vr[i][j] holds dims d8*8 .. +7 of key kq*4+j; write, per dim,
-                // its 4 keys as one 8-byte run of V^T
+                // its 4 keys as one 8-byte run of V^T.  Within each run of 4
+                // groups of 4 keys the middle two swap places, so the 8 keys
+                // one lane feeds an MFMA k-step (groups g and g+2) sit together.
+                const int kp = (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
 #pragma unroll
                 for (int pr = 0; pr < 4; ++pr) {
                     const uint32_t a = word(vr[i][0], pr), bb = word(vr[i][1], pr);
@@ -315,44 +323,50 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
                     hi.x = __builtin_amdgcn_perm(bb, a, 0x07060302u);
                     hi.y = __builtin_amdgcn_perm(d, c, 0x07060302u);
                     const int dim = d8 * 8 + 2 * pr;
-                    *reinterpret_cast<uint2 *>(&vt_lds[stage][dim * VS + kq * 4]) = lo;
-                    *reinterpret_cast<uint2 *>(&vt_lds[stage][(dim + 1) * VS + kq * 4]) = hi;
+                    *reinterpret_cast<uint2 *>(&vt_lds[stage][dim * VS + kp * 4]) = lo;
+                    *reinterpret_cast<uint2 *>(&vt_lds[stage][(dim + 1) * VS + kp * 4]) = hi;
                 }
             }
         }
     };
 
-    // ---- prologue: tiles 0 and 1 loading, tile 0 in LDS, slots of tiles 2
-    // and 3 in the slot stages, tile 2 loading --------------------------------
-    __syncthreads();                       // s_pre, s_tree
-    if (tid < kTileKeys) {
-        s_slot[0][tid] = lookup(kb + tid);
-        s_slot[1][tid] = lookup(kb + kTileKeys + tid);
+    // ---- prologue: slots of chunks 0 and 1 into the ring, tile 0 in LDS,
+    // tiles 1 and 2 loading ---------------------------------------------------
+    __syncthreads();                       // s_tree
+#pragma unroll
+    for (int j = 0; j < 2 * KPT; ++j) {
+        const int e = tid + j * NT;
+        s_ring[e / kChunkKeys][e % kChunkKeys] = slot_of(kb + e, pg[j]);
     }
     __syncthreads();
     issue(kreg0, vreg0, 0);
     if (ntiles > 1) issue(kreg1, vreg1, 1);
-    int64_t pending = -1;
-    if (tid < kTileKeys) pending = lookup(kb + 2 * kTileKeys + tid);
-    __syncthreads();
-    if (tid < kTileKeys) {
-        s_slot[0][tid] = pending;                                  // tile 2
-        pending = lookup(kb + 3 * kTileKeys + tid);
-    }
     stash(kreg0, vreg0, 0);
     __syncthreads();
-    if (ntiles > 2) issue(kreg0, vreg0, 0);                        // tile 2
-    if (tid < kTileKeys) s_slot[1][tid] = pending;                 // tile 3
-    __syncthreads();
+    if (ntiles > 2) issue(kreg0, vreg0, 2);
 
-    // one pipeline step; tile it+1 and it+3 live in the register set (kr, vr)
+    // one pipeline step; tile it+1 and then tile it+LEAD live in the register
+    // set (kr, vr).  Chunk c's ring half is last read when tile 8c+7 is issued
+    // (step 8c+7-LEAD); chunk c+2's page entries are loaded in the next step
+    // and turned into slots at the end of step 8c+15-LEAD, one step before
+    // tile 8c+16 is issued.
+    int cpg[KPT];
     auto step = [&](int it, uint4 (&kr)[KPER], uint4 (&vr)[VPER][4]) {
         const int tile_base = kb + it * kTileKeys;
         // write tile it+1 (registers -> LDS stage (it+1)&1), then reuse its
-        // registers for tile it+3, whose slots sit in s_slot[(it+3)&1]
+        // registers for tile it+LEAD
         if (it + 1 < ntiles) stash(kr, vr, (it + 1) & 1);
-        if (it + 3 < ntiles) issue(kr, vr, (it + 3) & 1);
-        if (tid < kTileKeys) pending = lookup(tile_base + 4 * kTileKeys + tid);   // tile it+4
+        if (it + LEAD < ntiles) issue(kr, vr, it + LEAD);
+        if (it % kChunkTiles == kChunkTiles - LEAD) {
+            const int cbase = kb + ((it + kChunkTiles + LEAD) / kChunkTiles) * kChunkKeys;
+            if (cbase < ke) {
+#pragma unroll
+                for (int j = 0; j < KPT; ++j) {
+                    const int p = cbase + tid + j * NT;
+                    cpg[j] = p < L ? P.page_table[(int64_t)b * P.max_pages + p / P.page_size] : -1;
+                }
+            }
+        }
 
         if (wave_active) {
             const __bf16 *kt = k_lds[it & 1];
@@ -400,33 +414,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
                 }
                 const float mneg = (m_run == -INFINITY) ? 0.f : -m_run;
                 float lsum = 0.f;
-                bf16x8 pf0, pf1;
+                bf16x8 pf[2];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[i], C, mneg));
                     const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[8 + i], C, mneg));
                     lsum += e0 + e1;
-                    pf0[i] = static_cast<__bf16>(e0);
-                    pf1[i] = static_cast<__bf16>(e1);
+                    pf[0][i] = static_cast<__bf16>(e0);
+                    pf[1][i] = static_cast<__bf16>(e1);
                 }
                 l_run += lsum;
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
-                        const __bf16 *vp = &vt[(dt * 32 + col) * VS + sub * 32 + 16 * st + 4 * half];
-                        const uint2 x0 = *reinterpret_cast<const uint2 *>(vp);
-                        const uint2 x1 = *reinterpret_cast<const uint2 *>(vp + 8);
-                        const uint4 w = make_uint4(x0.x, x0.y, x1.x, x1.y);
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, w), st == 0 ? pf0 : pf1, oacc[dt], 0, 0, 0);
+                        // keys sub*32 + 16*st + 4*half + {0..3, 8..11}: groups
+                        // g and g+2, stored side by side
+                        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(
+                            &vt[(dt * 32 + col) * VS + sub * 32 + 16 * st + 8 * half]);
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], oacc[dt],
+                                                                           0, 0, 0);
                     }
                 }
             }
         }
-        // tile it+4's slots go to the stage tile it+2's slots left (read when
-        // tile it+2 was issued, one iteration ago)
-        if (tid < kTileKeys) s_slot[it & 1][tid] = pending;
+        if (it % kChunkTiles == kChunkTiles - 1 - LEAD && it >= 2 * kChunkTiles - 1 - LEAD) {
+            const int c = (it + LEAD + 1) / kChunkTiles;
+            const int cbase = kb + c * kChunkKeys;
+            if (cbase < ke) {
+#pragma unroll
+                for (int j = 0; j < KPT; ++j) {
+                    const int e = tid + j * NT;
+                    s_ring[c & 1][e] = slot_of(cbase + e, cpg[j]);
+                }
+            }
+        }
         __syncthreads();
     };
     for (int it = 0; it < ntiles; it += 2) {
@@ -446,13 +468,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int j4 = 0; j4 < 4; ++j4) {
-                    uint32_t h[4];
+                    uint32_t hv[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        h[j] = __builtin_bit_cast(uint16_t,
-                                                  static_cast<__bf16>(oacc[dt][4 * j4 + j] * inv));
+                        hv[j] = __builtin_bit_cast(uint16_t,
+                                                   static_cast<__bf16>(oacc[dt][4 * j4 + j] * inv));
                     *reinterpret_cast<uint2 *>(op + dt * 32 + 8 * j4 + 4 * half) =
-                        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                        make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
                 }
         } else {
             const int64_t pidx = (((int64_t)b * P.hkv + kvh) * P.nsplit + split) * P.rows + rho;
@@ -707,7 +729,7 @@ extern "C" int spec_verify_attention(int batch, int n, int hq, int hkv, int d, i
         max_seq_len < 0 || num_slots < 0)
         return SPEC_ERR_SHAPE;
     if (hq % hkv != 0) return SPEC_ERR_SHAPE;
-    if (n > 64 || (d != 64 && d != 128)) return SPEC_ERR_UNSUPPORTED;
+    if (n > 64 || (d != 64 && d != 128) || num_slots > INT32_MAX) return SPEC_ERR_UNSUPPORTED;
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
     if ((int64_t)max_pages * page_size < (int64_t)max_seq_len && max_seq_len > 0) return SPEC_ERR_SHAPE;
     if (batch == 0) return SPEC_OK;

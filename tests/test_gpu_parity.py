@@ -235,6 +235,10 @@ SPLIT_CASES = {
     "L4032_4tile": W.shrink(W.CONFIGS[2], hist=("fixed", 4032), vocab=1000),
     "L2048": W.shrink(W.CONFIGS[2], hist=("fixed", 2048), vocab=1000),
     "b4_Lu": W.shrink(W.CONFIGS[3], batch=4, hist=("uniform", 1000, 3000), vocab=1000),
+    # 560 query rows per KV head (n=35, 16 query heads per KV head): waves of
+    # 64 rows, the last wave's second 32-row block cut at row 560
+    "g16_n35_Lu": W.shrink(W.CONFIGS[5], batch=2, hist=("uniform", 300, 2500), vocab=1000,
+                           num_draft_tokens=35, num_kv_heads=4),
 }
 
 
@@ -254,6 +258,38 @@ def test_verify_attention_split_remainders(name):
     err = _attn_err(got, ref.reshape(got.shape))
     say(f"    max rel err {err:.3e} over all {got.shape[0] * got.shape[1]} vectors")
     assert err <= ATTN_TOL[cfg.dtype]
+
+
+# Splits longer than the two 8-tile chunks of the slot ring the prologue
+# fills, so chunks are refilled inside the loop, for waves of 64 rows (512
+# rows per KV head) and of 32 rows: sampled vectors against the oracle.
+LONG_SPLIT_CASES = {
+    "rows512_L8700": W.shrink(W.CONFIGS[5], batch=4, hist=("fixed", 8700), vocab=1000),
+    "rows128_Lu": W.shrink(W.CONFIGS[3], batch=12, hist=("uniform", 4000, 9000), vocab=1000),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_SPLIT_CASES))
+def test_verify_attention_long_splits_sampled(name):
+    cfg = LONG_SPLIT_CASES[name]
+    w = W.make_workload(cfg, 23)
+    t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                          cfg.num_steps, cfg.num_draft_tokens)
+    b, n = cfg.batch, cfg.num_draft_tokens
+    say(f"[attention long splits] {name} b={b} L={w.seq_lens.tolist()}")
+    words = oracle.pack_mask(t["mask"], oracle.MASK_QLEN_BITS)
+    got, st = G.verify_attention(w, words)
+    assert st == 0
+    rng = np.random.default_rng(5)
+    rows = [(int(rng.integers(0, b * n)), int(rng.integers(0, cfg.num_q_heads))) for _ in range(48)]
+    rows += [(b * n - 1, cfg.num_q_heads - 1), (0, 0), (n - 1, 0), (b * n - n, cfg.num_q_heads - 1)]
+    ref = oracle.verify_attention(w.q, w.k_pool[0], w.v_pool[0], w.page_table, w.seq_lens,
+                                  w.out_cache_loc, t["mask"], cfg.num_q_heads, cfg.num_kv_heads,
+                                  cfg.page_size, cfg.dtype, rows=rows)
+    err = _attn_err(np.stack([got[r, h] for r, h in rows]), ref)
+    say(f"    max rel err {err:.3e} over {len(rows)} sampled vectors")
+    assert err <= ATTN_TOL[cfg.dtype]
+    assert np.isfinite(got).all()
 
 
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
