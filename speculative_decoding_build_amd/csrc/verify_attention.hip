@@ -24,11 +24,13 @@
 //     loads in flight during the current tile's math.
 //   * f32: the same splits on the vector ALUs (one wavefront per query row,
 //     lanes across head_dim).
-//   * splits > 1: each writes (max, sum, unnormalised O) partials in fp32; a
-//     merge kernel combines them by log-sum-exp.  One split writes O directly.
+//   * splits > 1: each writes its (max, sum) in fp32 and its O partial (bf16
+//     O / sum, or unnormalised f32 O on the f32 path); a merge kernel
+//     combines them by log-sum-exp.  One split writes O directly.
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "spec_common.h"
 
@@ -45,11 +47,14 @@ constexpr int kChunkTiles = 8;          // tiles per chunk of the slot ring
 constexpr int kChunkKeys = kChunkTiles * kTileKeys;
 constexpr int kMaxTreeNodes = 64;
 constexpr int kSmallGrid = 512;         // fewer 8-wave workgroups than this: use 4-wave ones
+constexpr int kPlanBatch = 1024;        // most requests a length-balanced plan covers
 
 struct AttnParams {
     int batch, n, hq, hkv, group, rows;   // rows = n * group
     int page_size, max_pages, max_seq_len;
     int split_len, nsplit, rowgroups, rows_per_group;
+    int dyn;                               // 1: splits follow the actual lengths (see plan_split)
+    int slots;                             // split slots per (KV head, row group) when dyn
     int word_bytes;
     float scale_log2;                      // sm_scale * log2(e)
     int64_t num_slots;
@@ -61,8 +66,14 @@ struct AttnParams {
     const int32_t *out_cache_loc;
     const uint8_t *mask;
     void *out;
-    float *part_o;                         // [b][hkv][nsplit][rows][D]
-    float2 *part_ml;                       // [b][hkv][nsplit][rows] (max log2, sum)
+    // partials of split slot j: O [j][hkv][rows][D] and (max log2, sum)
+    // [j][hkv][rows].  O is bf16 and already divided by the split's sum on
+    // the bf16 path, unnormalised f32 on the f32 path.  Static plan: request
+    // b's splits are slots b*nsplit + s; length-balanced plan: slots
+    // plan[b].x .. plan[b].x + plan[b].y - 1.
+    void *part_o;
+    float2 *part_ml;
+    int2 *plan;                            // [batch] (first slot, splits), dyn only
     int32_t *status;
 };
 
@@ -97,10 +108,10 @@ __device__ __forceinline__ int64_t key_slot(const AttnParams &P, int b, int L, i
 // take every split's partial without reading the sequence length.
 __device__ __forceinline__ void mark_empty_split(const AttnParams &P, int b, int kvh, int split,
                                                  int rg) {
-    if (P.nsplit == 1) return;
+    if (P.nsplit == 1 || P.dyn) return;
     const int r0 = rg * P.rows_per_group;
     const int r1 = min(P.rows, r0 + P.rows_per_group);
-    const int64_t base = (((int64_t)b * P.hkv + kvh) * P.nsplit + split) * P.rows;
+    const int64_t base = (((int64_t)b * P.nsplit + split) * P.hkv + kvh) * P.rows;
     for (int rho = r0 + (int)threadIdx.x; rho < r1; rho += blockDim.x)
         P.part_ml[base + rho] = make_float2(-INFINITY, 0.f);
 }
@@ -129,6 +140,80 @@ __device__ __forceinline__ Work decode_work(const AttnParams &P, int w, bool xcd
     k.kvh = j % P.hkv;
     k.b = j / P.hkv;
     return k;
+}
+
+// Length-balanced plan (batch > 1): request b has t_b = ceil((L_b + n) / 64)
+// tiles (L_b read as 0 when out of range) and gets
+//     s_b = max(1, min(t_b / kMinTiles, kMaxSplits, 1 + (S - batch) t_b / T))
+// of the S split slots, T = sum of t_b, so sum s_b <= S and long requests get
+// proportionally more splits; split k covers tiles [k t_b / s_b, (k+1) t_b / s_b).
+// Slots are handed out in request order.  Wave 0 of every workgroup
+// evaluates it from the sequence lengths (a deterministic computation,
+// identical in every workgroup) and finds the request and
+// split of its slot j; workgroup 0 also stores (first slot, s_b) per request
+// for the merge.  Returns in out[0..3] (b, k, s_b, t_b), b = -1 when slot j
+// is unused.
+constexpr int kMaxSplits = 64;
+
+__device__ void plan_split(const AttnParams &P, int j, bool store, int *out) {
+    constexpr int E = kPlanBatch / 64;
+    const int lane = threadIdx.x & 63;
+    int tb[E];
+    long long tsum = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int r = lane * E + e;
+        tb[e] = 0;
+        if (r < P.batch) {
+            int L = P.seq_lens[r];
+            if (L < 0 || L > P.max_seq_len) L = 0;
+            tb[e] = (L + P.n + kTileKeys - 1) / kTileKeys;
+        }
+        tsum += tb[e];
+    }
+    for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
+    // exact floor((S - batch) t_b / T): a double estimate (off by at most
+    // one) corrected with integer products
+    const long long spare = (long long)P.slots - P.batch;
+    const double rden = 1.0 / (double)tsum;
+    int sb[E];
+    int lsum = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        sb[e] = 0;
+        if (tb[e] > 0) {
+            const long long num = spare * tb[e];
+            long long q = (long long)((double)num * rden);
+            if (q * tsum > num) --q;
+            if ((q + 1) * tsum <= num) ++q;
+            const int v = 1 + (int)q;
+            sb[e] = max(1, min(v, min(tb[e] / kMinTiles, kMaxSplits)));
+        }
+        lsum += sb[e];
+    }
+    // exclusive scan of the lanes' split counts
+    int incl = lsum;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    const int total = __shfl(incl, 63, 64);
+    int off = incl - lsum;
+    if (lane == 0 && j >= total) out[0] = -1;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int r = lane * E + e;
+        if (r < P.batch) {
+            if (j >= off && j < off + sb[e]) {
+                out[0] = r;
+                out[1] = j - off;
+                out[2] = sb[e];
+                out[3] = tb[e];
+            }
+            if (store) P.plan[r] = make_int2(off, sb[e]);
+        }
+        off += sb[e];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -180,9 +265,38 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
     const int half = lane >> 5;
     const int col = lane & 31;
 
-    const Work wk = decode_work(P, blockIdx.x, xcd_remap != 0);
-    const int b = wk.b, kvh = wk.kvh, split = wk.split, rg = wk.rg;
-    const int kb = split * P.split_len;
+    int b, kvh, split, rg, nsp, kb, span;
+    int64_t slot_j;                        // split slot of the partials
+    if (P.dyn) {
+        // length-balanced plan: this workgroup is split slot j of (KV head,
+        // row group); rows groups of one slot are neighbours as below
+        const int total = P.slots * P.rowgroups * P.hkv;
+        int w = blockIdx.x;
+        if (xcd_remap) w = (w % 8) * (total / 8) + w / 8;
+        rg = w % P.rowgroups;
+        w /= P.rowgroups;
+        const int j = w % P.slots;
+        kvh = w / P.slots;
+        __shared__ int s_plan[4];
+        if (wave == 0) plan_split(P, j, blockIdx.x == 0, s_plan);
+        __syncthreads();
+        b = s_plan[0];
+        if (b < 0) return;                 // unused slot: no keys, no partials
+        split = s_plan[1];
+        nsp = s_plan[2];
+        const int t = s_plan[3];
+        const int tlo = (int)((int64_t)split * t / nsp), thi = (int)((int64_t)(split + 1) * t / nsp);
+        kb = tlo * kTileKeys;
+        span = (thi - tlo) * kTileKeys;
+        slot_j = j;
+    } else {
+        const Work wk = decode_work(P, blockIdx.x, xcd_remap != 0);
+        b = wk.b; kvh = wk.kvh; split = wk.split; rg = wk.rg;
+        nsp = P.nsplit;
+        kb = split * P.split_len;
+        span = P.split_len;
+        slot_j = (int64_t)b * P.nsplit + split;
+    }
     // Loads that do not depend on the sequence length go out with it: the
     // page-table entries of the split's first two slot chunks and the
     // request's tree slots.
@@ -204,7 +318,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
         mark_empty_split(P, b, kvh, split, rg);
         return;
     }
-    const int ke = min(L + P.n, kb + P.split_len);
+    const int ke = min(L + P.n, kb + span);
     if (kb >= ke) {
         mark_empty_split(P, b, kvh, split, rg);
         return;
@@ -461,33 +575,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
     if (rho < P.rows) {
         const int node = rho / P.group;
         const int h = kvh * P.group + rho % P.group;
-        if (P.nsplit == 1) {
-            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            __bf16 *op = static_cast<__bf16 *>(P.out) + (((int64_t)b * P.n + node) * P.hq + h) * D;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    uint32_t hv[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        hv[j] = __builtin_bit_cast(uint16_t,
-                                                   static_cast<__bf16>(oacc[dt][4 * j4 + j] * inv));
-                    *reinterpret_cast<uint2 *>(op + dt * 32 + 8 * j4 + 4 * half) =
-                        make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
-                }
+        // O / sum in bf16: the output itself for a request with one split,
+        // else this split's partial (the merge weights it by its sum)
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        __bf16 *op;
+        if (nsp == 1) {
+            op = static_cast<__bf16 *>(P.out) + (((int64_t)b * P.n + node) * P.hq + h) * D;
         } else {
-            const int64_t pidx = (((int64_t)b * P.hkv + kvh) * P.nsplit + split) * P.rows + rho;
-            float *po = P.part_o + pidx * D;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4)
-                    *reinterpret_cast<float4 *>(po + dt * 32 + 8 * j4 + 4 * half) =
-                        make_float4(oacc[dt][4 * j4 + 0], oacc[dt][4 * j4 + 1],
-                                    oacc[dt][4 * j4 + 2], oacc[dt][4 * j4 + 3]);
+            const int64_t pidx = (slot_j * P.hkv + kvh) * P.rows + rho;
+            op = static_cast<__bf16 *>(P.part_o) + pidx * D;
             if (half == 0) P.part_ml[pidx] = make_float2(m_run, l_tot);
         }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                uint32_t hv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    hv[j] = __builtin_bit_cast(uint16_t,
+                                               static_cast<__bf16>(oacc[dt][4 * j4 + j] * inv));
+                *reinterpret_cast<uint2 *>(op + dt * 32 + 8 * j4 + 4 * half) =
+                    make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+            }
     }
     for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, 64);
     if (lane == 0) spec::raise_status(P.status, err);
@@ -558,9 +668,9 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(AttnParams P) {
 #pragma unroll
             for (int j = 0; j < PER; ++j) op[lane + 64 * j] = o[j] * inv;
         } else {
-            const int64_t pidx = (((int64_t)b * P.hkv + kvh) * P.nsplit + split) * P.rows + rho;
+            const int64_t pidx = (((int64_t)b * P.nsplit + split) * P.hkv + kvh) * P.rows + rho;
 #pragma unroll
-            for (int j = 0; j < PER; ++j) P.part_o[pidx * D + lane + 64 * j] = o[j];
+            for (int j = 0; j < PER; ++j) static_cast<float *>(P.part_o)[pidx * D + lane + 64 * j] = o[j];
             if (lane == 0) P.part_ml[pidx] = make_float2(m, l);
         }
     }
@@ -572,12 +682,9 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(AttnParams P) {
 // merge of split partials: one wavefront per (row, head) output vector
 // ---------------------------------------------------------------------------
 //
-// Lane s reads split s's (max, sum) (at most 64 splits), the weights
-// exp2(m_s - M) go to every lane by readlane, and the unnormalised outputs
-// are accumulated 8 splits at a time with all 8 loads in flight.  Lanes own
-// D/64 consecutive dims.
-
-constexpr int kMaxSplits = 64;
+// Lane s reads split s's (max, sum) (at most 64 splits), the weights go to
+// every lane by readlane, and the partial outputs are accumulated 16 splits
+// at a time with all 16 loads in flight.  Lanes own D/64 consecutive dims.
 
 template <int D, int DTYPE>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
@@ -596,23 +703,39 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
     // partials' loads go out with these (one round, no sequence length);
     // an empty split's O is never read into the sum (weight 0, and its
     // memory was not written)
-    const int ns = P.nsplit;
-    const int64_t base = ((int64_t)b * P.hkv + kvh) * ns;
-    const float2 ml = lane < ns ? P.part_ml[(base + lane) * P.rows + rho] : make_float2(-INFINITY, 0.f);
-    const float *po = P.part_o + (base * P.rows + rho) * D + lane * PER;
-    const int64_t sstride = (int64_t)P.rows * D;
+    int64_t first = (int64_t)b * P.nsplit;
+    int ns = P.nsplit;
+    if (P.dyn) {
+        const int2 pl = P.plan[b];
+        if (pl.y <= 1) return;             // one split wrote O itself
+        first = pl.x;
+        ns = pl.y;
+    }
+    const int64_t vstride = (int64_t)P.hkv * P.rows;   // between split slots
+    const int64_t base = first * vstride + (int64_t)kvh * P.rows + rho;
+    const float2 ml = lane < ns ? P.part_ml[base + lane * vstride] : make_float2(-INFINITY, 0.f);
+    // bf16 partials are O / sum (weight exp2(m - M) * sum); f32 ones are
+    // unnormalised O (weight exp2(m - M))
+    typedef typename std::conditional<DTYPE == SPEC_BF16, uint16_t, float>::type PT;
+    const PT *po = static_cast<const PT *>(P.part_o) + base * D + lane * PER;
+    const int64_t sstride = vstride * D;
+    auto value = [](PT v) -> float {
+        if constexpr (DTYPE == SPEC_BF16) return spec::bf16_to_f32(v);
+        else return v;
+    };
     constexpr int kBatch = 16;
     float x[kBatch][PER];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const int s = min(u, ns - 1);
 #pragma unroll
-        for (int j = 0; j < PER; ++j) x[u][j] = po[s * sstride + j];
+        for (int j = 0; j < PER; ++j) x[u][j] = value(po[s * sstride + j]);
     }
     const float M = spec::wave_max(ml.x);
     const float Mu = (M == -INFINITY) ? 0.f : M;
-    const float w = (lane < ns && ml.x != -INFINITY) ? exp2f(ml.x - Mu) : 0.f;
-    const float lsum = spec::wave_sum(w * ml.y);
+    const float e = (lane < ns && ml.x != -INFINITY) ? exp2f(ml.x - Mu) : 0.f;
+    const float lsum = spec::wave_sum(e * ml.y);
+    const float w = DTYPE == SPEC_BF16 ? e * ml.y : e;
     float acc[PER] = {};
     for (int s0 = 0; s0 < ns; s0 += kBatch) {
         if (s0 > 0) {
@@ -620,7 +743,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
             for (int u = 0; u < kBatch; ++u) {
                 const int s = min(s0 + u, ns - 1);
 #pragma unroll
-                for (int j = 0; j < PER; ++j) x[u][j] = po[s * sstride + j];
+                for (int j = 0; j < PER; ++j) x[u][j] = value(po[s * sstride + j]);
             }
         }
 #pragma unroll
@@ -656,7 +779,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
 struct Plan {
     int nw;               // waves per workgroup (bf16: one 32-row query tile each)
     int rows_per_group, rowgroups;
-    int split_len, nsplit;
+    int split_len, nsplit;  // static plan: every request cut at max_seq_len's splits
+    int dyn, slots;         // length-balanced plan over `slots` split slots (bf16, batch > 1)
 };
 
 Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
@@ -689,14 +813,34 @@ Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
     const int tiles_per = (tiles + ns - 1) / ns;
     pl.split_len = tiles_per * kTileKeys;
     pl.nsplit = (keys + pl.split_len - 1) / pl.split_len;
+    // Several requests: split by the actual lengths instead, so a batch of
+    // mixed lengths gives every workgroup about the same number of tiles.
+    // No more slots than requests at max_seq_len could use.
+    if (dtype == SPEC_BF16 && batch > 1 && batch <= kPlanBatch) {
+        const int per_head = hkv * pl.rowgroups;
+        int S = (kTargetGroups + per_head - 1) / per_head;
+        S = std::min(S, batch * std::max(1, std::min(tiles / kMinTiles, kMaxSplits)));
+        if (S > batch) {
+            pl.dyn = 1;
+            pl.slots = S;
+        }
+    }
     return pl;
 }
 
-size_t workspace_bytes_for(const Plan &pl, int batch, int n, int hq, int hkv, int d) {
-    if (pl.nsplit <= 1) return 0;
+// Workspace: partial O [slots][hkv][rows][D] (bf16 or f32, the dtype), then
+// (max, sum) [slots][hkv][rows], then the per-request plan (dyn only).
+size_t workspace_bytes_for(const Plan &pl, int batch, int n, int hq, int hkv, int d, int dtype,
+                           size_t *off_ml = nullptr, size_t *off_plan = nullptr) {
+    if (!pl.dyn && pl.nsplit <= 1) return 0;
     const size_t rows = (size_t)n * (hq / hkv);
-    const size_t parts = (size_t)batch * hkv * pl.nsplit * rows;
-    return spec::align_up(parts * d * sizeof(float), 256) + spec::align_up(parts * sizeof(float2), 256);
+    const size_t slots = pl.dyn ? (size_t)pl.slots : (size_t)batch * pl.nsplit;
+    const size_t parts = slots * hkv * rows;
+    const size_t o_ml = spec::align_up(parts * d * (dtype == SPEC_BF16 ? 2 : 4), 256);
+    const size_t o_plan = o_ml + spec::align_up(parts * sizeof(float2), 256);
+    if (off_ml) *off_ml = o_ml;
+    if (off_plan) *off_plan = o_plan;
+    return o_plan + (pl.dyn ? spec::align_up((size_t)batch * sizeof(int2), 256) : 0);
 }
 
 template <int D>
@@ -714,7 +858,7 @@ extern "C" size_t spec_verify_attention_workspace_size(int batch, int n, int hq,
                                                        int max_seq_len, int dtype) {
     if (batch <= 0 || n <= 0 || hq <= 0 || hkv <= 0 || hq % hkv || max_seq_len < 0) return 0;
     const Plan pl = make_plan(batch, n, hq, hkv, max_seq_len, dtype);
-    return workspace_bytes_for(pl, batch, n, hq, hkv, d);
+    return workspace_bytes_for(pl, batch, n, hq, hkv, d, dtype);
 }
 
 extern "C" int spec_verify_attention(int batch, int n, int hq, int hkv, int d, int page_size,
@@ -742,7 +886,8 @@ extern "C" int spec_verify_attention(int batch, int n, int hq, int hkv, int d, i
     if (align_bad || reinterpret_cast<uintptr_t>(tree_mask) % wb) return SPEC_ERR_SHAPE;
 
     const Plan pl = make_plan(batch, n, hq, hkv, max_seq_len, dtype);
-    const size_t need = workspace_bytes_for(pl, batch, n, hq, hkv, d);
+    size_t off_ml = 0, off_plan = 0;
+    const size_t need = workspace_bytes_for(pl, batch, n, hq, hkv, d, dtype, &off_ml, &off_plan);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SPEC_ERR_WORKSPACE;
 
     AttnParams P{};
@@ -750,6 +895,7 @@ extern "C" int spec_verify_attention(int batch, int n, int hq, int hkv, int d, i
     P.page_size = page_size; P.max_pages = max_pages; P.max_seq_len = max_seq_len;
     P.split_len = pl.split_len; P.nsplit = pl.nsplit; P.rowgroups = pl.rowgroups;
     P.rows_per_group = pl.rows_per_group; P.word_bytes = wb;
+    P.dyn = pl.dyn; P.slots = pl.slots;
     const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)d);
     P.scale_log2 = scale * kLog2e;
     P.num_slots = num_slots;
@@ -757,16 +903,15 @@ extern "C" int spec_verify_attention(int batch, int n, int hq, int hkv, int d, i
     P.seq_lens = seq_lens; P.out_cache_loc = out_cache_loc;
     P.mask = static_cast<const uint8_t *>(tree_mask); P.out = out;
     if (need > 0) {
-        const size_t rows = (size_t)P.rows;
-        const size_t parts = (size_t)batch * hkv * pl.nsplit * rows;
-        P.part_o = static_cast<float *>(workspace);
-        P.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(workspace) +
-                                               spec::align_up(parts * d * sizeof(float), 256));
+        P.part_o = workspace;
+        P.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + off_ml);
+        if (pl.dyn) P.plan = reinterpret_cast<int2 *>(static_cast<char *>(workspace) + off_plan);
     }
     P.status = dev_status;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const unsigned groups = (unsigned)(pl.nsplit * pl.rowgroups * hkv * batch);
+    const unsigned groups = pl.dyn ? (unsigned)(pl.slots * pl.rowgroups * hkv)
+                                   : (unsigned)(pl.nsplit * pl.rowgroups * hkv * batch);
     if (dtype == SPEC_BF16) {
         if (d == 128) launch_mfma<128>(pl, P, groups, st);
         else launch_mfma<64>(pl, P, groups, st);
@@ -774,7 +919,7 @@ extern "C" int spec_verify_attention(int batch, int n, int hq, int hkv, int d, i
         if (d == 128) hipLaunchKernelGGL(attn_split_f32_kernel<128>, dim3(groups), dim3(256), 0, st, P);
         else hipLaunchKernelGGL(attn_split_f32_kernel<64>, dim3(groups), dim3(256), 0, st, P);
     }
-    if (pl.nsplit > 1) {
+    if (pl.dyn || pl.nsplit > 1) {
         const int64_t nvec = (int64_t)batch * n * hq;
         const dim3 mgrid((unsigned)((nvec + 3) / 4));
         if (dtype == SPEC_BF16) {
