@@ -48,6 +48,7 @@ constexpr int kChunkKeys = kChunkTiles * kTileKeys;
 constexpr int kMaxTreeNodes = 64;
 constexpr int kSmallGrid = 512;         // fewer 8-wave workgroups than this: use 4-wave ones
 constexpr int kPlanBatch = 1024;        // most requests a length-balanced plan covers
+constexpr int kMergeVec = 1;            // output vectors per merge wave (bf16)
 
 struct AttnParams {
     int batch, n, hq, hkv, group, rows;   // rows = n * group
@@ -149,71 +150,70 @@ __device__ __forceinline__ Work decode_work(const AttnParams &P, int w, bool xcd
 // proportionally more splits; split k covers tiles [k t_b / s_b, (k+1) t_b / s_b).
 // Slots are handed out in request order.  Wave 0 of every workgroup
 // evaluates it from the sequence lengths (a deterministic computation,
-// identical in every workgroup) and finds the request and
-// split of its slot j; workgroup 0 also stores (first slot, s_b) per request
-// for the merge.  Returns in out[0..3] (b, k, s_b, t_b), b = -1 when slot j
-// is unused.
+// identical in every workgroup; lane l holds requests l, 64 + l, ...) and
+// finds the request and split of its slot j; workgroup 0 also stores
+// (first slot, s_b) per request for the merge.  Returns in out[0..3]
+// (b, k, s_b, t_b), b = -1 when slot j is unused.
 constexpr int kMaxSplits = 64;
 
 __device__ void plan_split(const AttnParams &P, int j, bool store, int *out) {
     constexpr int E = kPlanBatch / 64;
     const int lane = threadIdx.x & 63;
+    const int ne = (P.batch + 63) / 64;    // entries in use; request e*64 + lane
     int tb[E];
     long long tsum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const int r = lane * E + e;
         tb[e] = 0;
-        if (r < P.batch) {
-            int L = P.seq_lens[r];
-            if (L < 0 || L > P.max_seq_len) L = 0;
-            tb[e] = (L + P.n + kTileKeys - 1) / kTileKeys;
+        if (e < ne) {
+            const int r = e * 64 + lane;
+            if (r < P.batch) {
+                int L = P.seq_lens[r];
+                if (L < 0 || L > P.max_seq_len) L = 0;
+                tb[e] = (L + P.n + kTileKeys - 1) / kTileKeys;
+            }
+            tsum += tb[e];
         }
-        tsum += tb[e];
     }
     for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
     // exact floor((S - batch) t_b / T): a double estimate (off by at most
     // one) corrected with integer products
     const long long spare = (long long)P.slots - P.batch;
     const double rden = 1.0 / (double)tsum;
-    int sb[E];
-    int lsum = 0;
+    int off = 0;                           // slots of all requests before entry e
+    bool found = false;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        sb[e] = 0;
+        if (e >= ne) continue;
+        const int r = e * 64 + lane;
+        int sb = 0;
         if (tb[e] > 0) {
             const long long num = spare * tb[e];
             long long q = (long long)((double)num * rden);
             if (q * tsum > num) --q;
             if ((q + 1) * tsum <= num) ++q;
-            const int v = 1 + (int)q;
-            sb[e] = max(1, min(v, min(tb[e] / kMinTiles, kMaxSplits)));
+            sb = max(1, min(1 + (int)q, min(tb[e] / kMinTiles, kMaxSplits)));
         }
-        lsum += sb[e];
-    }
-    // exclusive scan of the lanes' split counts
-    int incl = lsum;
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-    }
-    const int total = __shfl(incl, 63, 64);
-    int off = incl - lsum;
-    if (lane == 0 && j >= total) out[0] = -1;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int r = lane * E + e;
+        // slots of the lanes before this one, then of the whole entry
+        int incl = sb;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        const int first = off + incl - sb;
         if (r < P.batch) {
-            if (j >= off && j < off + sb[e]) {
+            if (j >= first && j < first + sb) {
                 out[0] = r;
-                out[1] = j - off;
-                out[2] = sb[e];
+                out[1] = j - first;
+                out[2] = sb;
                 out[3] = tb[e];
+                found = true;
             }
-            if (store) P.plan[r] = make_int2(off, sb[e]);
+            if (store) P.plan[r] = make_int2(first, sb);
         }
-        off += sb[e];
+        off += __shfl(incl, 63, 64);
     }
+    if (__ballot(found) == 0 && lane == 0) out[0] = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -682,93 +682,122 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(AttnParams P) {
 // merge of split partials: one wavefront per (row, head) output vector
 // ---------------------------------------------------------------------------
 //
-// Lane s reads split s's (max, sum) (at most 64 splits), the weights go to
-// every lane by readlane, and the partial outputs are accumulated 16 splits
-// at a time with all 16 loads in flight.  Lanes own D/64 consecutive dims.
+// A wave merges VPW output vectors (consecutive (row, head) indices), so the
+// loads of all of them go out together: first their plan entries, then every
+// split's (max, sum) and partial.  Lane s holds split s's (max, sum) (at most
+// 64 splits); the weights go to every lane by readlane and the partials are
+// accumulated 16 splits at a time.  Lanes own D/64 consecutive dims.
 
-template <int D, int DTYPE>
+template <int D, int DTYPE, int VPW>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
     constexpr int PER = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t vec = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b*n + node)*hq + h
-    const int64_t nvec = (int64_t)P.batch * P.n * P.hq;
-    if (vec >= nvec) return;
-    const int h = vec % P.hq;
-    const int64_t row = vec / P.hq;
-    const int node = row % P.n;
-    const int b = row / P.n;
-    const int kvh = h / P.group;
-    const int rho = node * P.group + h % P.group;
-    // every split wrote its (max, sum), empty ones (-inf, 0), so the
-    // partials' loads go out with these (one round, no sequence length);
-    // an empty split's O is never read into the sum (weight 0, and its
-    // memory was not written)
-    int64_t first = (int64_t)b * P.nsplit;
-    int ns = P.nsplit;
-    if (P.dyn) {
-        const int2 pl = P.plan[b];
-        if (pl.y <= 1) return;             // one split wrote O itself
-        first = pl.x;
-        ns = pl.y;
-    }
-    const int64_t vstride = (int64_t)P.hkv * P.rows;   // between split slots
-    const int64_t base = first * vstride + (int64_t)kvh * P.rows + rho;
-    const float2 ml = lane < ns ? P.part_ml[base + lane * vstride] : make_float2(-INFINITY, 0.f);
-    // bf16 partials are O / sum (weight exp2(m - M) * sum); f32 ones are
-    // unnormalised O (weight exp2(m - M))
-    typedef typename std::conditional<DTYPE == SPEC_BF16, uint16_t, float>::type PT;
-    const PT *po = static_cast<const PT *>(P.part_o) + base * D + lane * PER;
-    const int64_t sstride = vstride * D;
-    auto value = [](PT v) -> float {
-        if constexpr (DTYPE == SPEC_BF16) return spec::bf16_to_f32(v);
-        else return v;
-    };
     constexpr int kBatch = 16;
-    float x[kBatch][PER];
+    // bf16 partials are O / sum (weight exp2(m - M) * sum), kept packed as
+    // loaded (PER values in one word) until used; f32 ones are unnormalised
+    // O (weight exp2(m - M))
+    constexpr bool kBf = DTYPE == SPEC_BF16;
+    typedef typename std::conditional<kBf, typename std::conditional<PER == 2, uint32_t, uint16_t>::type,
+                                      float>::type WT;      // one lane's word of a partial
+    constexpr int NW_ = kBf ? 1 : PER;                      // words per lane and split
+    auto val = [](const WT (&w)[NW_], int j) -> float {
+        if constexpr (kBf) return spec::bf16_to_f32((uint16_t)(w[0] >> (16 * j)));
+        else return w[j];
+    };
+    const int lane = threadIdx.x & 63;
+    const int64_t vec0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW;
+    const int64_t nvec = (int64_t)P.batch * P.n * P.hq;
+    const int64_t vstride = (int64_t)P.hkv * P.rows;   // between split slots
+    const int64_t sstride = vstride * D / (kBf ? PER : 1);   // in words
+
+    int64_t base[VPW];
+    int ns[VPW];
+    // (1) plan entries
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int s = min(u, ns - 1);
-#pragma unroll
-        for (int j = 0; j < PER; ++j) x[u][j] = value(po[s * sstride + j]);
-    }
-    const float M = spec::wave_max(ml.x);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    const float e = (lane < ns && ml.x != -INFINITY) ? exp2f(ml.x - Mu) : 0.f;
-    const float lsum = spec::wave_sum(e * ml.y);
-    const float w = DTYPE == SPEC_BF16 ? e * ml.y : e;
-    float acc[PER] = {};
-    for (int s0 = 0; s0 < ns; s0 += kBatch) {
-        if (s0 > 0) {
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int s = min(s0 + u, ns - 1);
-#pragma unroll
-                for (int j = 0; j < PER; ++j) x[u][j] = value(po[s * sstride + j]);
-            }
+    for (int i = 0; i < VPW; ++i) {
+        const int64_t vec = vec0 + i;
+        ns[i] = 0;
+        base[i] = 0;
+        if (vec >= nvec) continue;
+        const int h = vec % P.hq;
+        const int64_t row = vec / P.hq;
+        const int node = row % P.n;
+        const int b = row / P.n;
+        int64_t first = (int64_t)b * P.nsplit;
+        int cnt = P.nsplit;
+        if (P.dyn) {
+            const int2 pl = P.plan[b];
+            first = pl.x;
+            cnt = pl.y > 1 ? pl.y : 0;     // one split wrote O itself
         }
+        ns[i] = cnt;
+        base[i] = first * vstride + (int64_t)(h / P.group) * P.rows + node * P.group + h % P.group;
+    }
+    // (2) every split's (max, sum) and the first kBatch partials of all VPW
+    // vectors.  An empty split (static plan) wrote (-inf, 0), so its O is
+    // never read into the sum (weight 0; its memory was not written).
+    auto words = [&](int i) -> const WT * {
+        return reinterpret_cast<const WT *>(static_cast<const char *>(P.part_o) +
+                                            (base[i] * D + lane * PER) * (kBf ? 2 : 4));
+    };
+    float2 ml[VPW];
+    WT x[VPW][kBatch][NW_];
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+        ml[i] = lane < ns[i] ? P.part_ml[base[i] + lane * vstride] : make_float2(-INFINITY, 0.f);
+        const WT *po = words(i);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const float ws = s0 + u < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u)) : 0.f;
-            if (ws > 0.f) {
+            const int sidx = max(0, min(u, ns[i] - 1));
 #pragma unroll
-                for (int j = 0; j < PER; ++j) acc[j] = fmaf(ws, x[u][j], acc[j]);
-            }
+            for (int j = 0; j < NW_; ++j) x[i][u][j] = ns[i] > 0 ? po[sidx * sstride + j] : WT(0);
         }
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    if (DTYPE == SPEC_BF16) {
-        uint16_t *op = static_cast<uint16_t *>(P.out) + vec * D + lane * PER;
-        uint32_t hb[PER];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) hb[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j] * inv));
-        if (PER == 2)
-            *reinterpret_cast<uint32_t *>(op) = hb[0] | (hb[PER - 1] << 16);
-        else
-            op[0] = (uint16_t)hb[0];
-    } else {
-        float *op = static_cast<float *>(P.out) + vec * D + lane * PER;
+    for (int i = 0; i < VPW; ++i) {
+        if (ns[i] == 0) continue;
+        const WT *po = words(i);
+        const float M = spec::wave_max(ml[i].x);
+        const float Mu = (M == -INFINITY) ? 0.f : M;
+        const float ex = (lane < ns[i] && ml[i].x != -INFINITY) ? exp2f(ml[i].x - Mu) : 0.f;
+        const float lsum = spec::wave_sum(ex * ml[i].y);
+        const float w = kBf ? ex * ml[i].y : ex;
+        float acc[PER] = {};
+        for (int s0 = 0; s0 < ns[i]; s0 += kBatch) {
+            if (s0 > 0) {
 #pragma unroll
-        for (int j = 0; j < PER; ++j) op[j] = acc[j] * inv;
+                for (int u = 0; u < kBatch; ++u) {
+                    const int sidx = min(s0 + u, ns[i] - 1);
+#pragma unroll
+                    for (int j = 0; j < NW_; ++j) x[i][u][j] = po[sidx * sstride + j];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const float ws = s0 + u < ns[i]
+                    ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u)) : 0.f;
+                if (ws > 0.f) {
+#pragma unroll
+                    for (int j = 0; j < PER; ++j) acc[j] = fmaf(ws, val(x[i][u], j), acc[j]);
+                }
+            }
+        }
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        const int64_t vec = vec0 + i;
+        if (kBf) {
+            uint16_t *op = static_cast<uint16_t *>(P.out) + vec * D + lane * PER;
+            uint32_t hb[PER];
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+                hb[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j] * inv));
+            if (PER == 2)
+                *reinterpret_cast<uint32_t *>(op) = hb[0] | (hb[PER - 1] << 16);
+            else
+                op[0] = (uint16_t)hb[0];
+        } else {
+            float *op = static_cast<float *>(P.out) + vec * D + lane * PER;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) op[j] = acc[j] * inv;
+        }
     }
 }
 
@@ -921,13 +950,16 @@ extern "C" int spec_verify_attention(int batch, int n, int hq, int hkv, int d, i
     }
     if (pl.dyn || pl.nsplit > 1) {
         const int64_t nvec = (int64_t)batch * n * hq;
-        const dim3 mgrid((unsigned)((nvec + 3) / 4));
         if (dtype == SPEC_BF16) {
-            if (d == 128) hipLaunchKernelGGL((attn_merge_kernel<128, SPEC_BF16>), mgrid, dim3(256), 0, st, P);
-            else hipLaunchKernelGGL((attn_merge_kernel<64, SPEC_BF16>), mgrid, dim3(256), 0, st, P);
+            const dim3 mgrid((unsigned)((nvec + 4 * kMergeVec - 1) / (4 * kMergeVec)));
+            if (d == 128)
+                hipLaunchKernelGGL((attn_merge_kernel<128, SPEC_BF16, kMergeVec>), mgrid, dim3(256), 0, st, P);
+            else
+                hipLaunchKernelGGL((attn_merge_kernel<64, SPEC_BF16, kMergeVec>), mgrid, dim3(256), 0, st, P);
         } else {
-            if (d == 128) hipLaunchKernelGGL((attn_merge_kernel<128, SPEC_F32>), mgrid, dim3(256), 0, st, P);
-            else hipLaunchKernelGGL((attn_merge_kernel<64, SPEC_F32>), mgrid, dim3(256), 0, st, P);
+            const dim3 mgrid((unsigned)((nvec + 3) / 4));
+            if (d == 128) hipLaunchKernelGGL((attn_merge_kernel<128, SPEC_F32, 1>), mgrid, dim3(256), 0, st, P);
+            else hipLaunchKernelGGL((attn_merge_kernel<64, SPEC_F32, 1>), mgrid, dim3(256), 0, st, P);
         }
     }
     return spec::launch_status();
