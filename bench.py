@@ -19,6 +19,10 @@ operation, the GPU time of that operation alone: a graph holding the
 operation for every copy, replayed between two HIP events on the stream the
 kernels run on.
 
+The target-only tree accept (the sibling-mass rule with thresholds 1, 1) is
+timed the same way as an extra operation (``extra_op_ms``); it is not part
+of the step.
+
 Prints one JSON line (rank 0).
 """
 from __future__ import annotations
@@ -84,6 +88,7 @@ class Inputs:
         self.predict, self.accept_index, self.accept_length = i32(b * n), i32(b * s1), i32(b)
         self.target_predict = i32(b * n)
         self.spredict, self.saccept_index, self.saccept_length = i32(b * n), i32(b * s1), i32(b)
+        self.tpredict, self.taccept_index, self.taccept_length = i32(b * n), i32(b * s1), i32(b)
         self.new_seq_lens, self.free_slots, self.num_free = i32(b), i32(b * n), i32(b)
         self.status = i32(1)
 
@@ -106,9 +111,10 @@ def _dev(torch, a):
     return torch.from_numpy(a).to("cuda")
 
 
-def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample):
+def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target=None):
     """The five operations of one step on input copy ``x``, as callables that
-    enqueue their kernels on the current stream."""
+    enqueue their kernels on the current stream, then (timed on its own, not
+    part of the step) the target-only accept."""
     b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
     code = S.SPEC_BF16 if cfg.dtype == "bf16" else S.SPEC_F32
 
@@ -146,12 +152,19 @@ def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample):
                           x.page_table, x.page_table.shape[1], x.seq_lens, x.out_cache_loc, ai,
                           al, x.new_seq_lens, x.free_slots, x.num_free, dev_status=x.status)
 
-    return [build, attention, greedy, sample, compact]
+    def target_only():
+        S.spec_accept_target_only(b, n, s1, cfg.vocab, code, x.tl, x.temperature, 1.0, 1.0,
+                                  x.uniforms, x.final_uniforms, x.draft_tokens, x.retrieve_index,
+                                  x.retrieve_next_token, x.retrieve_next_sibling, x.tpredict,
+                                  x.taccept_index, x.taccept_length, workspace=ws_target,
+                                  dev_status=x.status)
+
+    return [build, attention, greedy, sample, compact, target_only]
 
 
 def run_ops(S, cfg, x, ws_attn, ws_greedy, ws_sample):
     """Enqueue one step on the current stream."""
-    for f in op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample):
+    for f in op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample)[:len(OPS)]:
         f()
 
 
@@ -163,6 +176,7 @@ def cfg_max_len(cfg):
 
 
 OPS = ("build_tree", "verify_attention", "accept_greedy", "accept_sample", "compact_kv")
+EXTRA_OPS = ("accept_target_only",)     # timed alone, outside the step
 
 
 def cpu_baseline(cfg, w, tl, dl, budget_s):
@@ -267,6 +281,8 @@ def main():
                             device="cuda")
     ws_sample = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 1), dtype=torch.uint8,
                             device="cuda")
+    ws_target = torch.zeros(S.spec_accept_target_only_workspace_size(b, n, cfg.vocab),
+                            dtype=torch.uint8, device="cuda")
     S.spec_build_tree(b, cfg.topk, cfg.num_steps, n, S.SPEC_MASK_QLEN_BITS, base.scores,
                       base.tokens, base.parents, base.bonus, base.seq_lens, base.draft_tokens,
                       base.positions, base.tree_mask, base.retrieve_index,
@@ -293,8 +309,8 @@ def main():
         run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample)
     torch.cuda.synchronize()
 
-    calls = [op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample) for x in xs]
-    op_ms = {}
+    calls = [op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target) for x in xs]
+    op_ms, extra_ms = {}, {}
     if args.mode == "graph":
         # per-operation GPU times: one graph per operation holding that
         # operation at least 16 times back to back (cycling through the input
@@ -302,7 +318,7 @@ def main():
         # launch of a graph falls between the operations
         per_graph = max(16, copies)
         reps = max(2, math.ceil(64 / per_graph))
-        for j, op in enumerate(OPS):
+        for j, op in enumerate(OPS + EXTRA_OPS):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for i in range(per_graph):
@@ -315,7 +331,7 @@ def main():
                 g.replay()
             e1.record()
             torch.cuda.synchronize()
-            op_ms[op] = e0.elapsed_time(e1) / (reps * per_graph)
+            (op_ms if op in OPS else extra_ms)[op] = e0.elapsed_time(e1) / (reps * per_graph)
             del g
     else:
         # eager: events around every operation of eager steps (host launch
@@ -331,6 +347,13 @@ def main():
         torch.cuda.synchronize()
         for j, op in enumerate(OPS):
             op_ms[op] = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(k_ev):
+            calls[i % copies][len(OPS)]()
+        e1.record()
+        torch.cuda.synchronize()
+        extra_ms["accept_target_only"] = e0.elapsed_time(e1) / k_ev
 
     # eager steps (every launch from Python)
     k_e = max(5, min(args.steps, 20))
@@ -416,6 +439,8 @@ def main():
         "verify_attn_gbs": attn_gbs,
         "verify_attn_frac_hbm": attn_gbs / HBM_PEAK_GBS,
         "accept_greedy_sweep_gbs": greedy_gbs,
+        "extra_op_ms": extra_ms,
+        "accept_target_only_sweep_gbs": sweep_g / (extra_ms["accept_target_only"] * 1e-3) / 1e9,
         "mean_accept_length": float(acc_len.mean()),
         "dev_status": status,
         "roofline": {"kernel": "spec_verify_attention (split-KV MFMA + merge launches)",

@@ -236,6 +236,48 @@ int spec_accept_sample(int batch, int num_draft_tokens, int accept_width, int64_
                        size_t workspace_bytes, int32_t *dev_status, spec_stream_t stream);
 
 /*
+ * Target-only tree accept.  [P2] 四 (Target-only Tree Sampling) with the
+ * thresholds of [P1] 三条判定路径; [P5] 5.6 (same walk, other test).  No
+ * draft distribution is used.
+ *
+ *   target_logits [batch*n, vocab] dtype
+ *   temperature  [batch] f32 > 0
+ *   threshold_single, threshold_acc  host floats, threshold_acc > 0 (else
+ *       SPEC_ERR_SHAPE); 1 and 1 make the output law exactly p
+ *   uniforms     [batch, n] f32 in [0,1): uniforms[b][k] is the coin of
+ *       node k's children
+ *   final_uniforms [batch] f32 in [0,1): the terminal draw
+ * At node cur, p = softmax(target_logits[row(cur)] / T).  The children are
+ * tried in sibling order, each adding p(token) to a running mass that
+ * starts at 0; child c is accepted iff p(token) > 0 and (uniforms[b][cur] <
+ * mass / threshold_acc or p(token) >= threshold_single), and the walk
+ * continues from c with c's row and coin.  With no child accepted, or at a
+ * leaf, the terminal token is the smallest x whose cumulative R (vocabulary
+ * order) exceeds final_uniforms[b] * sum(R), R = p with the tokens of the
+ * children rejected at that node set to 0 (SPEC_ST_ZERO_RESIDUAL and x =
+ * vocab - 1 if sum(R) = 0).  Outputs as spec_accept_greedy.  Statistics are
+ * fp32 exponentials with fp64 sums; a decision closer than ~1e-6 to its
+ * threshold may differ from an exact evaluation.  Every verify row is read
+ * once (per-row softmax statistics), plus the visited children's logits and
+ * one 8192-entry chunk of the terminal row.
+ * workspace: spec_accept_target_only_workspace_size(batch, n, vocab) bytes
+ *   (16 bytes per verify row and 8192-entry chunk), 16-byte aligned and
+ *   zero-filled before its first use; every call leaves it zero-filled
+ *   again, so one workspace serves any number of calls in stream order
+ *   (concurrent calls need one each).  After a call that raised
+ *   SPEC_ST_SYNC, zero it again before the next call.
+ */
+size_t spec_accept_target_only_workspace_size(int batch, int num_draft_tokens, int64_t vocab);
+int spec_accept_target_only(int batch, int num_draft_tokens, int accept_width, int64_t vocab,
+                            int dtype, const void *target_logits, const float *temperature,
+                            float threshold_single, float threshold_acc, const float *uniforms,
+                            const float *final_uniforms, const int32_t *candidates,
+                            const int32_t *retrieve_index, const int32_t *retrieve_next_token,
+                            const int32_t *retrieve_next_sibling, int32_t *predict,
+                            int32_t *accept_index, int32_t *accept_length, void *workspace,
+                            size_t workspace_bytes, int32_t *dev_status, spec_stream_t stream);
+
+/*
  * Accepted-KV compaction.  [P1] KV 回写 (move_accept_tokens_to_target_kvcache)
  * and [P2] 六: the verify rows in accept_index (root plus accepted drafts;
  * the terminal token has no KV yet) move to the request's sequence positions

@@ -47,6 +47,7 @@ SPEC_MASK_QLEN_BITS = 2
 EXPORTS = ("spec_version", "spec_status_string", "spec_mask_word_bytes", "spec_build_tree",
            "spec_verify_attention_workspace_size", "spec_verify_attention",
            "spec_accept_workspace_size", "spec_accept_greedy", "spec_accept_sample",
+           "spec_accept_target_only_workspace_size", "spec_accept_target_only",
            "spec_compact_kv")
 
 _P = ctypes.c_void_p
@@ -76,6 +77,9 @@ _decl("spec_accept_greedy", _I, _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P
       _SZ, _P, _P)
 _decl("spec_accept_sample", _I, _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
       _P, _P, _P, _SZ, _P, _P)
+_decl("spec_accept_target_only_workspace_size", _SZ, _I, _I, _I64)
+_decl("spec_accept_target_only", _I, _I, _I, _I, _I64, _I, _P, _P, _F, _F, _P, _P, _P, _P, _P,
+      _P, _P, _P, _P, _P, _SZ, _P, _P)
 _decl("spec_compact_kv", _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I64, _P, _I, _P, _P, _P,
       _P, _P, _P, _P, _P, _P)
 
@@ -271,6 +275,44 @@ def spec_accept_sample(batch, num_draft_tokens, accept_width, vocab, dtype, targ
     ]
     _check("spec_accept_sample", _lib.spec_accept_sample(batch, n, accept_width, vocab, dtype,
                                                           *args, _stream(stream)))
+
+
+def spec_accept_target_only_workspace_size(batch, num_draft_tokens, vocab) -> int:
+    return _lib.spec_accept_target_only_workspace_size(batch, num_draft_tokens, vocab)
+
+
+def spec_accept_target_only(batch, num_draft_tokens, accept_width, vocab, dtype, target_logits,
+                            temperature, threshold_single, threshold_acc, uniforms,
+                            final_uniforms, candidates, retrieve_index, retrieve_next_token,
+                            retrieve_next_sibling, predict, accept_index, accept_length,
+                            workspace=None, workspace_bytes=None, dev_status=None, stream=None):
+    dev = _device()
+    n = num_draft_tokens
+    bn = batch * n
+    lb = bn * vocab * _ELEM.get(dtype, 4)
+    need_ws = spec_accept_target_only_workspace_size(batch, n, vocab)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [
+        _ptr(target_logits, "target_logits", dev, nbytes=lb),
+        _ptr(temperature, "temperature", dev, nbytes=batch * 4),
+        float(threshold_single),
+        float(threshold_acc),
+        _ptr(uniforms, "uniforms", dev, nbytes=bn * 4),
+        _ptr(final_uniforms, "final_uniforms", dev, nbytes=batch * 4),
+        _ptr(candidates, "candidates", dev, nbytes=bn * 4),
+        _ptr(retrieve_index, "retrieve_index", dev, nbytes=bn * 4),
+        _ptr(retrieve_next_token, "retrieve_next_token", dev, nbytes=bn * 4),
+        _ptr(retrieve_next_sibling, "retrieve_next_sibling", dev, nbytes=bn * 4),
+        _ptr(predict, "predict", dev, nbytes=bn * 4),
+        _ptr(accept_index, "accept_index", dev, nbytes=batch * accept_width * 4),
+        _ptr(accept_length, "accept_length", dev, nbytes=batch * 4),
+        _ptr(workspace, "workspace", dev, nbytes=need_ws, optional=batch == 0),
+        workspace_bytes,
+        _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
+    ]
+    _check("spec_accept_target_only", _lib.spec_accept_target_only(
+        batch, n, accept_width, vocab, dtype, *args, _stream(stream)))
 
 
 def spec_compact_kv(batch, num_draft_tokens, accept_width, num_layers, num_kv_heads, head_dim,

@@ -62,25 +62,6 @@ __device__ __forceinline__ uint64_t encode_bits(uint64_t b) {
     return b ^ kFlip;
 }
 
-// exp((x - m) / T) to about one float ulp: x - m as an exact float pair
-// (two-sum), 1/T as a float pair, the rounding of the product folded back
-// as a first-order correction.  A masked entry (x = -inf) gives 0.
-struct Scale {
-    float m;
-    float ithi;
-    float itlo;
-};
-
-__device__ __forceinline__ float exp_scaled(float x, const Scale &s) {
-    const float d = x - s.m;
-    const float bp = d - x;
-    const float derr = (x - (d - bp)) + (-s.m - bp);
-    const float y = d * s.ithi;
-    const float delta = fmaf(d, s.ithi, -y) + fmaf(d, s.itlo, derr * s.ithi);
-    const float e = expf(y);
-    return x == -INFINITY ? 0.f : fmaf(e, delta, e);   // -inf: the pair above is NaN
-}
-
 struct RowDist {
     Scale t, d;
     double inv_st, inv_sd;

@@ -64,6 +64,64 @@ __device__ __forceinline__ int64_t elem_index(int64_t start, int tid, int e) {
     return start + (int64_t)(e / 8) * kSweepThreads * 8 + tid * 8 + (e % 8);
 }
 
+// exp((x - m) / T) to about one float ulp: x - m as an exact float pair
+// (two-sum), 1/T as a float pair, the rounding of the product folded back
+// as a first-order correction.  A masked entry (x = -inf) gives 0.
+struct Scale {
+    float m;
+    float ithi;
+    float itlo;
+};
+
+__device__ __forceinline__ float exp_scaled(float x, const Scale &s) {
+    const float d = x - s.m;
+    const float bp = d - x;
+    const float derr = (x - (d - bp)) + (-s.m - bp);
+    const float y = d * s.ithi;
+    const float delta = fmaf(d, s.ithi, -y) + fmaf(d, s.itlo, derr * s.ithi);
+    const float e = expf(y);
+    return x == -INFINITY ? 0.f : fmaf(e, delta, e);   // -inf: the pair above is NaN
+}
+
+// exp((x - m) / T) from the hardware base-2 exponential: (x - m) as an
+// exact float pair, log2(e) / T as a float pair, so (x - m) log2(e) / T is
+// y + delta to about 2^-48 relative; 2^y (v_exp_f32) times (1 + delta ln 2).
+// A masked entry (x = -inf) gives 0; results below 2^-126 flush to 0.
+struct Scale2 {
+    float m;
+    float chi;
+    float clo;
+};
+
+__device__ __forceinline__ Scale2 make_scale2(float m, float temperature) {
+    const double c = 1.4426950408889634 / (double)temperature;
+    const float hi = (float)c;
+    return Scale2{m, hi, (float)(c - (double)hi)};
+}
+
+// the same scale at another max
+__device__ __forceinline__ Scale2 rebase(const Scale2 &s, float m) {
+    return Scale2{m, s.chi, s.clo};
+}
+
+__device__ __forceinline__ float exp2_scaled(float x, const Scale2 &s) {
+    constexpr float kLn2 = 0.69314718055994531f;
+    const float d = x - s.m;
+    const float bp = d - x;
+    const float derr = (x - (d - bp)) + (-s.m - bp);
+    const float y = d * s.chi;
+    const float delta = fmaf(d, s.chi, -y) + fmaf(d, s.clo, derr * s.chi);
+    const float e = __builtin_amdgcn_exp2f(y);
+    return x == -INFINITY ? 0.f : fmaf(e, delta * kLn2, e);
+}
+
+// 1/T as a float pair (high part, rounding remainder)
+__device__ __forceinline__ Scale make_scale(float m, float temperature) {
+    const double it = 1.0 / (double)temperature;
+    const float hi = (float)it;
+    return Scale{m, hi, (float)(it - (double)hi)};
+}
+
 // (v1, i1) beats (v2, i2): larger value, then smaller index; i < 0 = empty
 __device__ __forceinline__ bool arg_better(float v1, int i1, float v2, int i2) {
     return i1 >= 0 && (i2 < 0 || v1 > v2 || (v1 == v2 && i1 < i2));

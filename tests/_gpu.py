@@ -134,6 +134,32 @@ def accept_sample(w, tl, dl, tree, temperature=None, uniforms=None, final_unifor
                 accept_length=host(al), status=int(host(st)[0]))
 
 
+def accept_target_only(w, tl, tree, threshold_single=1.0, threshold_acc=1.0, temperature=None,
+                       uniforms=None, final_uniforms=None, workspace=None, accept_width=None):
+    cfg = w.cfg
+    b, n = cfg.batch, cfg.num_draft_tokens
+    s1 = cfg.num_steps + 1 if accept_width is None else accept_width
+    ws = workspace
+    if ws is None:
+        ws = torch.zeros(S.spec_accept_target_only_workspace_size(b, n, cfg.vocab),
+                         dtype=torch.uint8, device=DEV)
+    predict, ai, al, st = i32(b * n), i32(b * s1), i32(b), status()
+    predict.fill_(-7)
+    ai.fill_(-7)
+    T = w.temperature if temperature is None else temperature
+    U = w.uniforms if uniforms is None else uniforms
+    UF = w.final_uniforms if final_uniforms is None else final_uniforms
+    S.spec_accept_target_only(b, n, s1, cfg.vocab, dtype_code(cfg), dev(tl),
+                              dev(np.asarray(T, np.float32)), threshold_single, threshold_acc,
+                              dev(np.asarray(U, np.float32)), dev(np.asarray(UF, np.float32)),
+                              dev(tree["draft_tokens"]), dev(tree["retrieve_index"]),
+                              dev(tree["retrieve_next_token"]), dev(tree["retrieve_next_sibling"]),
+                              predict, ai, al, workspace=ws, dev_status=st)
+    torch.cuda.synchronize()
+    return dict(predict=host(predict), accept_index=host(ai).reshape(b, s1),
+                accept_length=host(al), status=int(host(st)[0]))
+
+
 def compact_kv(cfg, k_pool, v_pool, page_table, seq_lens, out_cache_loc, accept_index,
                accept_length):
     """Pools are numpy [layers, slots, hkv, d] (uint16 bits or f32)."""

@@ -48,6 +48,9 @@ def test_host_only_queries():
     assert S.spec_mask_word_bytes(0) == 0 and S.spec_mask_word_bytes(65) == 0
     assert S.spec_accept_workspace_size(1, 64, 128256, 0) > 0
     assert S.spec_accept_workspace_size(1, 64, 128256, 1) > S.spec_accept_workspace_size(1, 64, 128256, 0)
+    # one (max, sum) pair of 64-bit words per verify row and 8192-entry chunk
+    assert S.spec_accept_target_only_workspace_size(1, 64, 128256) == 64 * 16 * 16
+    assert S.spec_accept_target_only_workspace_size(0, 64, 128256) == 0
     # a single split needs no workspace; a long history does
     assert S.spec_verify_attention_workspace_size(2, 6, 2, 1, 64, 64, S.SPEC_F32) >= 0
     assert S.spec_verify_attention_workspace_size(4, 64, 64, 8, 128, 131072, S.SPEC_BF16) > 0
@@ -107,6 +110,19 @@ def test_host_errors_before_launch():
     ptrs = [fake] * 12
     ptrs[1] = P0
     assert asm(1, 6, 4, 32, 0, *ptrs, 1 << 20, fake, P0) == -1
+    to = lib.spec_accept_target_only
+    to.restype = I
+    to.argtypes = ([I, I, I, ctypes.c_int64, I, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                    ctypes.c_float] + [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p,
+                                                                ctypes.c_void_p])
+    fake = ctypes.c_void_p(0x1000)
+    big = 1 << 20
+    assert to(1, 6, 4, 32, 0, fake, fake, 1.0, 0.0, *([fake] * 10), big, P0, P0) == -2   # threshold_acc <= 0
+    assert to(1, 6, 4, 32, 9, fake, fake, 1.0, 1.0, *([fake] * 10), big, P0, P0) == -3
+    assert to(1, 6, 4, 32, 0, P0, fake, 1.0, 1.0, *([fake] * 10), big, P0, P0) == -1
+    assert to(1, 6, 4, 32, 0, fake, fake, 1.0, 1.0, *([fake] * 10), 8, P0, P0) == -5     # workspace small
+    assert to(1, 99, 4, 32, 0, fake, fake, 1.0, 1.0, *([fake] * 10), big, P0, P0) == -4
+    assert to(0, 6, 4, 32, 0, P0, P0, 1.0, 1.0, *([P0] * 10), 0, P0, P0) == 0
     ck = lib.spec_compact_kv
     ck.restype = I
     ck.argtypes = [I] * 8 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, I] + [ctypes.c_void_p] * 9 + [ctypes.c_void_p]
