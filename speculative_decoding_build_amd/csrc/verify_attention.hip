@@ -47,6 +47,7 @@ constexpr int kChunkTiles = 8;          // tiles per chunk of the slot ring
 constexpr int kChunkKeys = kChunkTiles * kTileKeys;
 constexpr int kMaxTreeNodes = 64;
 constexpr int kSmallGrid = 512;         // fewer 8-wave workgroups than this: use 4-wave ones
+constexpr int kOneRound = 256;          // workgroups that fit one per CU
 constexpr int kPlanBatch = 1024;        // most requests a length-balanced plan covers
 constexpr int kMergeVec = 1;            // output vectors per merge wave (bf16)
 
@@ -238,9 +239,13 @@ __device__ void plan_split(const AttnParams &P, int j, bool store, int *out) {
 
 constexpr float kLazy = 8.0f;
 
-template <int D, int NW>
+// KH = 2: the waves come in pairs that own the same 32 query rows and take
+// the two 32-key halves of every tile; the pair merges its (max, sum, O)
+// through LDS at the end.  NW / KH row blocks per workgroup.
+template <int D, int NW, int KH>
 __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams P, int xcd_remap) {
     static_assert(D == 64 || D == 128, "head_dim");
+    static_assert(KH == 1 || KH == 2, "key halves");
     constexpr int KS = D + 8;              // K row stride (bf16), 16-byte pad
     constexpr int VS = kTileKeys + 8;      // V^T row stride (bf16): 36 dwords, so the
                                            // 16-byte reads of 16 rows hit distinct banks
@@ -256,8 +261,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
     constexpr int DK = D / 16;             // MFMA k-steps over head_dim
     constexpr int DT = D / 32;             // 32-row d tiles of O^T
 
-    __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kTileKeys * KS];
-    __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * VS];
+    // K and V^T tile stages; after the loop the same bytes hold the key-half
+    // partners' (max, sum, O) for the merge
+    constexpr int KBYTES = 2 * kTileKeys * KS * 2, VBYTES = 2 * D * VS * 2;
+    constexpr int MSTRIDE = DT * 16 + 2;   // floats per lane: O^T, max, sum
+    constexpr int MBYTES = KH == 2 ? (NW / 2) * 64 * MSTRIDE * 4 : 0;
+    static_assert(MBYTES <= KBYTES + VBYTES, "merge buffer");
+    __shared__ __attribute__((aligned(16))) char lds_tiles[KBYTES + VBYTES];
+    auto k_lds = reinterpret_cast<__bf16 (*)[kTileKeys * KS]>(lds_tiles);
+    auto vt_lds = reinterpret_cast<__bf16 (*)[D * VS]>(lds_tiles + KBYTES);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -332,8 +344,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
     if (tid < P.n) s_tree[tid] = pre_tree;
 
     // ---- query fragments (B operand of S^T = K Q^T) -----------------------
-    const int rho = rg * P.rows_per_group + wave * 32 + col;
-    const bool wave_active = rg * P.rows_per_group + wave * 32 < P.rows;
+    const int rblk = wave % (NW / KH);     // row block of this wave
+    const int khalf = wave / (NW / KH);    // key half of this wave (KH = 2)
+    const int rho = rg * P.rows_per_group + rblk * 32 + col;
+    const bool wave_active = rg * P.rows_per_group + rblk * 32 < P.rows;
     bf16x8 qf[DK];
     uint64_t mword = 0;
     if (rho < P.rows) {
@@ -487,7 +501,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
             const __bf16 *vt = vt_lds[it & 1];
             const bool edge = (tile_base + kTileKeys > ke) || (tile_base + kTileKeys > L);
 #pragma unroll
-            for (int sub = 0; sub < kTileKeys / 32; ++sub) {
+            for (int si = 0; si < kTileKeys / 32 / KH; ++si) {
+                const int sub = KH == 2 ? khalf : si;
                 floatx16 sacc = floatx16{};
 #pragma unroll
                 for (int kk = 0; kk < DK; ++kk) {
@@ -568,6 +583,36 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
     for (int it = 0; it < ntiles; it += 2) {
         step(it, kreg1, vreg1);                  // even step: tiles it+1, it+3 use set 1
         if (it + 1 < ntiles) step(it + 1, kreg0, vreg0);
+    }
+
+    // ---- key-half merge: the second wave of a pair hands over its state ----
+    if constexpr (KH == 2) {
+        float *mb = reinterpret_cast<float *>(lds_tiles) + (rblk * 64 + lane) * MSTRIDE;
+        __syncthreads();                   // every wave is done with the tiles
+        if (khalf == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mb[dt * 16 + i] = oacc[dt][i];
+            mb[DT * 16] = m_run;
+            mb[DT * 16 + 1] = l_run;
+        }
+        __syncthreads();
+        if (khalf == 1) {
+            for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, 64);
+            if (lane == 0) spec::raise_status(P.status, err);
+            return;
+        }
+        const float m2 = mb[DT * 16], l2 = mb[DT * 16 + 1];
+        const float mm = fmaxf(m_run, m2);
+        const float a1 = m_run == -INFINITY ? 0.f : exp2f(m_run - mm);
+        const float a2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mm);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[dt][i] = oacc[dt][i] * a1 + mb[dt * 16 + i] * a2;
+        l_run = l_run * a1 + l2 * a2;
+        m_run = mm;
     }
 
     // ---- epilogue -------------------------------------------------------------
@@ -806,7 +851,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
 // ---------------------------------------------------------------------------
 
 struct Plan {
-    int nw;               // waves per workgroup (bf16: one 32-row query tile each)
+    int nw;               // waves per workgroup
+    int kh;               // bf16: waves per 32-row query block (2: key halves)
     int rows_per_group, rowgroups;
     int split_len, nsplit;  // static plan: every request cut at max_seq_len's splits
     int dyn, slots;         // length-balanced plan over `slots` split slots (bf16, batch > 1)
@@ -816,9 +862,10 @@ Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
     Plan pl{};
     const int rows = n * (hq / hkv);
     if (dtype == SPEC_BF16) {
-        // 8-wave workgroups (one row group of up to 256 rows) unless that
-        // leaves the device short of workgroups; then 4-wave ones, whose row
-        // groups read the same K/V (from L2) in parallel
+        // 8-wave workgroups of one wave per 32-row block (row groups of up to
+        // 256 rows) unless that leaves the device short of workgroups; then
+        // row groups of up to 128 rows, which read the same K/V (from L2) in
+        // parallel, each block served by two waves (key halves)
         pl.nw = rows <= 128 ? 4 : 8;
         if (pl.nw == 8) {
             const int tiles8 = (max_seq_len + n + kTileKeys - 1) / kTileKeys;
@@ -826,9 +873,11 @@ Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
                                 std::max(1, std::min(tiles8 / kMinTiles, kMaxSplits));
             if (groups8 < kSmallGrid) pl.nw = 4;
         }
+        pl.kh = 1;
         pl.rows_per_group = pl.nw * 32;
     } else {
         pl.nw = 4;
+        pl.kh = 1;
         pl.rows_per_group = rows;
     }
     pl.rowgroups = (rows + pl.rows_per_group - 1) / pl.rows_per_group;
@@ -854,6 +903,14 @@ Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
             pl.slots = S;
         }
     }
+    // A grid of 4-wave workgroups that fits one workgroup per CU leaves
+    // every SIMD one wave: give each 32-row block two waves instead, each
+    // taking one 32-key half of every tile.
+    const int groups = pl.dyn ? pl.slots * pl.rowgroups * hkv : pl.nsplit * pl.rowgroups * hkv * batch;
+    if (dtype == SPEC_BF16 && pl.nw == 4 && groups <= kOneRound) {
+        pl.nw = 8;
+        pl.kh = 2;
+    }
     return pl;
 }
 
@@ -875,10 +932,12 @@ size_t workspace_bytes_for(const Plan &pl, int batch, int n, int hq, int hkv, in
 template <int D>
 void launch_mfma(const Plan &pl, const AttnParams &P, unsigned groups, hipStream_t st) {
     const int remap = groups % 8 == 0 ? 1 : 0;
-    if (pl.nw == 4)
-        hipLaunchKernelGGL((attn_split_mfma_kernel<D, 4>), dim3(groups), dim3(256), 0, st, P, remap);
+    if (pl.kh == 2)
+        hipLaunchKernelGGL((attn_split_mfma_kernel<D, 8, 2>), dim3(groups), dim3(512), 0, st, P, remap);
+    else if (pl.nw == 4)
+        hipLaunchKernelGGL((attn_split_mfma_kernel<D, 4, 1>), dim3(groups), dim3(256), 0, st, P, remap);
     else
-        hipLaunchKernelGGL((attn_split_mfma_kernel<D, 8>), dim3(groups), dim3(512), 0, st, P, remap);
+        hipLaunchKernelGGL((attn_split_mfma_kernel<D, 8, 1>), dim3(groups), dim3(512), 0, st, P, remap);
 }
 
 }  // namespace
