@@ -885,16 +885,19 @@ Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
     // with at least kMinTiles tiles per split
     const int keys = max_seq_len + n;
     const int tiles = (keys + kTileKeys - 1) / kTileKeys;
+    // No split when the (request, KV head, row group) items alone fill the
+    // device: splitting would only add partials and the merge.
     const int base = batch * hkv * pl.rowgroups;
     int ns = (kTargetGroups + base - 1) / base;
     ns = std::max(1, std::min({ns, tiles / kMinTiles, kMaxSplits}));
+    if (base >= kOneRound) ns = 1;
     const int tiles_per = (tiles + ns - 1) / ns;
     pl.split_len = tiles_per * kTileKeys;
     pl.nsplit = (keys + pl.split_len - 1) / pl.split_len;
     // Several requests: split by the actual lengths instead, so a batch of
     // mixed lengths gives every workgroup about the same number of tiles.
     // No more slots than requests at max_seq_len could use.
-    if (dtype == SPEC_BF16 && batch > 1 && batch <= kPlanBatch) {
+    if (dtype == SPEC_BF16 && batch > 1 && batch <= kPlanBatch && base < kOneRound) {
         const int per_head = hkv * pl.rowgroups;
         int S = (kTargetGroups + per_head - 1) / per_head;
         S = std::min(S, batch * std::max(1, std::min(tiles / kMinTiles, kMaxSplits)));
