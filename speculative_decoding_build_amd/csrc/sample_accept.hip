@@ -31,8 +31,9 @@
 // data, so decisions need no communication.  When the grid cannot be
 // co-resident the walk runs as one 1024-thread workgroup per request.
 //
-// Per-entry probabilities are float32 exponentials of the exactly formed
-// argument (x - max) / T, normalised and accumulated in float64.
+// Per-entry probabilities are float32 exponentials (the hardware base-2
+// exponential) of the argument (x - max) log2(e) / T carried as a float
+// pair, normalised and accumulated in float64.
 #include <algorithm>
 
 #include "sweep_common.h"
@@ -63,7 +64,7 @@ __device__ __forceinline__ uint64_t encode_bits(uint64_t b) {
 }
 
 struct RowDist {
-    Scale t, d;
+    Scale2 t, d;
     double inv_st, inv_sd;
 };
 
@@ -186,19 +187,19 @@ __device__ __forceinline__ float full_wave_max(float v) {
 
 // s * exp((m - M) / T): a partial sum taken at max m, rescaled to max M
 // (float exponential of the exactly formed argument; 0 for an empty part)
-__device__ __forceinline__ double rescale(float m, double s, float M, float ithi, float itlo) {
-    return m == -INFINITY ? 0.0 : s * (double)exp_scaled(m, Scale{M, ithi, itlo});
+__device__ __forceinline__ double rescale(float m, double s, float M, float chi, float clo) {
+    return m == -INFINITY ? 0.0 : s * (double)exp2_scaled(m, Scale2{M, chi, clo});
 }
 
 // Max and sum of exponentials from every thread's partial (m, s), target and
 // draft at once; every thread gets the workgroup's values.
 template <int NT>
-__device__ void block_stats(float &mt, double &st, float &md, double &sd, float ithi, float itlo,
+__device__ void block_stats(float &mt, double &st, float &md, double &sd, float chi, float clo,
                             float *sm, double *ss) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float wt = full_wave_max(mt), wd = full_wave_max(md);
-    const double rt = full_wave_sum_d(rescale(mt, st, wt, ithi, itlo));
-    const double rd = full_wave_sum_d(rescale(md, sd, wd, ithi, itlo));
+    const double rt = full_wave_sum_d(rescale(mt, st, wt, chi, clo));
+    const double rd = full_wave_sum_d(rescale(md, sd, wd, chi, clo));
     if (lane == 0) {
         sm[2 * wave] = wt;
         sm[2 * wave + 1] = wd;
@@ -215,8 +216,8 @@ __device__ void block_stats(float &mt, double &st, float &md, double &sd, float 
     double St = 0.0, Sd = 0.0;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) {
-        St += rescale(sm[2 * w], ss[2 * w], Mt, ithi, itlo);
-        Sd += rescale(sm[2 * w + 1], ss[2 * w + 1], Md, ithi, itlo);
+        St += rescale(sm[2 * w], ss[2 * w], Mt, chi, clo);
+        Sd += rescale(sm[2 * w + 1], ss[2 * w + 1], Md, chi, clo);
     }
     __syncthreads();
     mt = Mt;
@@ -348,9 +349,10 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     const int n = A.n;
     const int base = req * n;
     const size_t eb = DT == SPEC_BF16 ? 2 : 4;
-    const double it = 1.0 / (double)A.temperature[req];
-    const float ithi = (float)it;
-    const float itlo = (float)(it - (double)ithi);
+    // log2(e) / T as a float pair (the exponentials are base 2)
+    const double it = 1.4426950408889634 / (double)A.temperature[req];
+    const float chi = (float)it;
+    const float clo = (float)(it - (double)chi);
 
     // my slice of the vocabulary and, inside it, my contiguous segment
     const int64_t v0 = min(A.vocab, (int64_t)g * A.slice);
@@ -466,16 +468,16 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                     }
                     mt = full_wave_max(jmt);
                     md = full_wave_max(jmd);
-                    st = full_wave_sum_d(rescale(jmt, jst, mt, ithi, itlo));
-                    sd = full_wave_sum_d(rescale(jmd, jsd, md, ithi, itlo));
+                    st = full_wave_sum_d(rescale(jmt, jst, mt, chi, clo));
+                    sd = full_wave_sum_d(rescale(jmd, jsd, md, chi, clo));
                 }
                 ++e;
             }
         }
         if (tid == 0) {
             RowDist r;
-            r.t = Scale{mt, ithi, itlo};
-            r.d = Scale{md, ithi, itlo};
+            r.t = Scale2{mt, chi, clo};
+            r.d = Scale2{md, chi, clo};
             r.inv_st = st > 0.0 ? 1.0 / st : 0.0;
             r.inv_sd = sd > 0.0 ? 1.0 / sd : 0.0;
             S.dist[xb & 1] = r;
@@ -542,8 +544,8 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                           [&](int64_t, const float (&xt)[8], const float (&xd)[8], int) {
 #pragma unroll
                               for (int j = 0; j < 8; ++j)
-                                  m += resid_from_exp(exp_scaled(xt[j], rd.t),
-                                                      exp_scaled(xd[j], rd.d), rd, cc);
+                                  m += resid_from_exp(exp2_scaled(xt[j], rd.t),
+                                                      exp2_scaled(xd[j], rd.d), rd, cc);
                           });
         }
         return m;
@@ -580,13 +582,13 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             }
             // the registers now take the exponentials relative to this
             // thread's max; one factor per row moves them to the row's max
-            const Scale sct{mt, ithi, itlo}, scd{md, ithi, itlo};
+            const Scale2 sct{mt, chi, clo}, scd{md, chi, clo};
             float ft = 0.f, fd = 0.f;
 #pragma unroll
             for (int i = 0; i < kCacheEntries; ++i) {
                 if (i == 8 && !wide) break;
-                ct[i] = exp_scaled(ct[i], sct);
-                cd[i] = exp_scaled(cd[i], scd);
+                ct[i] = exp2_scaled(ct[i], sct);
+                cd[i] = exp2_scaled(cd[i], scd);
                 ft += ct[i];
                 fd += cd[i];
             }
@@ -604,31 +606,31 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                                   md = fmaxf(md, xd[j]);
                               }
                           });
-            const Scale sct{mt, ithi, itlo}, scd{md, ithi, itlo};
+            const Scale2 sct{mt, chi, clo}, scd{md, chi, clo};
             float ft = 0.f, fd = 0.f;
             for_each8<DT>(trow, drow, sa, sb, A.vec_ok,
                           [&](int64_t, const float (&xt)[8], const float (&xd)[8], int) {
 #pragma unroll
                               for (int j = 0; j < 8; ++j) {
-                                  ft += exp_scaled(xt[j], sct);
-                                  fd += exp_scaled(xd[j], scd);
+                                  ft += exp2_scaled(xt[j], sct);
+                                  fd += exp2_scaled(xd[j], scd);
                               }
                           });
             st = ft;
             sd = fd;
         }
         const float thr_mt = mt, thr_md = md;
-        block_stats<NT>(mt, st, md, sd, ithi, itlo, S.sm, S.ss);
+        block_stats<NT>(mt, st, md, sd, chi, clo, S.sm, S.ss);
         rd = exchange_stats(mt, st, md, sd);
         if (is_child) {
-            S.cp[tid] = (double)exp_scaled(kid_t, rd.t) * rd.inv_st;
-            S.cq[tid] = (double)exp_scaled(kid_d, rd.d) * rd.inv_sd;
+            S.cp[tid] = (double)exp2_scaled(kid_t, rd.t) * rd.inv_st;
+            S.cq[tid] = (double)exp2_scaled(kid_d, rd.d) * rd.inv_sd;
         }
         __syncthreads();
         if (!alive) break;
         if constexpr (use_cache) {
-            const float ft = thr_mt == -INFINITY ? 0.f : exp_scaled(thr_mt, rd.t);
-            const float fd = thr_md == -INFINITY ? 0.f : exp_scaled(thr_md, rd.d);
+            const float ft = thr_mt == -INFINITY ? 0.f : exp2_scaled(thr_mt, rd.t);
+            const float fd = thr_md == -INFINITY ? 0.f : exp2_scaled(thr_md, rd.d);
 #pragma unroll
             for (int i = 0; i < kCacheEntries; ++i) {
                 if (i == 8 && !wide) break;
@@ -748,8 +750,8 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                                           if (x >= 0) return;
 #pragma unroll
                                           for (int j = 0; j < 8; ++j) {
-                                              run += resid_from_exp(exp_scaled(xt[j], rd.t),
-                                                                    exp_scaled(xd[j], rd.d), rd, c);
+                                              run += resid_from_exp(exp2_scaled(xt[j], rd.t),
+                                                                    exp2_scaled(xd[j], rd.d), rd, c);
                                               if (x < 0 && j < cnt && run > tgt) x = v + j;
                                           }
                                       });
