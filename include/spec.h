@@ -113,7 +113,9 @@ int spec_mask_word_bytes(int num_draft_tokens);
  * Data errors: parent index outside [0, ncand) -> SPEC_ST_RANGE; parent not
  *   kept -> SPEC_ST_NOT_CLOSED; such a node is attached to the root.
  * Limits: 1 <= n <= 64, n-1 <= ncand <= 4096, topk >= 1, num_steps >= 1.
- * Scores must not be NaN.
+ * Scores must not be NaN.  When n - 1 = ncand every candidate is kept (the
+ * chain of a topk-1 draft with n = num_steps + 1): the selection is the
+ * identity, the ranking is skipped and scores are not read.
  */
 int spec_build_tree(int batch, int topk, int num_steps, int num_draft_tokens, int mask_mode,
                     const float *scores, const int32_t *tokens, const int32_t *parents,

@@ -15,7 +15,9 @@
 // exactly "take the top n-1, then sort their indices ascending"; the
 // comparisons of each candidate are shared among all threads of the
 // workgroup.  Structure work (depth, ancestor bits, child/sibling links)
-// runs on one wavefront with a lane per node.
+// runs on one wavefront with a lane per node.  When every candidate is kept
+// (the chain of a topk-1 draft, n = num_steps + 1, the case the pages give a
+// dedicated chain builder), the ranking is skipped and no score is read.
 #include "spec_common.h"
 
 namespace {
@@ -60,9 +62,12 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     const int wave = tid / SPEC_WAVE;
     const int keep = n - 1;
     const float *sc = scores + (size_t)r * ncand;
+    // every candidate kept (a chain: topk 1, n = num_steps + 1, or any tree
+    // with n - 1 = ncand): the selection is the identity and no score is read
+    const bool all_kept = keep == ncand;
 
     for (int f = tid; f < ncand; f += kThreads) {
-        s_key[f] = order_key(sc[f], f);
+        if (!all_kept) s_key[f] = order_key(sc[f], f);
         s_tok[f] = tokens[(size_t)r * ncand + f];
     }
     if (parents != nullptr)
@@ -83,7 +88,14 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     const int parts = kThreads / per;                  // 1 .. 16
     const int span = ((ncand + parts - 1) / parts + 1) & ~1;   // keys per part, even
     int before_rounds = 0;
-    for (int f0 = 0; f0 < ncand; f0 += per) {
+    if (all_kept) {
+        for (int f = tid; f < ncand; f += kThreads) {
+            s_node[f] = static_cast<int16_t>(f + 1);
+            s_flat[f + 1] = f;
+        }
+        __syncthreads();
+    }
+    for (int f0 = 0; f0 < (all_kept ? 0 : ncand); f0 += per) {
         {
             const int c = tid % per, part = tid / per;
             const int f = f0 + c;

@@ -92,6 +92,35 @@ def _attn_err(got, ref):
     return float((num / np.maximum(den, 1e-30)).max())
 
 
+# Trees whose every candidate is kept (n - 1 = ncand): the kernel skips the
+# ranking; a full topk-2 step, a full 2-level topk-3 tree and a 7-node chain,
+# each with both mask layouts.
+ALL_KEPT = {
+    "topk2_s1_n3": dict(topk=2, num_steps=1, num_draft_tokens=3),
+    "topk3_s2_n13": dict(topk=3, num_steps=2, num_draft_tokens=13),
+    "chain_s6_n7": dict(topk=1, num_steps=6, num_draft_tokens=7),
+}
+
+
+@pytest.mark.parametrize("name", list(ALL_KEPT))
+def test_build_tree_all_kept(name):
+    cfg = W.shrink(W.CONFIGS[3], batch=3, hist=("fixed", 8), vocab=500, **ALL_KEPT[name])
+    w = W.make_workload(cfg, 5, attention=False)
+    t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                          cfg.num_steps, cfg.num_draft_tokens)
+    b, n = cfg.batch, cfg.num_draft_tokens
+    for mode in (S.SPEC_MASK_QLEN_BITS, S.SPEC_MASK_QLEN_U8):
+        g = G.build_tree(w, mask_mode=mode)
+        assert g["status"] == t["status"] == 0
+        np.testing.assert_array_equal(g["draft_tokens"], t["draft_tokens"])
+        np.testing.assert_array_equal(g["positions"], t["positions"])
+        np.testing.assert_array_equal(g["retrieve_next_token"].reshape(b, n), t["retrieve_next_token"])
+        np.testing.assert_array_equal(g["retrieve_next_sibling"].reshape(b, n),
+                                      t["retrieve_next_sibling"])
+        np.testing.assert_array_equal(g["selected"][:b * (n - 1)].reshape(b, n - 1), t["selected"])
+        np.testing.assert_array_equal(g["tree_mask"], oracle.pack_mask(t["mask"], mode))
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_verify_attention_small(name):
     w, t, _, _ = workload(name)
