@@ -35,6 +35,12 @@ Readings where the pages are silent (each also listed in the design notes):
     is drawn like the sampled accept's, from relu(p - buffer).
   * Malformed trees: a node whose parent is not selected (or whose parent
     index is out of range) hangs off the root and raises a status bit.
+  * Draft step: the draft distribution of a branch is softmax(logits) held at
+    float32 (the draft's probability dtype), rounded once from float64; its
+    top-k and the top-k over the path products rank by value descending,
+    lower index first among equal values; path products are float32
+    multiplications of float32 values (the page multiplies float32 tensors),
+    so both sides take every integer decision from the same float32 values.
 
 Status bits (OR-ed per call): 1 index out of range, 2 selection not closed
 under ancestors, 4 accepted path longer than the accept_index row, 8 residual
@@ -463,6 +469,96 @@ def accept_target_only(target_logits, temperature, threshold_single, threshold_a
     return dict(predict=predict, accept_index=accept_index, accept_length=accept_length,
                 margin=margin, draw_margin=draw_margin,
                 exempt=(margin < band) | (draw_margin < draw_band), status=status)
+
+
+# ---------------------------------------------------------------------------
+# Draft step (select_top_k_tokens)
+# ---------------------------------------------------------------------------
+
+def topk_desc(values, k):
+    """The k largest entries of a 1-D array ranked by (value descending,
+    index ascending): (values, indices).  [P1] fast_topk / torch.topk; the
+    order among equal values is this reading's."""
+    v = np.asarray(values)
+    order = sorted(range(v.size), key=lambda i: (-float(v[i]), i))[:k]
+    idx = np.array(order, dtype=np.int64)
+    return v[idx], idx
+
+
+def draft_probs(logits_row, dtype):
+    """[P1] the draft distribution a step ranks: softmax of the branch's
+    logits, float64 then rounded to float32."""
+    x = widen(logits_row, dtype)
+    e = np.exp(x - x.max())
+    return (e / e.sum()).astype(np.float32)
+
+
+def draft_step(draft_logits, branch_scores, step, topk, num_steps, dtype):
+    """One call of [P1] select_top_k_tokens for a batch.
+
+    draft_logits: [b, rows, V] logits of the live branches (rows = 1 at step
+    0, topk later); branch_scores: [b, topk] float32 path scores of the live
+    branches (unused at step 0).  Returns the step's blocks of the three
+    lists organize_draft_results concatenates, with their offsets, and the
+    next step's branch scores and input tokens:
+
+      step 0 (_select_top_k_tokens_first): scores = tokens-ranked top-k of
+        the root distribution, tokens = their ids, parents = arange(-1, topk);
+      step i >= 1 (_select_top_k_tokens_later): expand[j, c] = branch
+        score j x probability of branch j's c-th top-k token; scores =
+        expand flattened, tokens = the top-k ids of every branch, and the
+        top-k over the topk*topk products (cs) gives parents = cs + topk*topk
+        * (i - 1) + topk, the next branch scores expand[cs], and the next
+        input tokens tokens[cs].
+
+    The score/token block of step i starts at 0 (i = 0) or topk + (i - 1) *
+    topk^2 of the request's ncand entries; the parent block at 0 (i = 0) or
+    topk + 1 + (i - 1) * topk of its npar entries, and the last step's parent
+    block is not part of the list (organize_draft_results drops it).
+    ``gap`` is the smallest relative distance between the k-th and the
+    (k+1)-th value of any ranking the step made (inf when there is none).
+    """
+    dl = np.asarray(draft_logits)
+    b, rows, _ = dl.shape
+    tk2 = topk * topk
+    out = []
+    for r in range(b):
+        gap = math.inf
+        pv = np.zeros((rows, topk), np.float32)
+        pi = np.zeros((rows, topk), np.int64)
+        for j in range(rows):
+            p = draft_probs(dl[r, j], dtype)
+            vals, idx = topk_desc(p, topk + 1)
+            pv[j], pi[j] = vals[:topk], idx[:topk]
+            if vals.size > topk and vals[topk - 1] > 0:
+                gap = min(gap, (float(vals[topk - 1]) - float(vals[topk])) / float(vals[topk - 1]))
+        if step == 0:
+            res = dict(scores=pv[0].copy(), tokens=pi[0].copy(),
+                       parents=np.arange(-1, topk, dtype=np.int64),
+                       next_scores=pv[0].copy(), next_tokens=pi[0].copy())
+        else:
+            bs = np.asarray(branch_scores[r], dtype=np.float32)
+            expand = (bs[:, None] * pv).astype(np.float32)          # float32 products
+            flat = expand.reshape(-1)
+            tokens = pi.reshape(-1)
+            vals, cs = topk_desc(flat, topk + 1)
+            if vals.size > topk and vals[topk - 1] > 0:
+                gap = min(gap, (float(vals[topk - 1]) - float(vals[topk])) / float(vals[topk - 1]))
+            cs = cs[:topk]
+            res = dict(scores=flat.copy(), tokens=tokens.copy(),
+                       parents=cs + tk2 * (step - 1) + topk,
+                       next_scores=flat[cs].copy(), next_tokens=tokens[cs].copy())
+        res["gap"] = gap
+        out.append(res)
+    off_s = 0 if step == 0 else topk + (step - 1) * tk2
+    off_p = 0 if step == 0 else topk + 1 + (step - 1) * topk
+    return dict(
+        scores=np.stack([o["scores"] for o in out]), tokens=np.stack([o["tokens"] for o in out]),
+        parents=np.stack([o["parents"] for o in out]),
+        next_scores=np.stack([o["next_scores"] for o in out]),
+        next_tokens=np.stack([o["next_tokens"] for o in out]),
+        gap=np.array([o["gap"] for o in out]), score_offset=off_s, parent_offset=off_p,
+        write_parents=step < num_steps - 1)
 
 
 # ---------------------------------------------------------------------------

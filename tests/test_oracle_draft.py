@@ -1,0 +1,100 @@
+"""Pins of the oracle's draft step ([P1] select_top_k_tokens) against things
+other than itself: a hand-worked two-step example (tests/golden), the list
+lengths and offsets the page states, the tie rule, and the input
+generator's own draft-loop record (an independent float32 implementation of
+the same loop) on the shapes of every workload."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+
+def _logits_for(probs):
+    """float32 logits whose softmax is the given distribution."""
+    return np.log(np.asarray(probs, np.float64)).astype(np.float32)
+
+
+def test_hand_worked_two_steps(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "draft_step_tiny.json")))
+    topk, S = g["topk"], g["num_steps"]
+    s0 = g["step0"]
+    o = oracle.draft_step(_logits_for(s0["probs"])[None], None, 0, topk, S, "f32")
+    np.testing.assert_allclose(o["scores"][0], s0["scores"], rtol=1e-6)
+    assert o["tokens"][0].tolist() == s0["tokens"]
+    assert o["parents"][0].tolist() == s0["parents"]
+    s1 = g["step1"]
+    bs = np.asarray([s1["branch_scores"]], np.float32)
+    o1 = oracle.draft_step(_logits_for(s1["probs"])[None], bs, 1, topk, S, "f32")
+    np.testing.assert_allclose(o1["scores"][0], s1["scores"], rtol=1e-6)
+    assert o1["tokens"][0].tolist() == s1["tokens"]
+    assert o1["parents"][0].tolist() == s1["parents"]
+    np.testing.assert_allclose(o1["next_scores"][0], s1["next_scores"], rtol=1e-6)
+    assert o1["next_tokens"][0].tolist() == s1["next_tokens"]
+    assert o1["score_offset"] == g["offsets"]["step1_scores"]
+    assert o1["parent_offset"] == g["offsets"]["step1_parents"]
+    o2 = oracle.draft_step(_logits_for(s1["probs"])[None], bs, 2, topk, S, "f32")
+    assert o2["score_offset"] == g["offsets"]["step2_scores"]
+    assert o2["parent_offset"] == g["offsets"]["step2_parents"]
+    assert not o2["write_parents"]           # the last step's parents are dropped
+
+
+@pytest.mark.parametrize("topk,steps", [(4, 5), (8, 6), (1, 4), (2, 3)])
+def test_list_lengths_and_offsets(topk, steps):
+    # the page: score rows 1 + (steps-1) topk (17 for 5 steps of topk 4),
+    # token list topk + (steps-1) topk^2, parent list 1 + (steps-1) topk
+    ncand = topk + (steps - 1) * topk * topk
+    npar = 1 + (steps - 1) * topk
+    if (topk, steps) == (4, 5):
+        assert npar == 17
+    end_s = end_p = 0
+    for i in range(steps):
+        logits = np.zeros((1, 1 if i == 0 else topk, max(topk + 1, 4)), np.float32)
+        bs = None if i == 0 else np.full((1, topk), 0.5, np.float32)
+        o = oracle.draft_step(logits, bs, i, topk, steps, "f32")
+        assert o["score_offset"] == end_s
+        end_s += o["scores"].shape[1]
+        if o["write_parents"]:
+            assert o["parent_offset"] == end_p
+            end_p += o["parents"].shape[1]
+    assert end_s == ncand and end_p == npar
+
+
+def test_ties_take_the_lower_index():
+    logits = np.zeros((1, 1, 10), np.float32)
+    o = oracle.draft_step(logits, None, 0, 3, 2, "f32")
+    assert o["tokens"][0].tolist() == [0, 1, 2]
+    assert o["gap"][0] == 0.0
+    # equal products across branches: lower flat index first
+    o1 = oracle.draft_step(np.zeros((1, 3, 10), np.float32), np.full((1, 3), 0.2, np.float32), 1,
+                           3, 4, "f32")
+    assert o1["parents"][0].tolist() == [3, 4, 5]          # flat 0, 1, 2 + 9*0 + 3
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_reproduces_the_generators_draft_loop(cid):
+    cfg = W.CONFIGS[cid]
+    if cid != 1:
+        cfg = W.shrink(cfg, batch=min(cfg.batch, 3), hist=("fixed", 8), vocab=3000)
+    w = W.make_workload(cfg, 100 + cid, attention=False)
+    b, topk, S = cfg.batch, cfg.topk, cfg.num_steps
+    scores = np.zeros((b, cfg.ncand), np.float32)
+    tokens = np.zeros((b, cfg.ncand), np.int64)
+    parents = np.full((b, cfg.npar), -7, np.int64)
+    bs = None
+    for i in range(S):
+        rows = w.ctx_draft[:, 0:1] if i == 0 else w.ctx_draft[:, 1 + (i - 1) * topk:1 + i * topk]
+        o = oracle.draft_step(rows, bs, i, topk, S, cfg.dtype)
+        k = o["scores"].shape[1]
+        scores[:, o["score_offset"]:o["score_offset"] + k] = o["scores"]
+        tokens[:, o["score_offset"]:o["score_offset"] + k] = o["tokens"]
+        if o["write_parents"]:
+            p = o["parents"].shape[1]
+            parents[:, o["parent_offset"]:o["parent_offset"] + p] = o["parents"]
+        bs = o["next_scores"]
+    np.testing.assert_array_equal(tokens, w.tokens)
+    np.testing.assert_array_equal(parents, w.parents)
+    np.testing.assert_allclose(scores, w.scores, rtol=2e-6)
