@@ -280,6 +280,47 @@ int spec_accept_target_only(int batch, int num_draft_tokens, int accept_width, i
                             size_t workspace_bytes, int32_t *dev_status, spec_stream_t stream);
 
 /*
+ * Draft step: one call of select_top_k_tokens for a batch.  [P1]
+ * organize_draft_results:三张表的归约 (_select_top_k_tokens_first /
+ * _select_top_k_tokens_later and the offsets organize_draft_results reads);
+ * [P5] on the accumulated path score of the EAGLE-2 dynamic tree.
+ *
+ *   draft_logits [batch, rows, vocab] dtype: the draft model's logits of
+ *       the live branches, rows = 1 at step 0 (the root), topk later
+ *   branch_scores [batch, topk] f32: the live branches' path scores (the
+ *       previous call's next_scores); ignored (may be NULL) at step 0
+ * p = softmax(draft_logits row), rounded to f32.  Each row's top-topk
+ * entries are ranked by (p descending, token id ascending).
+ *   step 0: scores / tokens get the root's top-topk p and ids at offset 0;
+ *       parents gets -1, 0, .., topk-1 at offset 0.
+ *   step i >= 1: scores gets the f32 products branch_scores[j] * p_j[c]
+ *       (topk*topk, branch-major) and tokens their ids, at offset
+ *       topk + (i-1)*topk^2; the top-topk products (value descending, lower
+ *       flat index first) give parents = flat index + topk^2*(i-1) + topk at
+ *       offset topk + 1 + (i-1)*topk.
+ *   The parent block of step num_steps-1 is not written (it is not part of
+ *   the list; parents may be NULL then).  next_scores / next_tokens
+ *   [batch, topk] get the kept scores and ids (step 0: the root's top-topk),
+ *   the next call's branch_scores and input tokens; next_scores may be the
+ *   same buffer as branch_scores.
+ * Row layouts of scores / tokens [batch, topk + (num_steps-1)*topk^2] and
+ * parents [batch, 1 + (num_steps-1)*topk] are those spec_build_tree reads;
+ * entries of other steps are not touched.  Normalisers are sums of f32
+ * exponentials in f64, so a p may differ from the exact f64 softmax by an
+ * ulp and a ranking within ~1e-6 relative of a tie may differ from an
+ * exact evaluation.  topk <= 8 and rows * ceil(vocab / 8192) * topk <= 4096
+ * (vocab <= 524288 at topk 8), else SPEC_ERR_UNSUPPORTED; vocab >= topk.
+ * workspace: spec_draft_step_workspace_size(batch, topk, vocab) bytes,
+ *   8-byte aligned, any contents (80 bytes per row and 8192-entry chunk).
+ */
+size_t spec_draft_step_workspace_size(int batch, int topk, int64_t vocab);
+int spec_draft_step(int batch, int topk, int num_steps, int step, int64_t vocab, int dtype,
+                    const void *draft_logits, const float *branch_scores, float *scores,
+                    int32_t *tokens, int32_t *parents, float *next_scores,
+                    int32_t *next_tokens, void *workspace, size_t workspace_bytes,
+                    int32_t *dev_status, spec_stream_t stream);
+
+/*
  * Accepted-KV compaction.  [P1] KV 回写 (move_accept_tokens_to_target_kvcache)
  * and [P2] 六: the verify rows in accept_index (root plus accepted drafts;
  * the terminal token has no KV yet) move to the request's sequence positions

@@ -517,21 +517,33 @@ def draft_step(draft_logits, branch_scores, step, topk, num_steps, dtype):
     block is not part of the list (organize_draft_results drops it).
     ``gap`` is the smallest relative distance between the k-th and the
     (k+1)-th value of any ranking the step made (inf when there is none).
+    ``near_tie`` is the smallest relative distance between neighbours among
+    the first k+1 entries of any ranking the step made, leaving out
+    neighbours that are equal logits of one branch (every evaluation ranks
+    those by index): where it is tiny, an evaluation whose probabilities
+    differ from these by an ulp may order the entries otherwise.
     """
     dl = np.asarray(draft_logits)
     b, rows, _ = dl.shape
     tk2 = topk * topk
     out = []
+    def rel(a, c):
+        return (float(a) - float(c)) / float(a) if a > 0 else math.inf
+
     for r in range(b):
-        gap = math.inf
+        gap = near = math.inf
         pv = np.zeros((rows, topk), np.float32)
         pi = np.zeros((rows, topk), np.int64)
+        x = [widen(dl[r, j], dtype) for j in range(rows)]
         for j in range(rows):
             p = draft_probs(dl[r, j], dtype)
             vals, idx = topk_desc(p, topk + 1)
             pv[j], pi[j] = vals[:topk], idx[:topk]
             if vals.size > topk and vals[topk - 1] > 0:
-                gap = min(gap, (float(vals[topk - 1]) - float(vals[topk])) / float(vals[topk - 1]))
+                gap = min(gap, rel(vals[topk - 1], vals[topk]))
+            for t in range(vals.size - 1):
+                if x[j][idx[t]] != x[j][idx[t + 1]]:
+                    near = min(near, rel(vals[t], vals[t + 1]))
         if step == 0:
             res = dict(scores=pv[0].copy(), tokens=pi[0].copy(),
                        parents=np.arange(-1, topk, dtype=np.int64),
@@ -543,12 +555,17 @@ def draft_step(draft_logits, branch_scores, step, topk, num_steps, dtype):
             tokens = pi.reshape(-1)
             vals, cs = topk_desc(flat, topk + 1)
             if vals.size > topk and vals[topk - 1] > 0:
-                gap = min(gap, (float(vals[topk - 1]) - float(vals[topk])) / float(vals[topk - 1]))
+                gap = min(gap, rel(vals[topk - 1], vals[topk]))
+            for t in range(vals.size - 1):
+                j1, j2 = cs[t] // topk, cs[t + 1] // topk
+                if j1 != j2 or x[j1][tokens[cs[t]]] != x[j2][tokens[cs[t + 1]]]:
+                    near = min(near, rel(vals[t], vals[t + 1]))
             cs = cs[:topk]
             res = dict(scores=flat.copy(), tokens=tokens.copy(),
                        parents=cs + tk2 * (step - 1) + topk,
                        next_scores=flat[cs].copy(), next_tokens=tokens[cs].copy())
         res["gap"] = gap
+        res["near_tie"] = near
         out.append(res)
     off_s = 0 if step == 0 else topk + (step - 1) * tk2
     off_p = 0 if step == 0 else topk + 1 + (step - 1) * topk
@@ -557,7 +574,8 @@ def draft_step(draft_logits, branch_scores, step, topk, num_steps, dtype):
         parents=np.stack([o["parents"] for o in out]),
         next_scores=np.stack([o["next_scores"] for o in out]),
         next_tokens=np.stack([o["next_tokens"] for o in out]),
-        gap=np.array([o["gap"] for o in out]), score_offset=off_s, parent_offset=off_p,
+        gap=np.array([o["gap"] for o in out]),
+        near_tie=np.array([o["near_tie"] for o in out]), score_offset=off_s, parent_offset=off_p,
         write_parents=step < num_steps - 1)
 
 

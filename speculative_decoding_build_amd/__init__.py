@@ -48,6 +48,7 @@ EXPORTS = ("spec_version", "spec_status_string", "spec_mask_word_bytes", "spec_b
            "spec_verify_attention_workspace_size", "spec_verify_attention",
            "spec_accept_workspace_size", "spec_accept_greedy", "spec_accept_sample",
            "spec_accept_target_only_workspace_size", "spec_accept_target_only",
+           "spec_draft_step_workspace_size", "spec_draft_step",
            "spec_compact_kv")
 
 _P = ctypes.c_void_p
@@ -80,6 +81,8 @@ _decl("spec_accept_sample", _I, _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P
 _decl("spec_accept_target_only_workspace_size", _SZ, _I, _I, _I64)
 _decl("spec_accept_target_only", _I, _I, _I, _I, _I64, _I, _P, _P, _F, _F, _P, _P, _P, _P, _P,
       _P, _P, _P, _P, _P, _SZ, _P, _P)
+_decl("spec_draft_step_workspace_size", _SZ, _I, _I, _I64)
+_decl("spec_draft_step", _I, _I, _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P)
 _decl("spec_compact_kv", _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I64, _P, _I, _P, _P, _P,
       _P, _P, _P, _P, _P, _P)
 
@@ -313,6 +316,40 @@ def spec_accept_target_only(batch, num_draft_tokens, accept_width, vocab, dtype,
     ]
     _check("spec_accept_target_only", _lib.spec_accept_target_only(
         batch, n, accept_width, vocab, dtype, *args, _stream(stream)))
+
+
+def spec_draft_step_workspace_size(batch, topk, vocab) -> int:
+    return _lib.spec_draft_step_workspace_size(batch, topk, vocab)
+
+
+def spec_draft_step(batch, topk, num_steps, step, vocab, dtype, draft_logits, branch_scores,
+                    scores, tokens, parents, next_scores, next_tokens, workspace=None,
+                    workspace_bytes=None, dev_status=None, stream=None):
+    dev = _device()
+    rows = 1 if step == 0 else topk
+    ncand = topk + (num_steps - 1) * topk * topk
+    npar = 1 + (num_steps - 1) * topk
+    need_ws = spec_draft_step_workspace_size(batch, topk, vocab)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    none = batch == 0
+    args = [
+        _ptr(draft_logits, "draft_logits", dev, nbytes=batch * rows * vocab * _ELEM.get(dtype, 4),
+             optional=none),
+        _ptr(branch_scores, "branch_scores", dev, nbytes=batch * topk * 4,
+             optional=none or step == 0),
+        _ptr(scores, "scores", dev, nbytes=batch * ncand * 4, optional=none),
+        _ptr(tokens, "tokens", dev, nbytes=batch * ncand * 4, optional=none),
+        _ptr(parents, "parents", dev, nbytes=batch * npar * 4,
+             optional=none or step >= num_steps - 1),
+        _ptr(next_scores, "next_scores", dev, nbytes=batch * topk * 4, optional=none),
+        _ptr(next_tokens, "next_tokens", dev, nbytes=batch * topk * 4, optional=none),
+        _ptr(workspace, "workspace", dev, nbytes=need_ws, optional=batch == 0),
+        workspace_bytes,
+        _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
+    ]
+    _check("spec_draft_step", _lib.spec_draft_step(batch, topk, num_steps, step, vocab, dtype,
+                                                    *args, _stream(stream)))
 
 
 def spec_compact_kv(batch, num_draft_tokens, accept_width, num_layers, num_kv_heads, head_dim,

@@ -51,6 +51,9 @@ def test_host_only_queries():
     # one (max, sum) pair of 64-bit words per verify row and 8192-entry chunk
     assert S.spec_accept_target_only_workspace_size(1, 64, 128256) == 64 * 16 * 16
     assert S.spec_accept_target_only_workspace_size(0, 64, 128256) == 0
+    # per branch row and 8192-entry chunk: max, sum and up to 8 keys (80 bytes)
+    assert S.spec_draft_step_workspace_size(1, 8, 128256) == 8 * 16 * 80
+    assert S.spec_draft_step_workspace_size(0, 8, 128256) == 0
     # a single split needs no workspace; a long history does
     assert S.spec_verify_attention_workspace_size(2, 6, 2, 1, 64, 64, S.SPEC_F32) >= 0
     assert S.spec_verify_attention_workspace_size(4, 64, 64, 8, 128, 131072, S.SPEC_BF16) > 0
@@ -123,6 +126,24 @@ def test_host_errors_before_launch():
     assert to(1, 6, 4, 32, 0, fake, fake, 1.0, 1.0, *([fake] * 10), 8, P0, P0) == -5     # workspace small
     assert to(1, 99, 4, 32, 0, fake, fake, 1.0, 1.0, *([fake] * 10), big, P0, P0) == -4
     assert to(0, 6, 4, 32, 0, P0, P0, 1.0, 1.0, *([P0] * 10), 0, P0, P0) == 0
+    ds = lib.spec_draft_step
+    ds.restype = I
+    ds.argtypes = ([I, I, I, I, ctypes.c_int64, I] + [ctypes.c_void_p] * 8
+                   + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p])
+    f8 = [fake] * 8
+    assert ds(1, 4, 3, 3, 1000, 0, *f8, big, P0, P0) == -2          # step >= num_steps
+    assert ds(1, 4, 3, 1, 1000, 9, *f8, big, P0, P0) == -3
+    assert ds(1, 9, 3, 1, 1000, 0, *f8, big, P0, P0) == -4          # topk > 8
+    assert ds(1, 4, 3, 1, 3, 0, *f8, big, P0, P0) == -2             # vocab < topk
+    assert ds(1, 8, 3, 1, 1 << 20, 0, *f8, big, P0, P0) == -4       # 8 x 128 x 8 keys
+    nb = list(f8)
+    nb[1] = P0
+    assert ds(1, 4, 3, 1, 1000, 0, *nb, big, P0, P0) == -1          # branch scores at step 1
+    npr = list(f8)
+    npr[4] = P0
+    assert ds(1, 4, 3, 1, 1000, 0, *npr, big, P0, P0) == -1         # parents before the last step
+    assert ds(1, 4, 3, 1, 1000, 0, *f8, 8, P0, P0) == -5            # workspace small
+    assert ds(0, 4, 3, 1, 1000, 0, *([P0] * 8), 0, P0, P0) == 0
     ck = lib.spec_compact_kv
     ck.restype = I
     ck.argtypes = [I] * 8 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, I] + [ctypes.c_void_p] * 9 + [ctypes.c_void_p]

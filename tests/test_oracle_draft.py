@@ -68,10 +68,26 @@ def test_ties_take_the_lower_index():
     o = oracle.draft_step(logits, None, 0, 3, 2, "f32")
     assert o["tokens"][0].tolist() == [0, 1, 2]
     assert o["gap"][0] == 0.0
+    # equal logits of one branch rank by index on any evaluation: no near tie
+    assert o["near_tie"][0] == np.inf
     # equal products across branches: lower flat index first
     o1 = oracle.draft_step(np.zeros((1, 3, 10), np.float32), np.full((1, 3), 0.2, np.float32), 1,
                            3, 4, "f32")
     assert o1["parents"][0].tolist() == [3, 4, 5]          # flat 0, 1, 2 + 9*0 + 3
+    # ... but the 3rd and 4th products come from different branches: a tie
+    assert o1["near_tie"][0] == 0.0
+
+
+def test_near_tie_measures_neighbours():
+    # probabilities proportional to exp(logit): neighbours 3 and 2.5 differ by
+    # 1 - e^-0.5 relative, 2.5 and 2.5 - 1e-6 by ~1e-6, the last pair is past k+1
+    x = np.array([[[3.0, 2.5, 2.5 - 1e-6, 0.0, -5.0]]])
+    o = oracle.draft_step(x, None, 0, 2, 2, "f32")
+    assert o["tokens"][0].tolist() == [0, 1]
+    assert abs(o["gap"][0] - 1e-6) < 2e-7
+    assert abs(o["near_tie"][0] - 1e-6) < 2e-7
+    o = oracle.draft_step(x, None, 0, 1, 2, "f32")
+    assert abs(o["near_tie"][0] - (1 - np.exp(-0.5))) < 1e-6
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
