@@ -308,10 +308,13 @@ int spec_accept_target_only(int batch, int num_draft_tokens, int accept_width, i
  * entries of other steps are not touched.  Normalisers are sums of f32
  * exponentials in f64, so a p may differ from the exact f64 softmax by an
  * ulp and a ranking within ~1e-6 relative of a tie may differ from an
- * exact evaluation.  topk <= 8 and rows * ceil(vocab / 8192) * topk <= 4096
- * (vocab <= 524288 at topk 8), else SPEC_ERR_UNSUPPORTED; vocab >= topk.
- * workspace: spec_draft_step_workspace_size(batch, topk, vocab) bytes,
- *   8-byte aligned, any contents (80 bytes per row and 8192-entry chunk).
+ * exact evaluation.  topk <= 8 (else SPEC_ERR_UNSUPPORTED), vocab >= topk
+ * (else SPEC_ERR_SHAPE), rows * ceil(vocab / 8192) <= 2048 (vocab <=
+ * 2097152 at a later step of topk 8; else SPEC_ERR_UNSUPPORTED).
+ * workspace: spec_draft_step_workspace_size(batch, topk, vocab) bytes (80
+ *   bytes per branch row and 2048-entry chunk), 8-byte aligned, any
+ *   contents; calls in stream order may share one (concurrent calls need
+ *   one each).  Two kernels are launched on `stream`.
  */
 size_t spec_draft_step_workspace_size(int batch, int topk, int64_t vocab);
 int spec_draft_step(int batch, int topk, int num_steps, int step, int64_t vocab, int dtype,

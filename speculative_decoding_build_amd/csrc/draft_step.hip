@@ -15,24 +15,37 @@
 // last step's parent block is not part of the list).  Ties rank the lower
 // index first.
 //
-// Launch 1, one workgroup per (branch row, 8192-entry chunk): the chunk's
-// max, its float64 sum of exponentials (float32 base-2 exponentials of the
-// argument carried as a float pair) and its top-k entries as 64-bit order
-// keys (the logit's order-preserving bits, then the complemented index: a
-// larger key is a larger logit, or the lower index of equal logits; logit
-// order is probability order).  Launch 2, one workgroup per request: each
-// row's max and normaliser from its chunks, its top-k by rank among the
-// chunks' keys, the probabilities of those entries (float64 exponential,
-// rounded to float32), then the step's products and selection.
+// Two launches.  In the first, each workgroup takes one (branch row,
+// chunk) item, a chunk being 2048 or 8192 vocabulary entries (the smaller
+// when the grid would otherwise leave most of the device idle), and writes
+// the chunk's max, its float64 sum of exponentials (float32 base-2
+// exponentials of the argument carried as a float pair) and its top-k
+// entries as 64-bit order keys (the logit's order-preserving bits, then the
+// complemented index: a larger key is a larger logit, or the lower index of
+// equal logits; logit order is probability order).  The top-k needs no
+// per-element sort: with tau the k-th largest of the threads' maxima, only
+// the k threads whose maximum reaches tau can hold entries >= tau, and
+// every top-k entry is >= tau, so the at most k x (entries per thread)
+// candidates >= tau are ranked among themselves.  In the second launch one
+// workgroup per request merges the request's chunks the same way (per row,
+// tau = the k-th largest chunk best: at most k x k candidates), forms each
+// row's max and normaliser, the probabilities of the kept entries (float64
+// exponential, rounded to float32), then the step's products and selection.
 #include "sweep_common.h"
 
 using namespace spec;
 
 namespace {
 
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / SPEC_WAVE;
 constexpr int kMaxK = 8;                   // topk at most
-constexpr int kItemWords = 2 + kMaxK;      // per chunk item: max, sum, keys
-constexpr int kMaxKeys = 4096;             // rows x chunks x topk a request merges in LDS
+constexpr int kItemWords = 2 + kMaxK;      // per chunk item: max, sum, keys (descending)
+constexpr int kMergePer = 8;               // chunk items per merge thread, separate launch
+constexpr int kMergeChunks = kMergePer * kThreads;   // rows x chunks of one request
+constexpr int kSmallE = 8;                 // entries per thread of a 2048-entry chunk
+constexpr int kLargeE = 32;                // ... of an 8192-entry chunk
+constexpr int64_t kSmallGrid = 2048;       // largest grid of 2048-entry chunks
 
 __device__ __forceinline__ uint64_t order_key(float v, int64_t i) {
     uint32_t bits = __float_as_uint(v == 0.f ? 0.f : v);
@@ -50,189 +63,200 @@ __device__ __forceinline__ int key_index(uint64_t k) {
     return (int)(0xFFFFFFFFu - (uint32_t)k);
 }
 
+__device__ __forceinline__ void put(uint64_t *p, uint64_t v) { *p = v; }
+
 struct DraftArgs {
     const void *logits;                    // [batch][rows][vocab]
     int64_t vocab;
     bool vec_ok;
-    int batch, topk, num_steps, step, rows, nchunks;
+    int batch, topk, num_steps, step, rows, nchunks, ncand, npar;
     const float *branch_scores;            // [batch][topk] (step >= 1)
     float *scores;                         // [batch][ncand]
     int32_t *tokens;                       // [batch][ncand]
     int32_t *parents;                      // [batch][npar]
     float *next_scores;                    // [batch][topk]
     int32_t *next_tokens;                  // [batch][topk]
-    int ncand, npar;
-    uint64_t *items;                       // [batch * rows * nchunks][kItemWords]
+    uint64_t *items;                       // [batch][rows][nchunks][kItemWords]
     int32_t *status;
 };
 
-// insert key k into the descending list t (largest first), keeping K entries
-template <int K>
-__device__ __forceinline__ void insert_desc(uint64_t (&t)[K], uint64_t k) {
-    if (k <= t[K - 1]) return;
-    t[K - 1] = k;
+// Element e of thread tid sits at start + (e / 8) * 2048 + tid * 8 + e % 8:
+// each 8-group is one 16-byte load (bf16), a wave reads 1 KB contiguous.
+__device__ __forceinline__ int64_t elem_at(int64_t start, int tid, int e) {
+    return start + (int64_t)(e / 8) * kThreads * 8 + tid * 8 + (e % 8);
+}
+
+template <int DT, int E>
+__device__ __forceinline__ void load_elems(const void *base, int64_t start, int64_t end,
+                                           bool vec_ok, int tid, float (&x)[E]) {
 #pragma unroll
-    for (int j = K - 1; j > 0; --j) {
-        if (t[j] > t[j - 1]) {
-            const uint64_t x = t[j];
-            t[j] = t[j - 1];
-            t[j - 1] = x;
+    for (int g = 0; g < E / 8; ++g) {
+        const int64_t e0 = elem_at(start, tid, g * 8);
+        if (DT == SPEC_BF16) {
+            const uint16_t *p = static_cast<const uint16_t *>(base);
+            if (vec_ok && e0 + 8 <= end) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(p + e0);
+                x[g * 8 + 0] = lo_bf16(w.x);
+                x[g * 8 + 1] = hi_bf16(w.x);
+                x[g * 8 + 2] = lo_bf16(w.y);
+                x[g * 8 + 3] = hi_bf16(w.y);
+                x[g * 8 + 4] = lo_bf16(w.z);
+                x[g * 8 + 5] = hi_bf16(w.z);
+                x[g * 8 + 6] = lo_bf16(w.w);
+                x[g * 8 + 7] = hi_bf16(w.w);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    x[g * 8 + j] = (e0 + j < end) ? bf16_to_f32(p[e0 + j]) : -INFINITY;
+            }
+        } else {
+            const float *p = static_cast<const float *>(base);
+            if (vec_ok && e0 + 8 <= end) {
+                const float4 a = *reinterpret_cast<const float4 *>(p + e0);
+                const float4 b = *reinterpret_cast<const float4 *>(p + e0 + 4);
+                x[g * 8 + 0] = a.x; x[g * 8 + 1] = a.y; x[g * 8 + 2] = a.z; x[g * 8 + 3] = a.w;
+                x[g * 8 + 4] = b.x; x[g * 8 + 5] = b.y; x[g * 8 + 6] = b.z; x[g * 8 + 7] = b.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[g * 8 + j] = (e0 + j < end) ? p[e0 + j] : -INFINITY;
+            }
         }
     }
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+constexpr int kRegPer = 2;                 // chunk items per merge thread with keys in registers
+constexpr int kRegChunks = kRegPer * kThreads;
+
+struct ChunkShared {
+    uint64_t tkey[kThreads];               // thread maxima
+    uint64_t cand[kThreads];               // candidates (at most k x E <= 256)
+    uint64_t wtop[kWaves][kMaxK];          // each wave's top-k thread maxima
+    double dred[kWaves];
+    uint64_t tau, best;
+    int nc;
+};
+
+template <int CAP>
+struct MergeShared {
+    uint64_t bk[CAP];                      // chunk bests (their values: the chunk maxima)
+    double cs[CAP];                        // chunk sums
+    uint64_t rc[kMaxK][kMaxK * kMaxK];     // each row's candidates
+    uint64_t sel[kMaxK][kMaxK];            // each row's top-k keys by rank
+    uint64_t rtau[kMaxK];
+    double Z[kMaxK];                       // each row's normaliser
+    float M[kMaxK];                        // each row's max
+    float ex[SPEC_WAVE];                   // the step's products
+    float bs[SPEC_WAVE];                   // their branch scores
+    int rn[kMaxK];
+};
+
+// Number of entries of u[0, n) greater than `mine` (LDS, 8 reads in flight).
+__device__ __forceinline__ int count_greater(const uint64_t *u, int n, uint64_t mine) {
+    int c = 0, i = 0;
+    for (; i + 8 <= n; i += 8) {
+        uint64_t v[8];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t w = __shfl_xor(v, o, SPEC_WAVE);
-        v = w > v ? w : v;
+        for (int k = 0; k < 8; ++k) v[k] = u[i + k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c += v[k] > mine;
     }
-    return v;
+    for (; i < n; ++i) c += u[i] > mine;
+    return c;
 }
 
-// KT >= topk: the per-thread and per-wave lists hold KT keys
-template <int DT, int KT>
-__global__ __launch_bounds__(kSweepThreads) void draft_chunk_kernel(DraftArgs A) {
-    __shared__ float s_f[kSweepThreads / SPEC_WAVE];
-    __shared__ double s_d[kSweepThreads / SPEC_WAVE];
-    __shared__ uint64_t s_k[kSweepThreads / SPEC_WAVE][KT];
+// One (branch row, chunk) item: max, sum and top-k keys into its slot.
+template <int DT, int E>
+__device__ void chunk_item(const DraftArgs &A, ChunkShared &S, int64_t t) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t t = blockIdx.x;
-    const int64_t row = t / A.nchunks;     // (request, branch) row
-    const int64_t start = (t % A.nchunks) * kChunk;
-    const int64_t end = min(A.vocab, start + kChunk);
-    const char *rowp = static_cast<const char *>(A.logits) + row * A.vocab * (DT == SPEC_BF16 ? 2 : 4);
-    float x[kPerThread];
-    load_chunk<DT>(rowp, start, end, A.vec_ok, tid, x);
-    // max
-    float m = -INFINITY;
+    const int K = A.topk;
+    const int64_t row = t / A.nchunks;     // request * rows + branch
+    const int64_t start = (t % A.nchunks) * (int64_t)(kThreads * E);
+    const int64_t end = min(A.vocab, start + kThreads * E);
+    float x[E];
+    load_elems<DT, E>(static_cast<const char *>(A.logits) + row * A.vocab * (DT == SPEC_BF16 ? 2 : 4),
+                      start, end, A.vec_ok, tid, x);
+    // this thread's largest key: its max value at its lowest index (0: no entry)
+    float vm = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) m = fmaxf(m, x[e]);
+    for (int e = 0; e < E; ++e) vm = fmaxf(vm, x[e]);
+    int first = -1;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, SPEC_WAVE));
-    if (lane == 0) s_f[wave] = m;
+    for (int e = E - 1; e >= 0; --e)
+        if (elem_at(start, tid, e) < end && x[e] == vm) first = e;
+    const uint64_t mk = first >= 0 ? order_key(vm, elem_at(start, tid, first)) : 0;
+    S.tkey[tid] = mk;
+    if (tid < kWaves * kMaxK) S.wtop[tid / kMaxK][tid % kMaxK] = 0;
+    if (tid == 0) {
+        S.nc = 0;
+        S.tau = 1;                         // every entry, until a k-th thread maximum exists
+    }
     __syncthreads();
-    m = s_f[0];
+    // the wave's top-k thread maxima, then the block's among those
+    const int wr = count_greater(S.tkey + wave * SPEC_WAVE, SPEC_WAVE, mk);
+    const bool wtop = mk != 0 && wr < K;
+    if (wtop) S.wtop[wave][wr] = mk;
+    __syncthreads();
+    if (wtop) {
+        const int br = count_greater(&S.wtop[0][0], kWaves * kMaxK, mk);
+        if (br == 0) S.best = mk;
+        if (br == K - 1) S.tau = mk;
+    }
+    __syncthreads();
+    const uint64_t tau = S.tau;
+    const float m = key_value(S.best);
+    if (mk >= tau) {
+        // only the k threads whose maximum reaches tau hold candidates
 #pragma unroll
-    for (int w = 1; w < kSweepThreads / SPEC_WAVE; ++w) m = fmaxf(m, s_f[w]);
-    // sum of exponentials, and this thread's top-k keys
-    const Scale2 sc = make_scale2(m, 1.0f);
+        for (int e = 0; e < E; ++e) {
+            const int64_t idx = elem_at(start, tid, e);
+            const uint64_t k = idx < end ? order_key(x[e], idx) : 0;
+            if (k >= tau) S.cand[atomicAdd(&S.nc, 1)] = k;
+        }
+    }
     double s = 0.0;
-    uint64_t top[KT];
+    if (m != -INFINITY) {
+        const Scale2 scl = make_scale2(m, 1.0f);
 #pragma unroll
-    for (int j = 0; j < KT; ++j) top[j] = 0;
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-        const int64_t idx = elem_index(start, tid, e);
-        if (idx < end) {
-            if (m != -INFINITY) s += (double)exp2_scaled(x[e], sc);
-            insert_desc<KT>(top, order_key(x[e], idx));
-        }
+        for (int e = 0; e < E; ++e) s += (double)exp2_scaled(x[e], scl);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, SPEC_WAVE);
-    if (lane == 0) s_d[wave] = s;
-    // the wave's top-k: k rounds of a wave max over the lists' heads
-#pragma unroll
-    for (int r = 0; r < KT; ++r) {
-        const uint64_t best = wave_max_u64(top[0]);
-        if (best != 0 && top[0] == best) {
-#pragma unroll
-            for (int j = 0; j < KT - 1; ++j) top[j] = top[j + 1];
-            top[KT - 1] = 0;
-        }
-        if (lane == 0) s_k[wave][r] = best;
-    }
+    s = wave_sum_d(s);
+    if (lane == 0) S.dred[wave] = s;
     __syncthreads();
-    if (wave == 0) {
-        // rank of each of the block's 4 x KT keys among them; the chunk
-        // keeps the first topk
-        constexpr int NK = (kSweepThreads / SPEC_WAVE) * KT;
-        const uint64_t mine = lane < NK ? s_k[lane / KT][lane % KT] : 0;
-        int rank = 0;
-        for (int q = 0; q < NK; ++q) rank += s_k[q / KT][q % KT] > mine;
-        uint64_t *it = A.items + t * kItemWords;
-        if (lane == 0) {
-            double sum = 0.0;
+    const int nc = S.nc;
+    uint64_t *it = A.items + t * kItemWords;
+    if (tid < nc) {
+        const uint64_t mine = S.cand[tid];
+        const int rank = count_greater(S.cand, nc, mine);
+        if (rank < K) put(it + 2 + rank, mine);
+    }
+    if (tid >= nc && tid < K) put(it + 2 + tid, 0);      // a chunk with fewer than k entries
+    if (tid == 0) {
+        double sum = 0.0;
 #pragma unroll
-            for (int w = 0; w < kSweepThreads / SPEC_WAVE; ++w) sum += s_d[w];
-            it[0] = (uint64_t)__float_as_uint(m);
-            it[1] = __builtin_bit_cast(uint64_t, sum);
-        }
-        if (lane < NK && mine != 0 && rank < A.topk) it[2 + rank] = mine;
-        // empty entries (a chunk with fewer than topk entries) read as 0
-        if (lane < A.topk) {
-            int filled = 0;
-            for (int q = 0; q < NK; ++q) filled += s_k[q / KT][q % KT] != 0;
-            if (lane >= filled) it[2 + lane] = 0;
-        }
+        for (int w = 0; w < kWaves; ++w) sum += S.dred[w];
+        put(it, (uint64_t)__float_as_uint(m));
+        put(it + 1, __builtin_bit_cast(uint64_t, sum));
     }
 }
 
-__global__ __launch_bounds__(kSweepThreads) void draft_select_kernel(DraftArgs A) {
-    __shared__ uint64_t s_keys[kMaxKeys];
-    __shared__ float s_M[kMaxK];
-    __shared__ double s_Z[kMaxK];
-    __shared__ uint64_t s_sel[kMaxK][kMaxK];   // [row][rank]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = blockIdx.x;
-    const int K = A.topk, rows = A.rows, nch = A.nchunks;
-    const int per_row = nch * K;               // keys of one row
-    // every row's chunk keys into LDS (chunk c's keys c*K .. c*K+K-1)
-    const uint64_t *items = A.items + (int64_t)r * rows * nch * kItemWords;
-    for (int q = tid; q < rows * per_row; q += blockDim.x) {
-        const int j = q / per_row, rest = q % per_row;
-        s_keys[q] = items[((int64_t)j * nch + rest / K) * kItemWords + 2 + rest % K];
-    }
-    // each row's max and normaliser: a wave per row
-    for (int j = wave; j < rows; j += kSweepThreads / SPEC_WAVE) {
-        float m = -INFINITY;
-        for (int c = lane; c < nch; c += SPEC_WAVE)
-            m = fmaxf(m, __uint_as_float((uint32_t)items[((int64_t)j * nch + c) * kItemWords]));
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, SPEC_WAVE));
-        const Scale2 sc = make_scale2(m, 1.0f);
-        double z = 0.0;
-        for (int c = lane; c < nch; c += SPEC_WAVE) {
-            const uint64_t *it = items + ((int64_t)j * nch + c) * kItemWords;
-            const float mc = __uint_as_float((uint32_t)it[0]);
-            if (mc != -INFINITY) z += __builtin_bit_cast(double, it[1]) * (double)exp2_scaled(mc, sc);
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, SPEC_WAVE);
-        if (lane == 0) {
-            s_M[j] = m;
-            s_Z[j] = z;
-        }
-    }
-    __syncthreads();
-    // each row's top-k: rank of every key among its row's keys
-    for (int q = tid; q < rows * per_row; q += blockDim.x) {
-        const uint64_t mine = s_keys[q];
-        if (mine == 0) continue;
-        const int j = q / per_row;
-        const uint64_t *rk = s_keys + j * per_row;
-        int rank = 0;
-        for (int u = 0; u < per_row; ++u) rank += rk[u] > mine;
-        if (rank < K) s_sel[j][rank] = mine;
-    }
-    __syncthreads();
-    if (wave != 0) return;
+// The step's outputs for request r from S.M, S.Z, S.sel (wave 0).
+template <int CAP>
+__device__ void finish_request(const DraftArgs &A, MergeShared<CAP> &S, int r, int err, float bsv) {
+    const int lane = threadIdx.x & 63;
+    const int K = A.topk, R = A.rows;
     // probabilities of the selected entries (lane = row * K + rank)
-    const int nsel = rows * K;
-    int err = 0;
     float p = 0.f;
     int tok = -1;
-    if (lane < nsel) {
+    if (lane < R * K) {
         const int j = lane / K, k = lane % K;
-        const uint64_t key = s_sel[j][k];
+        const uint64_t key = S.sel[j][k];
         tok = key_index(key);
         if (tok < 0 || tok >= A.vocab) {
             err |= SPEC_ST_RANGE;
             tok = 0;
         }
-        const double z = s_Z[j];
-        const double e = exp((double)key_value(key) - (double)s_M[j]);
+        const double z = S.Z[j];
+        const double e = exp((double)key_value(key) - (double)S.M[j]);
         p = z > 0.0 ? (float)(e / z) : 0.f;
     }
     const int K2 = K * K;
@@ -253,14 +277,13 @@ __global__ __launch_bounds__(kSweepThreads) void draft_select_kernel(DraftArgs A
         const int off = K + (A.step - 1) * K2;
         float ex = 0.f;
         if (lane < K2) {
-            ex = A.branch_scores[(int64_t)r * K + lane / K] * p;
+            ex = bsv * p;
             sc[off + lane] = ex;
             tk[off + lane] = tok;
         }
-        __builtin_amdgcn_wave_barrier();
         int rank = 0;
         for (int u = 0; u < K2; ++u) {
-            const float o = __shfl(ex, u, SPEC_WAVE);
+            const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), u));
             rank += (o > ex) || (o == ex && u < lane);
         }
         if (lane < K2 && rank < K) {
@@ -270,28 +293,156 @@ __global__ __launch_bounds__(kSweepThreads) void draft_select_kernel(DraftArgs A
                 pa[K + 1 + (A.step - 1) * K + rank] = lane + K2 * (A.step - 1) + K;
         }
     }
+#pragma unroll
     for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, SPEC_WAVE);
     if (lane == 0) raise_status(A.status, err);
 }
 
+// Request r's chunk items (rows x chunks, at most CAP of them) -> each
+// row's max, normaliser and top-k keys; then the step's outputs.  REG: at
+// most kRegPer items per thread, whose keys stay in registers; otherwise
+// the candidate chunks' keys are read again.
+template <int CAP, bool REG>
+__device__ void merge_request(const DraftArgs &A, MergeShared<CAP> &S, int r) {
+    constexpr int P = kRegPer;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = A.topk, R = A.rows, nch = A.nchunks, nq = R * nch, nw = 2 + K;
+    const uint64_t *items = A.items + (int64_t)r * nq * kItemWords;
+    float bsv = 0.f;
+    if (wave == 0 && A.step > 0 && lane < K * K) bsv = A.branch_scores[(int64_t)r * K + lane / K];
+    uint64_t w[P][kItemWords];
+    for (int q0 = 0; q0 < nq; q0 += P * kThreads) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int q = q0 + tid + i * kThreads;
+#pragma unroll
+            for (int u = 0; u < kItemWords; ++u)
+                w[i][u] = (q < nq && u < nw) ? items[(int64_t)q * kItemWords + u] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int q = q0 + tid + i * kThreads;
+            if (q < nq) {
+                S.cs[q] = __builtin_bit_cast(double, w[i][1]);
+                S.bk[q] = w[i][2];
+            }
+        }
+        if (REG) break;
+    }
+    if (tid < R) {
+        S.rn[tid] = 0;
+        S.rtau[tid] = 1;                   // every nonzero key, until a k-th chunk best exists
+    }
+    if (wave == 0) S.bs[lane] = bsv;
+    __syncthreads();
+    // each row's max (its largest chunk best) and tau (its k-th largest)
+    for (int q = tid; q < nq; q += kThreads) {
+        const int j = q / nch;
+        const uint64_t mine = S.bk[q];
+        const int rank = count_greater(S.bk + j * nch, nch, mine);
+        if (rank == 0) S.M[j] = key_value(mine);
+        if (rank == K - 1) S.rtau[j] = mine;
+    }
+    __syncthreads();
+    // each row's normaliser (a wave per row)
+    for (int j = wave; j < R; j += kWaves) {
+        const Scale2 scl = make_scale2(S.M[j], 1.0f);
+        double z = 0.0;
+        for (int c = lane; c < nch; c += SPEC_WAVE) {
+            const float mc = key_value(S.bk[j * nch + c]);
+            if (mc != -INFINITY) z += S.cs[j * nch + c] * (double)exp2_scaled(mc, scl);
+        }
+        z = wave_sum_d(z);
+        if (lane == 0) S.Z[j] = z;
+    }
+    // candidates: the keys >= tau of the chunks whose best reaches tau (at
+    // most k chunks of a row, k keys each)
+    if (REG) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int q = tid + i * kThreads;
+            if (q < nq) {
+                const int j = q / nch;
+                const uint64_t tau = S.rtau[j];
+                if (w[i][2] >= tau) {
+#pragma unroll
+                    for (int u = 2; u < kItemWords; ++u)
+                        if (u < nw && w[i][u] != 0 && w[i][u] >= tau)
+                            S.rc[j][atomicAdd(&S.rn[j], 1)] = w[i][u];
+                }
+            }
+        }
+    } else {
+        for (int q = tid; q < nq; q += kThreads) {
+            const int j = q / nch;
+            const uint64_t tau = S.rtau[j];
+            const uint64_t *it = items + (int64_t)q * kItemWords;
+            if (S.bk[q] >= tau) {
+                for (int u = 2; u < nw; ++u) {
+                    const uint64_t key = it[u];
+                    if (key != 0 && key >= tau) S.rc[j][atomicAdd(&S.rn[j], 1)] = key;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (int q = tid; q < R * kMaxK * kMaxK; q += kThreads) {
+        const int j = q / (kMaxK * kMaxK), c = q % (kMaxK * kMaxK);
+        const int n = S.rn[j];
+        if (c < n) {
+            const uint64_t mine = S.rc[j][c];
+            const int rank = count_greater(S.rc[j], n, mine);
+            if (rank < K) S.sel[j][rank] = mine;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) finish_request<CAP>(A, S, r, 0, S.bs[lane]);
+}
+
+template <int DT, int E>
+__global__ __launch_bounds__(kThreads) void draft_chunk_kernel(DraftArgs A) {
+    __shared__ ChunkShared S;
+    chunk_item<DT, E>(A, S, blockIdx.x);
+}
+
+template <int CAP, bool REG>
+__global__ __launch_bounds__(kThreads) void draft_merge_kernel(DraftArgs A) {
+    __shared__ MergeShared<CAP> S;
+    merge_request<CAP, REG>(A, S, blockIdx.x);
+}
+
+int64_t small_chunks(int64_t vocab) { return (vocab + kThreads * kSmallE - 1) / (kThreads * kSmallE); }
+
+int chunk_entries(int batch, int rows, int64_t vocab) {
+    const int64_t small = small_chunks(vocab);
+    if ((int64_t)batch * rows * small <= kSmallGrid && rows * small <= kRegChunks)
+        return kThreads * kSmallE;
+    return kThreads * kLargeE;
+}
+
+size_t items_bytes(int batch, int topk, int64_t vocab) {
+    return spec::align_up((size_t)batch * topk * small_chunks(vocab) * kItemWords * 8, 256);
+}
+
 template <int DT>
-void launch_chunks(const DraftArgs &A, int64_t items, hipStream_t st) {
-    const dim3 g((unsigned)items), b(kSweepThreads);
-    if (A.topk == 1)
-        hipLaunchKernelGGL((draft_chunk_kernel<DT, 1>), g, b, 0, st, A);
-    else if (A.topk == 2)
-        hipLaunchKernelGGL((draft_chunk_kernel<DT, 2>), g, b, 0, st, A);
-    else if (A.topk <= 4)
-        hipLaunchKernelGGL((draft_chunk_kernel<DT, 4>), g, b, 0, st, A);
+void launch(const DraftArgs &A, int64_t items, int chunk, hipStream_t st) {
+    const dim3 b(kThreads);
+    if (chunk == kThreads * kSmallE)
+        hipLaunchKernelGGL((draft_chunk_kernel<DT, kSmallE>), dim3((unsigned)items), b, 0, st, A);
     else
-        hipLaunchKernelGGL((draft_chunk_kernel<DT, kMaxK>), g, b, 0, st, A);
+        hipLaunchKernelGGL((draft_chunk_kernel<DT, kLargeE>), dim3((unsigned)items), b, 0, st, A);
+    if (A.rows * A.nchunks <= kRegChunks)
+        hipLaunchKernelGGL((draft_merge_kernel<kRegChunks, true>), dim3((unsigned)A.batch), b, 0, st, A);
+    else
+        hipLaunchKernelGGL((draft_merge_kernel<kMergeChunks, false>), dim3((unsigned)A.batch), b, 0, st,
+                           A);
 }
 
 }  // namespace
 
 extern "C" size_t spec_draft_step_workspace_size(int batch, int topk, int64_t vocab) {
     if (batch <= 0 || topk <= 0 || vocab <= 0) return 0;
-    return spec::align_up((size_t)batch * topk * num_chunks(vocab) * kItemWords * sizeof(uint64_t), 256);
+    return items_bytes(batch, topk, vocab);
 }
 
 extern "C" int spec_draft_step(int batch, int topk, int num_steps, int step, int64_t vocab,
@@ -305,14 +456,15 @@ extern "C" int spec_draft_step(int batch, int topk, int num_steps, int step, int
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
     if (vocab < topk) return SPEC_ERR_SHAPE;
     const int rows = step == 0 ? 1 : topk;
-    const int nch = num_chunks(vocab);
-    if (topk > kMaxK || vocab > INT_MAX || (int64_t)rows * nch * topk > kMaxKeys)
-        return SPEC_ERR_UNSUPPORTED;
+    if (topk > kMaxK || vocab > INT_MAX) return SPEC_ERR_UNSUPPORTED;
+    const int chunk = chunk_entries(batch < 1 ? 1 : batch, rows, vocab);
+    const int64_t nch = (vocab + chunk - 1) / chunk;
+    if (rows * nch > kMergeChunks) return SPEC_ERR_UNSUPPORTED;
     if (batch == 0) return SPEC_OK;
     if (!draft_logits || !scores || !tokens || !next_scores || !next_tokens) return SPEC_ERR_NULL;
     if (step > 0 && !branch_scores) return SPEC_ERR_NULL;
     if (num_steps > 1 && step < num_steps - 1 && !parents) return SPEC_ERR_NULL;
-    if (!workspace || workspace_bytes < spec_draft_step_workspace_size(batch, topk, vocab) ||
+    if (!workspace || workspace_bytes < items_bytes(batch, topk, vocab) ||
         reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
         return SPEC_ERR_WORKSPACE;
     const int64_t items = (int64_t)batch * rows * nch;
@@ -327,22 +479,21 @@ extern "C" int spec_draft_step(int batch, int topk, int num_steps, int step, int
     A.num_steps = num_steps;
     A.step = step;
     A.rows = rows;
-    A.nchunks = nch;
+    A.nchunks = (int)nch;
+    A.ncand = topk + (num_steps - 1) * topk * topk;
+    A.npar = 1 + (num_steps - 1) * topk;
     A.branch_scores = branch_scores;
     A.scores = scores;
     A.tokens = tokens;
     A.parents = parents;
     A.next_scores = next_scores;
     A.next_tokens = next_tokens;
-    A.ncand = topk + (num_steps - 1) * topk * topk;
-    A.npar = 1 + (num_steps - 1) * topk;
     A.items = static_cast<uint64_t *>(workspace);
     A.status = dev_status;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (dtype == SPEC_BF16)
-        launch_chunks<SPEC_BF16>(A, items, st);
+        launch<SPEC_BF16>(A, items, chunk, st);
     else
-        launch_chunks<SPEC_F32>(A, items, st);
-    hipLaunchKernelGGL(draft_select_kernel, dim3(batch), dim3(kSweepThreads), 0, st, A);
+        launch<SPEC_F32>(A, items, chunk, st);
     return spec::launch_status();
 }

@@ -51,8 +51,9 @@ def test_host_only_queries():
     # one (max, sum) pair of 64-bit words per verify row and 8192-entry chunk
     assert S.spec_accept_target_only_workspace_size(1, 64, 128256) == 64 * 16 * 16
     assert S.spec_accept_target_only_workspace_size(0, 64, 128256) == 0
-    # per branch row and 8192-entry chunk: max, sum and up to 8 keys (80 bytes)
-    assert S.spec_draft_step_workspace_size(1, 8, 128256) == 8 * 16 * 80
+    # 80 bytes (max, sum, up to 8 keys) per branch row and 2048-entry chunk,
+    # rounded up to 256 bytes
+    assert S.spec_draft_step_workspace_size(1, 8, 128256) == -(-8 * 63 * 80 // 256) * 256
     assert S.spec_draft_step_workspace_size(0, 8, 128256) == 0
     # a single split needs no workspace; a long history does
     assert S.spec_verify_attention_workspace_size(2, 6, 2, 1, 64, 64, S.SPEC_F32) >= 0
@@ -135,7 +136,7 @@ def test_host_errors_before_launch():
     assert ds(1, 4, 3, 1, 1000, 9, *f8, big, P0, P0) == -3
     assert ds(1, 9, 3, 1, 1000, 0, *f8, big, P0, P0) == -4          # topk > 8
     assert ds(1, 4, 3, 1, 3, 0, *f8, big, P0, P0) == -2             # vocab < topk
-    assert ds(1, 8, 3, 1, 1 << 20, 0, *f8, big, P0, P0) == -4       # 8 x 128 x 8 keys
+    assert ds(1, 8, 3, 1, (1 << 21) + 1, 0, *f8, big, P0, P0) == -4  # 8 rows x 257 chunks
     nb = list(f8)
     nb[1] = P0
     assert ds(1, 4, 3, 1, 1000, 0, *nb, big, P0, P0) == -1          # branch scores at step 1

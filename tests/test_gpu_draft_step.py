@@ -6,9 +6,12 @@ oracle's branch scores), so each call is compared on identical inputs; a
 chained run then feeds the kernel its own outputs, in place, and compares
 the finished lists.  Cases: the tiny float32 workload, shrunken copies of the
 four bf16 workloads with several 8192-entry chunks and a ragged tail, a
-vocabulary of exactly topk entries, one chunk, the largest vocabulary topk 8
-supports, float32 over 50000 entries, and the four full-size workloads
-(sampled requests).
+vocabulary of exactly topk entries, 8192 entries, the largest vocabularies
+of the one-launch and the two-launch forms, float32 over 50000 entries, the
+four full-size workloads and more requests than one launch merges (sampled
+requests, whole batch in one call).  The kernel picks 2048-entry chunks for
+small grids and 8192-entry chunks for large ones; the cases cover both, and
+chunks holding fewer than topk entries.
 
 Bar: tokens, parents and next tokens bit-exact, scores and next scores
 within 1e-6 relative, entries outside the step's blocks untouched; requests
@@ -47,7 +50,7 @@ CASES = {
     "chain_b64_v40000": W.shrink(W.CONFIGS[4], hist=H8, vocab=40000),
     "c5_b2_v16385": W.shrink(W.CONFIGS[5], batch=2, hist=H8, vocab=16385),
     "vocab_eq_topk": W.shrink(W.CONFIGS[2], batch=2, hist=H8, vocab=8),
-    "one_chunk": W.shrink(W.CONFIGS[3], batch=3, hist=H8, vocab=8192),
+    "v8192": W.shrink(W.CONFIGS[3], batch=3, hist=H8, vocab=8192),
     "f32_v50000": W.shrink(W.CONFIGS[1], batch=3, vocab=50000),
 }
 
@@ -66,8 +69,9 @@ def _sentinel_lists(b, cfg):
 
 def _call(cfg, b, step, rows, bs, sc, tk, pa, ns, nt, ws=None):
     if ws is None:
-        ws = torch.empty(max(1, S.spec_draft_step_workspace_size(b, cfg.topk, cfg.vocab)),
-                         dtype=torch.uint8, device="cuda")
+        # any contents: start from a non-zero pattern
+        ws = torch.full((max(1, S.spec_draft_step_workspace_size(b, cfg.topk, cfg.vocab)),), 0xA5,
+                        dtype=torch.uint8, device="cuda")
     st = G.status()
     S.spec_draft_step(b, cfg.topk, cfg.num_steps, step, cfg.vocab, G.dtype_code(cfg),
                       G.dev(rows), bs, sc, tk, pa, ns, nt, workspace=ws, dev_status=st)
@@ -132,29 +136,49 @@ def test_draft_step_cases(name):
 
 
 def test_draft_step_largest_vocabulary():
-    # topk 8: 8 branch rows x 64 chunks x 8 keys fill the 4096 keys one
-    # request merges; two steps suffice to cover both forms
-    cfg = W.shrink(W.CONFIGS[2], hist=H8, vocab=524288)
-    w = W.make_workload(cfg, 52, attention=False)
-    say(f"[draft-step] largest vocabulary V={cfg.vocab}")
-    _stepwise(cfg, w, np.arange(1), "v524288", steps=2)
-    sc, tk, pa = _sentinel_lists(1, cfg)
-    ws = torch.empty(S.spec_draft_step_workspace_size(1, 8, cfg.vocab + 1), dtype=torch.uint8,
-                     device="cuda")
+    # step 0 over 1048576 entries: one row of 512 chunks of 2048, the most
+    # one launch merges; then a later step over 2097152 entries: 8 branch
+    # rows of 256 chunks of 8192, the most a separate merge launch takes
+    # (one more entry is refused)
+    say("[draft-step] largest vocabulary")
+    for V, step in ((1048576, 0), (2097152, 1)):
+        cfg = W.shrink(W.CONFIGS[2], hist=H8, vocab=V)
+        rng = np.random.default_rng(52 + step)
+        nrows = 1 if step == 0 else 8
+        _, rows = W._logit_pair(cfg, rng, nrows)
+        rows = rows[None]
+        bs = None if step == 0 else np.sort(rng.random((1, 8), dtype=np.float32))[:, ::-1].copy()
+        o = oracle.draft_step(rows, bs, step, 8, cfg.num_steps, cfg.dtype)
+        sc, tk, pa = _sentinel_lists(1, cfg)
+        ns = torch.full((1, 8), -3.0, dtype=torch.float32, device="cuda")
+        nt = torch.full((1, 8), -7, dtype=torch.int32, device="cuda")
+        assert _call(cfg, 1, step, rows, None if bs is None else G.dev(bs), sc, tk, pa, ns, nt) == 0
+        _compare_step(o, _host_lists(sc, tk, pa, ns, nt), cfg, step, o["near_tie"] < NEAR,
+                      f"v{V}")
+    V1 = 2097153
+    ws = torch.zeros(S.spec_draft_step_workspace_size(1, 8, V1), dtype=torch.uint8, device="cuda")
     with pytest.raises(S.SpecError):
-        S.spec_draft_step(1, 8, cfg.num_steps, 1, cfg.vocab + 1, G.dtype_code(cfg),
-                          torch.zeros(8 * (cfg.vocab + 1), dtype=torch.int16, device="cuda"),
-                          sc[0, :8].contiguous(), sc, tk, pa, sc[0, :8].contiguous(),
-                          tk[0, :8].contiguous(), workspace=ws)
+        S.spec_draft_step(1, 8, cfg.num_steps, 1, V1, G.dtype_code(cfg),
+                          torch.zeros(8 * V1, dtype=torch.int16, device="cuda"),
+                          ns, sc, tk, pa, ns, nt, workspace=ws)
 
 
-@pytest.mark.parametrize("cid", [2, 3, 4, 5])
-def test_draft_step_full(cid):
-    cfg = W.CONFIGS[cid]
-    w = W.make_workload(cfg, 1000 * cid + 2, attention=False)
+# the four full-size workloads; a batch large enough for 8192-entry chunks
+# whose last chunk holds one entry (fewer than topk); more requests than one
+# launch merges (a separate merge launch)
+LARGE = {"cfg2": W.CONFIGS[2], "cfg3": W.CONFIGS[3], "cfg4": W.CONFIGS[4], "cfg5": W.CONFIGS[5],
+         "b40_v16385": W.shrink(W.CONFIGS[5], batch=40, hist=H8, vocab=16385),
+         "b1100_v5000": W.shrink(W.CONFIGS[4], batch=1100, hist=H8, vocab=5000)}
+
+
+@pytest.mark.parametrize("name", list(LARGE))
+def test_draft_step_full(name):
+    cfg = LARGE[name]
+    w = W.make_workload(cfg, 1000 * len(name) + cfg.batch, attention=False)
     b = cfg.batch
     req = np.unique(np.array([0, b // 2, b - 1]))
-    say(f"[draft-step full] cfg{cid} b={b} topk={cfg.topk} V={cfg.vocab} requests {req.tolist()}")
+    cid = name
+    say(f"[draft-step full] {name} b={b} topk={cfg.topk} V={cfg.vocab} requests {req.tolist()}")
     # the whole batch in one call; the sampled requests against the oracle
     topk = cfg.topk
     bs_o = None
@@ -172,7 +196,7 @@ def test_draft_step_full(cid):
             gbs = G.dev(full_bs)
         assert _call(cfg, b, step, rows_all, gbs, sc, tk, pa, ns, nt) == 0
         g = {k: v[req] for k, v in _host_lists(sc, tk, pa, ns, nt).items()}
-        _compare_step(o, g, cfg, step, o["near_tie"] < NEAR, f"cfg{cid}")
+        _compare_step(o, g, cfg, step, o["near_tie"] < NEAR, cid)
         bs_o = o["next_scores"]
 
 
@@ -187,7 +211,7 @@ def test_draft_step_chained_in_place(name):
     sc, tk, pa = _sentinel_lists(b, cfg)
     ns = torch.zeros((b, topk), dtype=torch.float32, device="cuda")
     nt = torch.zeros((b, topk), dtype=torch.int32, device="cuda")
-    ws = torch.empty(S.spec_draft_step_workspace_size(b, topk, cfg.vocab), dtype=torch.uint8,
+    ws = torch.zeros(S.spec_draft_step_workspace_size(b, topk, cfg.vocab), dtype=torch.uint8,
                      device="cuda")
     exempt = np.zeros(b, bool)
     bs = None
