@@ -19,9 +19,11 @@ operation, the GPU time of that operation alone: a graph holding the
 operation for every copy, replayed between two HIP events on the stream the
 kernels run on.
 
-The target-only tree accept (the sibling-mass rule with thresholds 1, 1) is
-timed the same way as an extra operation (``extra_op_ms``); it is not part
-of the step.
+Two operations are timed the same way as extra operations
+(``extra_op_ms``), not part of the step: the target-only tree accept (the
+sibling-mass rule with thresholds 1, 1) and the draft loop's selection (one
+draft-step call per draft step over the workload's draft logits, the path
+scores chained from call to call).
 
 Prints one JSON line (rank 0).
 """
@@ -91,15 +93,24 @@ class Inputs:
         self.tpredict, self.taccept_index, self.taccept_length = i32(b * n), i32(b * s1), i32(b)
         self.new_seq_lens, self.free_slots, self.num_free = i32(b), i32(b * n), i32(b)
         self.status = i32(1)
+        # the draft loop: each step's branch rows of draft logits, contiguous
+        k = cfg.topk
+        self.dsteps = [d(w.ctx_draft[:, 0:1] if i == 0 else w.ctx_draft[:, 1 + (i - 1) * k:1 + i * k])
+                       for i in range(cfg.num_steps)]
+        self.dscores = torch.zeros(b * cfg.ncand, dtype=torch.float32, device="cuda")
+        self.dtokens, self.dparents = i32(b * cfg.ncand), i32(b * cfg.npar)
+        self.dnext_scores = torch.zeros(b * k, dtype=torch.float32, device="cuda")
+        self.dnext_tokens = i32(b * k)
 
     def clone(self, torch):
         other = object.__new__(Inputs)
         for k, v in self.__dict__.items():
-            other.__dict__[k] = v.clone()
+            other.__dict__[k] = [t.clone() for t in v] if isinstance(v, list) else v.clone()
         return other
 
     def nbytes(self):
-        return sum(v.numel() * v.element_size() for v in self.__dict__.values())
+        return sum(sum(t.numel() * t.element_size() for t in v) if isinstance(v, list)
+                   else v.numel() * v.element_size() for v in self.__dict__.values())
 
 
 def _dev(torch, a):
@@ -111,10 +122,11 @@ def _dev(torch, a):
     return torch.from_numpy(a).to("cuda")
 
 
-def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target=None):
+def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target=None, ws_draft=None):
     """The five operations of one step on input copy ``x``, as callables that
-    enqueue their kernels on the current stream, then (timed on its own, not
-    part of the step) the target-only accept."""
+    enqueue their kernels on the current stream, then (timed on their own,
+    not part of the step) the target-only accept and the draft loop's
+    selection."""
     b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
     code = S.SPEC_BF16 if cfg.dtype == "bf16" else S.SPEC_F32
 
@@ -159,7 +171,14 @@ def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target=None):
                                   x.taccept_index, x.taccept_length, workspace=ws_target,
                                   dev_status=x.status)
 
-    return [build, attention, greedy, sample, compact, target_only]
+    def draft_steps():
+        for i in range(cfg.num_steps):
+            S.spec_draft_step(b, cfg.topk, cfg.num_steps, i, cfg.vocab, code, x.dsteps[i],
+                              None if i == 0 else x.dnext_scores, x.dscores, x.dtokens,
+                              x.dparents, x.dnext_scores, x.dnext_tokens, workspace=ws_draft,
+                              dev_status=x.status)
+
+    return [build, attention, greedy, sample, compact, target_only, draft_steps]
 
 
 def run_ops(S, cfg, x, ws_attn, ws_greedy, ws_sample):
@@ -176,7 +195,7 @@ def cfg_max_len(cfg):
 
 
 OPS = ("build_tree", "verify_attention", "accept_greedy", "accept_sample", "compact_kv")
-EXTRA_OPS = ("accept_target_only",)     # timed alone, outside the step
+EXTRA_OPS = ("accept_target_only", "draft_steps")     # timed alone, outside the step
 
 
 def cpu_baseline(cfg, w, tl, dl, budget_s):
@@ -283,6 +302,8 @@ def main():
                             device="cuda")
     ws_target = torch.zeros(S.spec_accept_target_only_workspace_size(b, n, cfg.vocab),
                             dtype=torch.uint8, device="cuda")
+    ws_draft = torch.empty(S.spec_draft_step_workspace_size(b, cfg.topk, cfg.vocab),
+                           dtype=torch.uint8, device="cuda")
     S.spec_build_tree(b, cfg.topk, cfg.num_steps, n, S.SPEC_MASK_QLEN_BITS, base.scores,
                       base.tokens, base.parents, base.bonus, base.seq_lens, base.draft_tokens,
                       base.positions, base.tree_mask, base.retrieve_index,
@@ -309,7 +330,7 @@ def main():
         run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample)
     torch.cuda.synchronize()
 
-    calls = [op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target) for x in xs]
+    calls = [op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target, ws_draft) for x in xs]
     op_ms, extra_ms = {}, {}
     if args.mode == "graph":
         # per-operation GPU times: one graph per operation holding that
@@ -347,13 +368,14 @@ def main():
         torch.cuda.synchronize()
         for j, op in enumerate(OPS):
             op_ms[op] = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(k_ev):
-            calls[i % copies][len(OPS)]()
-        e1.record()
-        torch.cuda.synchronize()
-        extra_ms["accept_target_only"] = e0.elapsed_time(e1) / k_ev
+        for j, op in enumerate(EXTRA_OPS):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(k_ev):
+                calls[i % copies][len(OPS) + j]()
+            e1.record()
+            torch.cuda.synchronize()
+            extra_ms[op] = e0.elapsed_time(e1) / k_ev
 
     # eager steps (every launch from Python)
     k_e = max(5, min(args.steps, 20))
@@ -406,6 +428,7 @@ def main():
         base.saccept_length.cpu().numpy()
     attn_bytes = W.attention_bytes(cfg, w.seq_lens)
     sweep_g = b * n * cfg.vocab * (2 if cfg.dtype == "bf16" else 4)
+    draft_bytes = b * cfg.npar * cfg.vocab * (2 if cfg.dtype == "bf16" else 4)
     attn_gbs = attn_bytes / (op_ms["verify_attention"] * 1e-3) / 1e9
     greedy_gbs = sweep_g / (op_ms["accept_greedy"] * 1e-3) / 1e9
     accept_op = "accept_greedy" if "greedy" in cfg.accept else "accept_sample"
@@ -441,6 +464,8 @@ def main():
         "accept_greedy_sweep_gbs": greedy_gbs,
         "extra_op_ms": extra_ms,
         "accept_target_only_sweep_gbs": sweep_g / (extra_ms["accept_target_only"] * 1e-3) / 1e9,
+        "draft_step_calls": cfg.num_steps,
+        "draft_steps_sweep_gbs": draft_bytes / (extra_ms["draft_steps"] * 1e-3) / 1e9,
         "mean_accept_length": float(acc_len.mean()),
         "dev_status": status,
         "roofline": {"kernel": "spec_verify_attention (split-KV MFMA + merge launches)",
