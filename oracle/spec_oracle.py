@@ -638,3 +638,108 @@ def compact_kv(k_pool, v_pool, page_table, seq_lens, out_cache_loc, accept_index
         num_free[r] = cnt
     return dict(k_pool=k_out, v_pool=v_out, new_seq_lens=new_seq_lens,
                 free_slots=free_slots, num_free=num_free, status=status)
+
+
+# ---------------------------------------------------------------------------
+# C6  Memory-side neighbours: FULL mask, paged draft-branch planning
+# ---------------------------------------------------------------------------
+
+def full_mask(seq_lens, tree_mask, fill_prefix=True, prior=None):
+    """[P1] 三种 mask 形态 (FULL_MASK) with its fill_prefix_mask switch.
+
+    Every verify row sees the whole committed prefix and, among the tree
+    nodes, its QLEN_ONLY mask row.  Layout (the per-request blocks of the
+    [rows, prefix + tree] mask, concatenated): request b's block starts at
+    n * sum_{b' < b} (L_b' + n) bytes and holds n rows of L_b + n bytes; row
+    k is L_b prefix bytes of 1, then tree_mask[b, k, :] as bytes.  With
+    fill_prefix false the prefix bytes are not written: they keep the
+    values of ``prior`` (same size; zeros when None).
+    tree_mask: bool [b, n, n].  Returns uint8 [n * sum(L_b + n)]."""
+    L = np.asarray(seq_lens, np.int64)
+    tm = np.asarray(tree_mask, bool)
+    b, n, _ = tm.shape
+    total = int(n * (L.sum() + n * b))
+    out = np.zeros(total, np.uint8) if prior is None else np.array(prior, np.uint8, copy=True)
+    assert out.size == total
+    off = 0
+    for r in range(b):
+        width = int(L[r]) + n
+        for k in range(n):
+            row = off + k * width
+            if fill_prefix:
+                out[row:row + int(L[r])] = 1
+            out[row + int(L[r]):row + width] = tm[r, k].astype(np.uint8)
+        off += n * width
+    return out
+
+
+def plan_draft_branches(seq_lens, page_table, branch_pages, topk, num_steps, page_size,
+                        num_pages):
+    """[P1] prepare_for_draft (KV slots for the draft writes) and
+    duplicate_prefix_tail_to_draft_branches.
+
+    Request b has L committed tokens; its prefix tail (the tokens on its last,
+    partial page) is tail = L mod page_size tokens at slots
+    page_table[b][L div page_size] * page_size + [0, tail).
+      * topk > 1: branch j owns the pages branch_pages[b][j][0 ..), a
+        page-aligned region whose slot t is page t div page_size, offset
+        t mod page_size.  Its first `tail` slots are holes standing for the
+        prefix tail: they receive a copy of the prefix tail's KV (every
+        layer, K and V), so reading the branch's pages whole gives the right
+        tokens.  Draft step s of branch j writes region slot tail + s.
+      * topk == 1 (the contiguous case): the single branch continues the
+        prefix in place: draft step s writes the slot of position L + s
+        through page_table; nothing is copied.
+    (page_size 1 makes tail 0: no copies in either case.)
+
+    Returns out_cache_loc int64 [b, topk, num_steps] (-1 where a page id is
+    out of range), copies: list of (src_slot, dst_slot), status (bit 1 on a
+    page id outside [0, num_pages))."""
+    L = np.asarray(seq_lens, np.int64)
+    pt = np.asarray(page_table, np.int64)
+    bp = np.asarray(branch_pages, np.int64)
+    b = L.size
+    ps = page_size
+    out = np.full((b, topk, num_steps), -1, np.int64)
+    copies = []
+    status = 0
+
+    def slot_of(page, off):
+        nonlocal status
+        if not (0 <= page < num_pages):
+            status |= ST_RANGE
+            return -1
+        return int(page) * ps + off
+
+    for r in range(b):
+        tail = int(L[r]) % ps
+        if topk == 1:
+            for s in range(num_steps):
+                pos = int(L[r]) + s
+                out[r, 0, s] = slot_of(pt[r, pos // ps], pos % ps)
+            continue
+        src_page = pt[r, int(L[r]) // ps] if tail > 0 else 0
+        for j in range(topk):
+            for t in range(tail):
+                src = slot_of(src_page, t)
+                dst = slot_of(bp[r, j, t // ps], t % ps)
+                if src >= 0 and dst >= 0:
+                    copies.append((src, dst))
+            for s in range(num_steps):
+                t = tail + s
+                out[r, j, s] = slot_of(bp[r, j, t // ps], t % ps)
+    return dict(out_cache_loc=out, copies=copies, status=status)
+
+
+def duplicate_prefix_tail(k_pool, v_pool, copies):
+    """Apply the copies of plan_draft_branches to pools [layers, slots, hkv,
+    d] (new arrays; every source is read before any destination is written)."""
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    if copies:
+        src = np.array([c[0] for c in copies], np.int64)
+        dst = np.array([c[1] for c in copies], np.int64)
+        k_rows, v_rows = k_out[:, src].copy(), v_out[:, src].copy()
+        k_out[:, dst] = k_rows
+        v_out[:, dst] = v_rows
+    return k_out, v_out
