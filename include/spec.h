@@ -1,7 +1,9 @@
 /*
  * spec.h - C ABI of the tree speculative-decoding hot path for AMD MI355X
  * (gfx950): tree build, tree-masked verify attention, greedy and
- * rejection-sampled tree accept, accepted-KV compaction.
+ * rejection-sampled tree accept, accepted-KV compaction; the target-only
+ * tree accept, the draft step, the FULL mask and paged draft-branch
+ * planning.
  *
  * Sources (web pages, cited by title and section):
  *   [P1] "SGLang 源码完全拆解(十一):投机解码——草稿生成、批量验证与 token 接受如何接进同一条前向"
@@ -352,6 +354,62 @@ int spec_compact_kv(int batch, int num_draft_tokens, int accept_width, int num_l
                     const int32_t *accept_index, const int32_t *accept_length,
                     int32_t *new_seq_lens, int32_t *free_slots, int32_t *num_free,
                     int32_t *dev_status, spec_stream_t stream);
+
+/*
+ * FULL tree mask.  [P1] 三种 mask 形态 (FULL_MASK) and the fill_prefix_mask
+ * switch: every verify row sees the whole committed prefix and, among the
+ * tree nodes, its QLEN_ONLY row.
+ *
+ *   seq_lens [batch] i32 committed lengths L_b, 0 <= L_b <= max_seq_len
+ *   tree_mask_bits [batch*n] words of spec_mask_word_bytes(n) bytes: the
+ *       SPEC_MASK_QLEN_BITS mask spec_build_tree writes (word-aligned)
+ *   full_mask: u8 bytes, 16-byte aligned, full_mask_bytes of them; request
+ *       b's block starts at n * sum_{b' < b} (L_b' + n) and holds n rows of
+ *       L_b + n bytes: L_b prefix bytes (1), then byte j of the tree part =
+ *       bit j of the row's word.  The caller sizes it n * sum_b (L_b + n).
+ *   fill_prefix: nonzero writes every byte; zero writes only the tree
+ *       bytes (the prefix bytes keep what the buffer held)
+ * Writes past full_mask_bytes are dropped and raise SPEC_ST_RANGE, as does
+ * L_b outside [0, max_seq_len] (bytes past max_seq_len + n of a row are
+ * then not written).  n <= 64 (else SPEC_ERR_UNSUPPORTED).
+ */
+int spec_full_mask(int batch, int num_draft_tokens, const int32_t *seq_lens, int max_seq_len,
+                   const void *tree_mask_bits, int fill_prefix, void *full_mask,
+                   int64_t full_mask_bytes, int32_t *dev_status, spec_stream_t stream);
+
+/*
+ * Paged draft-branch planning.  [P1] prepare_for_draft (KV slots of the
+ * draft writes) and duplicate_prefix_tail_to_draft_branches.
+ *
+ * Request b has L_b committed tokens; its prefix tail is the tail = L_b mod
+ * page_size tokens on its last, partial page page_table[b][L_b div
+ * page_size].
+ *   topk > 1: branch j owns the pages branch_pages[b][j][0 .. pages_per_branch)
+ *       (caller-allocated, distinct from the request's prefix pages), a
+ *       page-aligned region whose slot t is page t div page_size, offset
+ *       t mod page_size.  Its first `tail` slots receive a copy of the prefix
+ *       tail's K and V (every layer), so whole-page reads of the branch see
+ *       its tokens; draft step s of branch j writes region slot tail + s.
+ *       pages_per_branch * page_size >= page_size - 1 + num_steps (else
+ *       SPEC_ERR_SHAPE).
+ *   topk == 1 (the contiguous case): the branch continues the prefix in
+ *       place; step s writes the slot of position L_b + s through page_table
+ *       (which must hold those pages); nothing is copied; branch_pages may
+ *       be NULL.
+ *   k_pool, v_pool [num_layers, num_slots, num_kv_heads, head_dim] dtype,
+ *       updated in place (16-byte aligned; a row's bytes a multiple of 16,
+ *       else SPEC_ERR_UNSUPPORTED); page ids lie in [0, num_slots / page_size)
+ *   page_table [batch, max_pages] i32
+ * Output: out_cache_loc [batch, topk, num_steps] i32, the slot draft step s
+ * of branch j writes (-1 and SPEC_ST_RANGE where a page id is out of
+ * range; such a copy is skipped).
+ */
+int spec_plan_draft_branches(int batch, int topk, int num_steps, int page_size, int num_layers,
+                             int num_kv_heads, int head_dim, int dtype, void *k_pool,
+                             void *v_pool, int64_t num_slots, const int32_t *seq_lens,
+                             const int32_t *page_table, int max_pages,
+                             const int32_t *branch_pages, int pages_per_branch,
+                             int32_t *out_cache_loc, int32_t *dev_status, spec_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -48,7 +48,8 @@ EXPORTS = ("spec_version", "spec_status_string", "spec_mask_word_bytes", "spec_b
            "spec_verify_attention_workspace_size", "spec_verify_attention",
            "spec_accept_workspace_size", "spec_accept_greedy", "spec_accept_sample",
            "spec_accept_target_only_workspace_size", "spec_accept_target_only",
-           "spec_draft_step_workspace_size", "spec_draft_step",
+           "spec_draft_step_workspace_size", "spec_draft_step", "spec_full_mask",
+           "spec_plan_draft_branches",
            "spec_compact_kv")
 
 _P = ctypes.c_void_p
@@ -83,6 +84,9 @@ _decl("spec_accept_target_only", _I, _I, _I, _I, _I64, _I, _P, _P, _F, _F, _P, _
       _P, _P, _P, _P, _P, _SZ, _P, _P)
 _decl("spec_draft_step_workspace_size", _SZ, _I, _I, _I64)
 _decl("spec_draft_step", _I, _I, _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P)
+_decl("spec_full_mask", _I, _I, _I, _P, _I, _P, _I, _P, _I64, _P, _P)
+_decl("spec_plan_draft_branches", _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I64, _P, _P, _I, _P,
+      _I, _P, _P, _P)
 _decl("spec_compact_kv", _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I64, _P, _I, _P, _P, _P,
       _P, _P, _P, _P, _P, _P)
 
@@ -350,6 +354,50 @@ def spec_draft_step(batch, topk, num_steps, step, vocab, dtype, draft_logits, br
     ]
     _check("spec_draft_step", _lib.spec_draft_step(batch, topk, num_steps, step, vocab, dtype,
                                                     *args, _stream(stream)))
+
+
+def spec_full_mask(batch, num_draft_tokens, seq_lens, max_seq_len, tree_mask_bits, fill_prefix,
+                   full_mask, dev_status=None, stream=None):
+    dev = _device()
+    n = num_draft_tokens
+    wb = max(1, spec_mask_word_bytes(n))
+    none = batch == 0
+    args = [
+        _ptr(seq_lens, "seq_lens", dev, nbytes=batch * 4, optional=none),
+        max_seq_len,
+        _ptr(tree_mask_bits, "tree_mask_bits", dev, nbytes=batch * n * wb, optional=none),
+        1 if fill_prefix else 0,
+        _ptr(full_mask, "full_mask", dev, optional=none),
+        0 if full_mask is None else full_mask.numel() * full_mask.element_size(),
+        _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
+    ]
+    _check("spec_full_mask", _lib.spec_full_mask(batch, n, *args, _stream(stream)))
+
+
+def spec_plan_draft_branches(batch, topk, num_steps, page_size, num_layers, num_kv_heads,
+                             head_dim, dtype, k_pool, v_pool, num_slots, seq_lens, page_table,
+                             max_pages, branch_pages, pages_per_branch, out_cache_loc,
+                             dev_status=None, stream=None):
+    dev = _device()
+    pool = num_layers * num_slots * num_kv_heads * head_dim * _ELEM.get(dtype, 4)
+    none = batch == 0
+    args = [
+        _ptr(k_pool, "k_pool", dev, nbytes=pool, optional=none),
+        _ptr(v_pool, "v_pool", dev, nbytes=pool, optional=none),
+        num_slots,
+        _ptr(seq_lens, "seq_lens", dev, nbytes=batch * 4, optional=none),
+        _ptr(page_table, "page_table", dev, nbytes=batch * max_pages * 4, optional=none),
+        max_pages,
+        _ptr(branch_pages, "branch_pages", dev, nbytes=batch * topk * pages_per_branch * 4,
+             optional=none or topk == 1),
+        pages_per_branch,
+        _ptr(out_cache_loc, "out_cache_loc", dev, nbytes=batch * topk * num_steps * 4,
+             optional=none),
+        _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
+    ]
+    _check("spec_plan_draft_branches", _lib.spec_plan_draft_branches(
+        batch, topk, num_steps, page_size, num_layers, num_kv_heads, head_dim, dtype, *args,
+        _stream(stream)))
 
 
 def spec_compact_kv(batch, num_draft_tokens, accept_width, num_layers, num_kv_heads, head_dim,

@@ -145,6 +145,27 @@ def test_host_errors_before_launch():
     assert ds(1, 4, 3, 1, 1000, 0, *npr, big, P0, P0) == -1         # parents before the last step
     assert ds(1, 4, 3, 1, 1000, 0, *f8, 8, P0, P0) == -5            # workspace small
     assert ds(0, 4, 3, 1, 1000, 0, *([P0] * 8), 0, P0, P0) == 0
+    fm = lib.spec_full_mask
+    fm.restype = I
+    fm.argtypes = [I, I, ctypes.c_void_p, I, ctypes.c_void_p, I, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    al16 = ctypes.c_void_p(0x1000)
+    assert fm(1, 65, al16, 8, al16, 1, al16, 1 << 20, P0, P0) == -4        # n > 64
+    assert fm(1, 0, al16, 8, al16, 1, al16, 1 << 20, P0, P0) == -2
+    assert fm(1, 8, P0, 8, al16, 1, al16, 1 << 20, P0, P0) == -1
+    assert fm(1, 8, al16, 8, al16, 1, ctypes.c_void_p(0x1001), 1 << 20, P0, P0) == -2
+    assert fm(0, 8, P0, 8, P0, 1, P0, 0, P0, P0) == 0
+    pb = lib.spec_plan_draft_branches
+    pb.restype = I
+    pb.argtypes = ([I] * 8 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                              ctypes.c_void_p, I, ctypes.c_void_p, I, ctypes.c_void_p,
+                              ctypes.c_void_p, ctypes.c_void_p])
+    a6 = [al16] * 2
+    assert pb(1, 2, 5, 4, 1, 8, 128, 1, *a6, 1024, al16, al16, 8, al16, 1, al16, P0, P0) == -2  # region small
+    assert pb(1, 2, 5, 4, 1, 8, 128, 9, *a6, 1024, al16, al16, 8, al16, 2, al16, P0, P0) == -3
+    assert pb(1, 2, 5, 4, 1, 1, 6, 0, *a6, 1024, al16, al16, 8, al16, 2, al16, P0, P0) == -4  # 24-byte rows
+    assert pb(1, 2, 5, 4, 1, 8, 128, 1, *a6, 1024, al16, al16, 8, P0, 2, al16, P0, P0) == -1
+    assert pb(0, 2, 5, 4, 1, 8, 128, 1, P0, P0, 1024, P0, P0, 8, P0, 2, P0, P0, P0) == 0
     ck = lib.spec_compact_kv
     ck.restype = I
     ck.argtypes = [I] * 8 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, I] + [ctypes.c_void_p] * 9 + [ctypes.c_void_p]
