@@ -19,11 +19,13 @@ operation, the GPU time of that operation alone: a graph holding the
 operation for every copy, replayed between two HIP events on the stream the
 kernels run on.
 
-Two operations are timed the same way as extra operations
+Four operations are timed the same way as extra operations
 (``extra_op_ms``), not part of the step: the target-only tree accept (the
-sibling-mass rule with thresholds 1, 1) and the draft loop's selection (one
+sibling-mass rule with thresholds 1, 1), the draft loop's selection (one
 draft-step call per draft step over the workload's draft logits, the path
-scores chained from call to call).
+scores chained from call to call), the FULL tree mask with its prefix
+filled, and the paged draft-branch planning (prefix-tail duplication into
+the branches' pages of a one-layer draft KV pool, draft write slots).
 
 Prints one JSON line (rank 0).
 """
@@ -122,7 +124,7 @@ def _dev(torch, a):
     return torch.from_numpy(a).to("cuda")
 
 
-def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target=None, ws_draft=None):
+def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target=None, ws_draft=None, mem=None):
     """The five operations of one step on input copy ``x``, as callables that
     enqueue their kernels on the current stream, then (timed on their own,
     not part of the step) the target-only accept and the draft loop's
@@ -178,7 +180,19 @@ def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target=None, ws_draft=
                               x.dparents, x.dnext_scores, x.dnext_tokens, workspace=ws_draft,
                               dev_status=x.status)
 
-    return [build, attention, greedy, sample, compact, target_only, draft_steps]
+    def full_mask():
+        S.spec_full_mask(b, n, x.seq_lens, cfg_max_len(cfg), x.tree_mask, True, mem["full_mask"],
+                         dev_status=x.status)
+
+    def plan_branches():
+        S.spec_plan_draft_branches(b, cfg.topk, cfg.num_steps, cfg.page_size, 1, cfg.num_kv_heads,
+                                   cfg.head_dim, code, mem["k"], mem["v"], mem["slots"],
+                                   x.seq_lens, x.page_table, x.page_table.shape[1],
+                                   mem["branch_pages"] if cfg.topk > 1 else None,
+                                   mem["per_branch"], mem["draft_loc"], dev_status=x.status)
+
+    return [build, attention, greedy, sample, compact, target_only, draft_steps, full_mask,
+            plan_branches]
 
 
 def run_ops(S, cfg, x, ws_attn, ws_greedy, ws_sample):
@@ -190,12 +204,36 @@ def run_ops(S, cfg, x, ws_attn, ws_greedy, ws_sample):
 _MAXLEN = {}
 
 
+def memory_side_buffers(torch, S, cfg, w):
+    """Buffers the FULL-mask and branch-planning extra operations share across
+    input copies: the mask output (n * sum(L + n) bytes) and a one-layer draft
+    KV pool holding the target's page ids plus, per request and branch, the
+    pages of a branch region (ids after the target's)."""
+    b, n, ps, k = cfg.batch, cfg.num_draft_tokens, cfg.page_size, cfg.topk
+    full_bytes = int(n * (int(w.seq_lens.sum()) + n * b))
+    per_branch = (ps - 1 + cfg.num_steps + ps - 1) // ps
+    used = int(w.page_table.max()) + 1
+    pages = used + b * k * per_branch
+    eb = 2 if cfg.dtype == "bf16" else 4
+    mem = {
+        "full_mask": torch.empty(max(16, full_bytes), dtype=torch.uint8, device="cuda"),
+        "full_bytes": full_bytes,
+        "k": torch.empty(pages * ps * cfg.num_kv_heads * cfg.head_dim * eb, dtype=torch.uint8, device="cuda"),
+        "v": torch.empty(pages * ps * cfg.num_kv_heads * cfg.head_dim * eb, dtype=torch.uint8, device="cuda"),
+        "slots": pages * ps,
+        "per_branch": per_branch,
+        "branch_pages": torch.arange(used, pages, dtype=torch.int32, device="cuda"),
+        "draft_loc": torch.zeros(b * k * cfg.num_steps, dtype=torch.int32, device="cuda"),
+    }
+    return mem
+
+
 def cfg_max_len(cfg):
     return _MAXLEN[cfg.name]
 
 
 OPS = ("build_tree", "verify_attention", "accept_greedy", "accept_sample", "compact_kv")
-EXTRA_OPS = ("accept_target_only", "draft_steps")     # timed alone, outside the step
+EXTRA_OPS = ("accept_target_only", "draft_steps", "full_mask", "plan_draft_branches")
 
 
 def cpu_baseline(cfg, w, tl, dl, budget_s):
@@ -304,6 +342,7 @@ def main():
                             dtype=torch.uint8, device="cuda")
     ws_draft = torch.empty(S.spec_draft_step_workspace_size(b, cfg.topk, cfg.vocab),
                            dtype=torch.uint8, device="cuda")
+    mem = memory_side_buffers(torch, S, cfg, w)
     S.spec_build_tree(b, cfg.topk, cfg.num_steps, n, S.SPEC_MASK_QLEN_BITS, base.scores,
                       base.tokens, base.parents, base.bonus, base.seq_lens, base.draft_tokens,
                       base.positions, base.tree_mask, base.retrieve_index,
@@ -330,7 +369,8 @@ def main():
         run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample)
     torch.cuda.synchronize()
 
-    calls = [op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target, ws_draft) for x in xs]
+    calls = [op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target, ws_draft, mem)
+             for x in xs]
     op_ms, extra_ms = {}, {}
     if args.mode == "graph":
         # per-operation GPU times: one graph per operation holding that
@@ -465,6 +505,8 @@ def main():
         "extra_op_ms": extra_ms,
         "accept_target_only_sweep_gbs": sweep_g / (extra_ms["accept_target_only"] * 1e-3) / 1e9,
         "draft_step_calls": cfg.num_steps,
+        "full_mask_bytes": mem["full_bytes"],
+        "full_mask_write_gbs": mem["full_bytes"] / (extra_ms["full_mask"] * 1e-3) / 1e9,
         "draft_steps_sweep_gbs": draft_bytes / (extra_ms["draft_steps"] * 1e-3) / 1e9,
         "mean_accept_length": float(acc_len.mean()),
         "dev_status": status,

@@ -6,9 +6,9 @@
 // n * sum_{b' < b} (L_b' + n) bytes and holds n rows of L_b + n bytes: L_b
 // prefix bytes of 1, then the tree row expanded from its bit-packed word.
 // Without the prefix fill only the tree bytes are written.  One workgroup
-// per (row, 4096-byte range of the row), aligned 16-byte stores inside the
-// row and byte stores at its two ends; the request offset is a block sum of
-// the earlier requests' lengths.
+// per (row, 32 KB range of the row), aligned 16-byte streaming stores inside the row
+// and byte stores at its two ends; the request offset is a block sum of the
+// earlier requests' lengths.
 //
 // Paged draft-branch planning (same page, prepare_for_draft and
 // duplicate_prefix_tail_to_draft_branches): with page_size > 1 and topk > 1
@@ -18,13 +18,21 @@
 // tokens, and draft step s of branch j writes region slot tail + s.  With
 // topk 1 the single branch continues the prefix in place (the contiguous
 // case): step s writes the slot of position L + s through the page table.
-// One workgroup per (request, layer); the layer-0 workgroup writes the
-// draft slots.
+// One workgroup per (request, layer, 1024 16-byte units of the copies, each
+// thread's four loads in flight together); the first workgroup of layer 0
+// writes the draft slots.
+#include <algorithm>
+
 #include "spec_common.h"
 
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
+constexpr int kPer = 4;                    // 16-byte units per thread, in flight together
+constexpr int kMaskPer = 8;                // 16-byte mask units per thread
+constexpr int kRowSpan = kThreads * 16 * kMaskPer;   // bytes of a mask row per workgroup
 
 __device__ __forceinline__ uint64_t mask_word(const uint8_t *p, int wb) {
     switch (wb) {
@@ -75,7 +83,9 @@ __global__ __launch_bounds__(kThreads) void full_mask_kernel(
         // the tree bytes only
         if (part == 0 && tid < n && a0 + L + tid < end) out[a0 + L + tid] = (bits >> tid) & 1u;
     } else {
-        const int64_t A = (a0 & ~(int64_t)15) + ((int64_t)part * kThreads + tid) * 16;
+#pragma unroll
+      for (int h = 0; h < kMaskPer; ++h) {
+        const int64_t A = (a0 & ~(int64_t)15) + (int64_t)part * kRowSpan + (h * kThreads + tid) * 16;
         if (A < end && A + 16 > a0) {
             uint8_t v[16];
 #pragma unroll
@@ -85,18 +95,19 @@ __global__ __launch_bounds__(kThreads) void full_mask_kernel(
                        : col < L ? 1 : (uint8_t)((bits >> (int)(col - L)) & 1u);
             }
             if (A >= a0 && A + 16 <= end) {
-                uint4 u;
+                u32x4 u;
                 u.x = v[0] | (v[1] << 8) | (v[2] << 16) | ((uint32_t)v[3] << 24);
                 u.y = v[4] | (v[5] << 8) | (v[6] << 16) | ((uint32_t)v[7] << 24);
                 u.z = v[8] | (v[9] << 8) | (v[10] << 16) | ((uint32_t)v[11] << 24);
                 u.w = v[12] | (v[13] << 8) | (v[14] << 16) | ((uint32_t)v[15] << 24);
-                *reinterpret_cast<uint4 *>(out + A) = u;
+                __builtin_nontemporal_store(u, reinterpret_cast<u32x4 *>(out + A));
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     if (A + i >= a0 && A + i < end) out[A + i] = v[i];
             }
         }
+      }
     }
     if (tid == 0 && part == 0) spec::raise_status(status, err);
 }
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void plan_branches_kernel(
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ branch_pages,
     int32_t *__restrict__ out_cache_loc, int32_t *__restrict__ status) {
     __shared__ int s_err;
-    const int b = blockIdx.x, layer = blockIdx.y, tid = threadIdx.x;
+    const int b = blockIdx.x, layer = blockIdx.y, part = blockIdx.z, tid = threadIdx.x;
     if (tid == 0) s_err = 0;
     __syncthreads();
     int err = 0;
@@ -121,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void plan_branches_kernel(
     const int32_t *pt = page_table + (int64_t)b * max_pages;
     const int32_t *bp = branch_pages + (int64_t)b * topk * pages_per_branch;
     // the draft write slots
-    if (layer == 0) {
+    if (layer == 0 && part == 0) {
         for (int q = tid; q < topk * num_steps; q += kThreads) {
             const int j = q / num_steps, s = q % num_steps;
             int64_t page = -1;
@@ -149,23 +160,39 @@ __global__ __launch_bounds__(kThreads) void plan_branches_kernel(
         if (src_page < 0 || src_page >= num_pages) {
             err |= SPEC_ST_RANGE;
         } else {
+            // this workgroup's kThreads * kPer units of the topk * tail rows
             const int64_t units = (int64_t)topk * tail * row16;
             uint4 *kl = k_pool + layer * layer_stride16;
             uint4 *vl = v_pool + layer * layer_stride16;
-            for (int64_t q = tid; q < units; q += kThreads) {
-                const int u = (int)(q % row16);
-                const int t = (int)((q / row16) % tail);
-                const int j = (int)(q / ((int64_t)row16 * tail));
-                const int64_t dst_page = bp[(int64_t)j * pages_per_branch];   // t < page_size
-                if (dst_page < 0 || dst_page >= num_pages) {
-                    err |= SPEC_ST_RANGE;
-                    continue;
+            int64_t dst[kPer];
+            uint4 kv[kPer], vv[kPer];
+#pragma unroll
+            for (int h = 0; h < kPer; ++h) {
+                const int64_t q = ((int64_t)part * kPer + h) * kThreads + tid;
+                dst[h] = -1;
+                kv[h] = make_uint4(0, 0, 0, 0);
+                vv[h] = kv[h];
+                if (q < units) {
+                    const int u = (int)(q % row16);
+                    const int t = (int)((q / row16) % tail);
+                    const int j = (int)(q / ((int64_t)row16 * tail));
+                    const int64_t dst_page = bp[(int64_t)j * pages_per_branch];   // t < page_size
+                    if (dst_page < 0 || dst_page >= num_pages) {
+                        err |= SPEC_ST_RANGE;
+                    } else {
+                        const int64_t src = (src_page * page_size + t) * row16 + u;
+                        dst[h] = (dst_page * page_size + t) * row16 + u;
+                        kv[h] = kl[src];
+                        vv[h] = vl[src];
+                    }
                 }
-                const int64_t src = (src_page * page_size + t) * row16 + u;
-                const int64_t dst = (dst_page * page_size + t) * row16 + u;
-                const uint4 kv = kl[src], vv = vl[src];
-                kl[dst] = kv;
-                vl[dst] = vv;
+            }
+#pragma unroll
+            for (int h = 0; h < kPer; ++h) {
+                if (dst[h] >= 0) {
+                    kl[dst[h]] = kv[h];
+                    vl[dst[h]] = vv[h];
+                }
             }
         }
     }
@@ -190,7 +217,7 @@ extern "C" int spec_full_mask(int batch, int num_draft_tokens, const int32_t *se
         reinterpret_cast<uintptr_t>(full_mask) % 16 != 0)
         return SPEC_ERR_SHAPE;
     const int64_t wmax = (int64_t)max_seq_len + n;
-    const int64_t per_row = fill_prefix ? (wmax / 16 + 2 + kThreads - 1) / kThreads : 1;
+    const int64_t per_row = fill_prefix ? ((wmax / 16 + 2) * 16 + kRowSpan - 1) / kRowSpan : 1;
     const int64_t grid = (int64_t)batch * n * per_row;
     if (grid > INT_MAX) return SPEC_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(full_mask_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
@@ -225,7 +252,11 @@ extern "C" int spec_plan_draft_branches(int batch, int topk, int num_steps, int 
     if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15u)
         return SPEC_ERR_SHAPE;
     const int row16 = (int)(row_bytes / 16);
-    hipLaunchKernelGGL(plan_branches_kernel, dim3(batch, num_layers), dim3(kThreads), 0,
+    // copy units of a (request, layer): at most topk * (page_size - 1) rows
+    const int64_t max_units = topk > 1 ? (int64_t)topk * (page_size - 1) * row16 : 0;
+    const int64_t parts = std::max<int64_t>(1, (max_units + kThreads * kPer - 1) / (kThreads * kPer));
+    if (parts > 65535) return SPEC_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(plan_branches_kernel, dim3(batch, num_layers, (unsigned)parts), dim3(kThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), topk, num_steps, page_size,
                        max_pages, pages_per_branch, row16, num_slots / page_size,
                        num_slots * row16, static_cast<uint4 *>(k_pool),
