@@ -641,6 +641,62 @@ def compact_kv(k_pool, v_pool, page_table, seq_lens, out_cache_loc, accept_index
 
 
 # ---------------------------------------------------------------------------
+# C7  Sampling-parameter pre-pass
+# ---------------------------------------------------------------------------
+
+def filter_logits(logits, dtype, temperature, top_k, top_p, band=1e-6):
+    """[P2] 四 (eagle_sample: the target softmax at the request's temperature,
+    then top-k / top-p filtering and renormalisation) and [P1] 三条判定路径
+    (the sampled path renormalises top-k / top-p before the accept).
+
+    Row i (request of row i given by the per-row parameters) has
+    p = softmax(x / T) in float64.  Entries are ranked by p descending, lower
+    index first; entry of rank r is kept iff r < top_k (when 1 <= top_k < V)
+    and the mass of the entries ranked above it is < top_p (when top_p < 1),
+    i.e. the smallest top set reaching mass top_p.  Both rules are decided on
+    the same p, then one renormalisation: the kept logits are returned as
+    they were and the others as -inf, so softmax(filtered / T) is the
+    renormalised distribution.  A greedy request is top_k = 1.
+
+    logits [rows, V] (float32 or bf16 bit patterns); temperature, top_k,
+    top_p: per row.  Returns (filtered logits in the input's storage type,
+    kept bool [rows, V], near bool [rows]: a top-p decision within `band` of
+    top_p, where an evaluation whose masses are an ulp off may keep one entry
+    more or less)."""
+    x = widen(logits, dtype)
+    rows, V = x.shape
+    kept = np.zeros((rows, V), bool)
+    near = np.zeros(rows, bool)
+    for i in range(rows):
+        xi = x[i]
+        T = float(temperature[i])
+        e = np.exp((xi - xi.max()) / T)
+        p = e / e.sum()
+        order = np.lexsort((np.arange(V), -xi))     # x descending, index ascending
+        k = int(top_k[i])
+        tp = float(top_p[i])
+        before = 0.0
+        for r, j in enumerate(order):
+            keep = True
+            if 1 <= k < V and r >= k:
+                keep = False
+            if tp < 1.0:
+                if abs(before - tp) < band:
+                    near[i] = True
+                if before >= tp:
+                    keep = False
+            if not keep:
+                break
+            kept[i, j] = True
+            before += p[j]
+    if dtype == "bf16":
+        out = np.where(kept, np.asarray(logits, np.uint16), np.uint16(0xFF80))
+    else:
+        out = np.where(kept, np.asarray(logits, np.float32), np.float32(-np.inf))
+    return out, kept, near
+
+
+# ---------------------------------------------------------------------------
 # C6  Memory-side neighbours: FULL mask, paged draft-branch planning
 # ---------------------------------------------------------------------------
 
