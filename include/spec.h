@@ -2,8 +2,8 @@
  * spec.h - C ABI of the tree speculative-decoding hot path for AMD MI355X
  * (gfx950): tree build, tree-masked verify attention, greedy and
  * rejection-sampled tree accept, accepted-KV compaction; the target-only
- * tree accept, the draft step, the FULL mask and paged draft-branch
- * planning.
+ * tree accept, the draft step, the top-k / top-p pre-pass, the FULL mask and
+ * paged draft-branch planning.
  *
  * Sources (web pages, cited by title and section):
  *   [P1] "SGLang 源码完全拆解(十一):投机解码——草稿生成、批量验证与 token 接受如何接进同一条前向"
@@ -354,6 +354,34 @@ int spec_compact_kv(int batch, int num_draft_tokens, int accept_width, int num_l
                     const int32_t *accept_index, const int32_t *accept_length,
                     int32_t *new_seq_lens, int32_t *free_slots, int32_t *num_free,
                     int32_t *dev_status, spec_stream_t stream);
+
+/*
+ * Sampling-parameter pre-pass: top-k / top-p filtering of the target
+ * distribution.  [P2] 四 (eagle_sample: the target softmax at the request's
+ * temperature, then top-k / top-p filtering and renormalisation) and [P1]
+ * 三条判定路径.
+ *
+ *   logits [batch*n, vocab] dtype; row i belongs to request i / n
+ *   temperature [batch] f32 > 0; top_k [batch] i32 (< 1 or >= vocab: off);
+ *   top_p [batch] f32 (>= 1: off; <= 0 keeps nothing)
+ *   out [batch*n, vocab] dtype, may be the same buffer as logits
+ * p = softmax(x / T) per row; entries rank by p descending, lower index
+ * first; the entry of rank r is kept iff r < top_k and the mass of the
+ * entries ranked above it is < top_p.  out holds the kept logits unchanged
+ * and -inf elsewhere, so softmax(out / T) is the renormalised distribution
+ * that spec_accept_sample / spec_accept_target_only then read with the same
+ * temperature.  A greedy request in a sampled batch is top_k = 1.  Masses
+ * are float32 exponentials summed in float64: a top-p decision within ~1e-6
+ * of top_p may differ from an exact evaluation.  vocab <= 524288 (else
+ * SPEC_ERR_UNSUPPORTED).  Five launches (seven for f32) on `stream`.
+ * workspace: spec_sampling_filter_workspace_size(batch, n, vocab) bytes,
+ *   16-byte aligned, any contents.
+ */
+size_t spec_sampling_filter_workspace_size(int batch, int num_draft_tokens, int64_t vocab);
+int spec_sampling_filter(int batch, int num_draft_tokens, int64_t vocab, int dtype,
+                         const void *logits, const float *temperature, const int32_t *top_k,
+                         const float *top_p, void *out, void *workspace, size_t workspace_bytes,
+                         int32_t *dev_status, spec_stream_t stream);
 
 /*
  * FULL tree mask.  [P1] 三种 mask 形态 (FULL_MASK) and the fill_prefix_mask
