@@ -19,11 +19,12 @@ operation, the GPU time of that operation alone: a graph holding the
 operation for every copy, replayed between two HIP events on the stream the
 kernels run on.
 
-Four operations are timed the same way as extra operations
+Five operations are timed the same way as extra operations
 (``extra_op_ms``), not part of the step: the target-only tree accept (the
 sibling-mass rule with thresholds 1, 1), the draft loop's selection (one
 draft-step call per draft step over the workload's draft logits, the path
-scores chained from call to call), the FULL tree mask with its prefix
+scores chained from call to call), the top-k / top-p pre-pass over the
+verify logits (top_k 50, top_p 0.9), the FULL tree mask with its prefix
 filled, and the paged draft-branch planning (prefix-tail duplication into
 the branches' pages of a one-layer draft KV pool, draft write slots).
 
@@ -180,6 +181,10 @@ def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target=None, ws_draft=
                               x.dparents, x.dnext_scores, x.dnext_tokens, workspace=ws_draft,
                               dev_status=x.status)
 
+    def sampling_filter():
+        S.spec_sampling_filter(b, n, cfg.vocab, code, x.tl, x.temperature, mem["top_k"],
+                               mem["top_p"], mem["filtered"], dev_status=x.status)
+
     def full_mask():
         S.spec_full_mask(b, n, x.seq_lens, cfg_max_len(cfg), x.tree_mask, True, mem["full_mask"],
                          dev_status=x.status)
@@ -191,8 +196,8 @@ def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target=None, ws_draft=
                                    mem["branch_pages"] if cfg.topk > 1 else None,
                                    mem["per_branch"], mem["draft_loc"], dev_status=x.status)
 
-    return [build, attention, greedy, sample, compact, target_only, draft_steps, full_mask,
-            plan_branches]
+    return [build, attention, greedy, sample, compact, target_only, draft_steps, sampling_filter,
+            full_mask, plan_branches]
 
 
 def run_ops(S, cfg, x, ws_attn, ws_greedy, ws_sample):
@@ -205,8 +210,8 @@ _MAXLEN = {}
 
 
 def memory_side_buffers(torch, S, cfg, w):
-    """Buffers the FULL-mask and branch-planning extra operations share across
-    input copies: the mask output (n * sum(L + n) bytes) and a one-layer draft
+    """Buffers the pre-pass, FULL-mask and branch-planning extra operations
+    share across input copies: the filtered logits, the mask output (n * sum(L + n) bytes) and a one-layer draft
     KV pool holding the target's page ids plus, per request and branch, the
     pages of a branch region (ids after the target's)."""
     b, n, ps, k = cfg.batch, cfg.num_draft_tokens, cfg.page_size, cfg.topk
@@ -224,6 +229,9 @@ def memory_side_buffers(torch, S, cfg, w):
         "per_branch": per_branch,
         "branch_pages": torch.arange(used, pages, dtype=torch.int32, device="cuda"),
         "draft_loc": torch.zeros(b * k * cfg.num_steps, dtype=torch.int32, device="cuda"),
+        "top_k": torch.full((b,), 50, dtype=torch.int32, device="cuda"),
+        "top_p": torch.full((b,), 0.9, dtype=torch.float32, device="cuda"),
+        "filtered": torch.empty(b * n * cfg.vocab * eb, dtype=torch.uint8, device="cuda"),
     }
     return mem
 
@@ -233,7 +241,8 @@ def cfg_max_len(cfg):
 
 
 OPS = ("build_tree", "verify_attention", "accept_greedy", "accept_sample", "compact_kv")
-EXTRA_OPS = ("accept_target_only", "draft_steps", "full_mask", "plan_draft_branches")
+EXTRA_OPS = ("accept_target_only", "draft_steps", "sampling_filter", "full_mask",
+             "plan_draft_branches")
 
 
 def cpu_baseline(cfg, w, tl, dl, budget_s):
@@ -505,6 +514,7 @@ def main():
         "extra_op_ms": extra_ms,
         "accept_target_only_sweep_gbs": sweep_g / (extra_ms["accept_target_only"] * 1e-3) / 1e9,
         "draft_step_calls": cfg.num_steps,
+        "sampling_filter_gbs": 2 * sweep_g / (extra_ms["sampling_filter"] * 1e-3) / 1e9,
         "full_mask_bytes": mem["full_bytes"],
         "full_mask_write_gbs": mem["full_bytes"] / (extra_ms["full_mask"] * 1e-3) / 1e9,
         "draft_steps_sweep_gbs": draft_bytes / (extra_ms["draft_steps"] * 1e-3) / 1e9,

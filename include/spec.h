@@ -372,16 +372,12 @@ int spec_compact_kv(int batch, int num_draft_tokens, int accept_width, int num_l
  * that spec_accept_sample / spec_accept_target_only then read with the same
  * temperature.  A greedy request in a sampled batch is top_k = 1.  Masses
  * are float32 exponentials summed in float64: a top-p decision within ~1e-6
- * of top_p may differ from an exact evaluation.  vocab <= 524288 (else
- * SPEC_ERR_UNSUPPORTED).  Five launches (seven for f32) on `stream`.
- * workspace: spec_sampling_filter_workspace_size(batch, n, vocab) bytes,
- *   16-byte aligned, any contents.
+ * of top_p may differ from an exact evaluation.  vocab <= 2^31 - 1.  One
+ * launch on `stream`, no workspace.
  */
-size_t spec_sampling_filter_workspace_size(int batch, int num_draft_tokens, int64_t vocab);
 int spec_sampling_filter(int batch, int num_draft_tokens, int64_t vocab, int dtype,
                          const void *logits, const float *temperature, const int32_t *top_k,
-                         const float *top_p, void *out, void *workspace, size_t workspace_bytes,
-                         int32_t *dev_status, spec_stream_t stream);
+                         const float *top_p, void *out, int32_t *dev_status, spec_stream_t stream);
 
 /*
  * FULL tree mask.  [P1] 三种 mask 形态 (FULL_MASK) and the fill_prefix_mask

@@ -147,17 +147,15 @@ def test_host_errors_before_launch():
     assert ds(0, 4, 3, 1, 1000, 0, *([P0] * 8), 0, P0, P0) == 0
     sf = lib.spec_sampling_filter
     sf.restype = I
-    sf.argtypes = [I, I, ctypes.c_int64, I] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t,
-                                                                      ctypes.c_void_p, ctypes.c_void_p]
-    f6 = [ctypes.c_void_p(0x1000)] * 6
-    assert sf(1, 4, 1000, 9, *f6, big, P0, P0) == -3
-    assert sf(1, 4, 524289, 0, *f6, big, P0, P0) == -4      # 65 chunks
-    assert sf(1, 0, 1000, 0, *f6, big, P0, P0) == -2
-    n6 = list(f6)
-    n6[2] = P0
-    assert sf(1, 4, 1000, 0, *n6, big, P0, P0) == -1
-    assert sf(1, 4, 1000, 0, *f6, 8, P0, P0) == -5
-    assert sf(0, 4, 1000, 0, *([P0] * 6), 0, P0, P0) == 0
+    sf.argtypes = [I, I, ctypes.c_int64, I] + [ctypes.c_void_p] * 7
+    f5 = [ctypes.c_void_p(0x1000)] * 5
+    assert sf(1, 4, 1000, 9, *f5, P0, P0) == -3
+    assert sf(1, 4, 1 << 31, 0, *f5, P0, P0) == -4
+    assert sf(1, 0, 1000, 0, *f5, P0, P0) == -2
+    n5 = list(f5)
+    n5[2] = P0
+    assert sf(1, 4, 1000, 0, *n5, P0, P0) == -1
+    assert sf(0, 4, 1000, 0, *([P0] * 5), P0, P0) == 0
     fm = lib.spec_full_mask
     fm.restype = I
     fm.argtypes = [I, I, ctypes.c_void_p, I, ctypes.c_void_p, I, ctypes.c_void_p, ctypes.c_int64,

@@ -51,11 +51,8 @@ def _gpu_filter(logits, dtype, b, n, V, k, p, t, in_place=False):
     code = S.SPEC_BF16 if dtype == "bf16" else S.SPEC_F32
     x = G.dev(logits)
     out = x if in_place else torch.empty_like(x)
-    ws = torch.empty(S.spec_sampling_filter_workspace_size(b, n, V), dtype=torch.uint8,
-                     device="cuda")
     st = G.status()
-    S.spec_sampling_filter(b, n, V, code, x, G.dev(t), G.dev(k), G.dev(p), out, workspace=ws,
-                           dev_status=st)
+    S.spec_sampling_filter(b, n, V, code, x, G.dev(t), G.dev(k), G.dev(p), out, dev_status=st)
     torch.cuda.synchronize()
     res = G.host(out, np.uint16 if dtype == "bf16" else None)
     return res.reshape(b * n, V), int(G.host(st)[0])
