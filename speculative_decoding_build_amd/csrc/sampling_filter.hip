@@ -43,9 +43,25 @@ __device__ __forceinline__ uint32_t value_key(float v) {
     return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
 }
 
+constexpr int kCand = 1024;                // candidates the fast path ranks
+constexpr int kWaveTop = 8;                // tau: the least of the waves' 8th largest thread maxima
+
 struct RowShared {
-    uint32_t cnt[kMaxBins];
-    double mass[kMaxBins];
+    union {
+        struct {
+            uint32_t cnt[kMaxBins];
+            double mass[kMaxBins];
+        };
+        struct {
+            uint64_t tk[kRT];              // each thread's largest key
+            uint64_t ck[kCand];            // candidates: keys >= tau, their masses
+            double cm[kCand];
+            uint64_t sk[kCand];            // the candidates by rank
+            double sm[kCand];
+        };
+    };
+    uint64_t w8[kRW];
+    int nc, rmin;
     uint32_t wc[kRW];
     double wm[kRW];
     float wf[kRW];
@@ -187,26 +203,48 @@ __global__ __launch_bounds__(kRT) void filter_row_kernel(
     char *rout = static_cast<char *>(out) + row * V * eb;
     float x[8];
 
-    // pass 1: the row max
+    // pass 1: the row max and each thread's largest 64-bit key (value
+    // bits, then the complemented index: unique, larger = ranked higher)
     float m = -INFINITY;
+    uint64_t tk = 0;
     for (int64_t t0 = 0; t0 < V; t0 += kTile) {
-        load8<DT>(rin, t0 + tid * 8, V, vec_ok, x);
+        const int64_t i0 = t0 + tid * 8;
+        load8<DT>(rin, i0, V, vec_ok, x);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m = fmaxf(m, x[j]);
+        for (int j = 0; j < 8; ++j) {
+            if (i0 + j < V) {
+                m = fmaxf(m, x[j]);
+                const uint64_t k64 = ((uint64_t)value_key(x[j]) << 32) |
+                                     (uint32_t)(0xFFFFFFFFu - (uint32_t)(i0 + j));
+                tk = k64 > tk ? k64 : tk;
+            }
+        }
     }
     m = wave_max(m);
     if (lane == 0) S.wf[wave] = m;
-    for (int i = tid; i < kMaxBins; i += kRT) {
-        S.cnt[i] = 0;
-        S.mass[i] = 0.0;
+    S.tk[tid] = tk;
+    if (tid < kRW) S.w8[tid] = 0;
+    if (tid == 0) {
+        S.nc = 0;
+        S.rmin = INT_MAX;
     }
     __syncthreads();
     m = S.wf[0];
     for (int w = 1; w < kRW; ++w) m = fmaxf(m, S.wf[w]);
     const Scale2 scl = make_scale2(m, T);
+    // tau: the least of the waves' 8th largest thread maxima, so at least
+    // 8 x 16 entries are >= tau
+    {
+        int r = 0;
+        const uint64_t *wk = S.tk + wave * SPEC_WAVE;
+        for (int u = 0; u < SPEC_WAVE; ++u) r += wk[u] > tk;
+        if (tk != 0 && r == kWaveTop - 1) S.w8[wave] = tk;
+    }
+    __syncthreads();
+    uint64_t tau = S.w8[0];
+    for (int w = 1; w < kRW; ++w) tau = S.w8[w] < tau ? S.w8[w] : tau;
 
-    // pass 2: Z and the histogram of the top 12 key bits
-    constexpr int kB1 = 12;
+    // pass 2: Z and the candidates (entries with key >= tau)
     double z = 0.0;
     for (int64_t t0 = 0; t0 < V; t0 += kTile) {
         const int64_t i0 = t0 + tid * 8;
@@ -216,9 +254,15 @@ __global__ __launch_bounds__(kRT) void filter_row_kernel(
             if (i0 + j < V) {
                 const float e = m == -INFINITY ? 0.f : exp2_scaled(x[j], scl);
                 z += (double)e;
-                const uint32_t d = (value_key(x[j]) >> (32 - KEYBITS)) >> (KEYBITS - kB1);
-                atomicAdd(&S.cnt[d], 1u);
-                atomicAdd(&S.mass[d], (double)e);
+                const uint64_t k64 = ((uint64_t)value_key(x[j]) << 32) |
+                                     (uint32_t)(0xFFFFFFFFu - (uint32_t)(i0 + j));
+                if (k64 >= tau) {
+                    const int slot = atomicAdd(&S.nc, 1);
+                    if (slot < kCand) {
+                        S.ck[slot] = k64;
+                        S.cm[slot] = (double)e;
+                    }
+                }
             }
         }
     }
@@ -227,18 +271,80 @@ __global__ __launch_bounds__(kRT) void filter_row_kernel(
     __syncthreads();
     z = 0.0;
     for (int w = 0; w < kRW; ++w) z += S.wm[w];
+    const int nc = S.nc;
     __syncthreads();
     const double tpz = tpf < 1.f ? (double)tpf * z : INFINITY;
+
+    // fast path: the candidates are the top nc entries of the row; when the
+    // kept set ends among them its last entry's key is the cutoff
+    bool fast = false, keep_all = k == 0 && !(tpz < INFINITY);
+    uint64_t cutoff = 0;
+    if (!keep_all && nc <= kCand) {
+        for (int q = tid; q < nc; q += kRT) {
+            const uint64_t mine = S.ck[q];
+            int r = 0;
+            for (int u = 0; u < nc; ++u) r += S.ck[u] > mine;
+            S.sk[r] = mine;
+            S.sm[r] = S.cm[q];
+        }
+        __syncthreads();
+        // inclusive mass by rank (thread t holds rank t), then the last kept
+        // rank: min(top_k - 1, the first rank whose inclusive mass reaches
+        // top_p * Z)
+        double v = tid < nc ? S.sm[tid] : 0.0;
+#pragma unroll
+        for (int o = 1; o < SPEC_WAVE; o <<= 1) {
+            const double u = __shfl_up(v, o, SPEC_WAVE);
+            if (lane >= o) v += u;
+        }
+        if (lane == 63) S.wm[wave] = v;
+        __syncthreads();
+        for (int w = 0; w < wave; ++w) v += S.wm[w];
+        if (tid < nc && ((k > 0 && tid + 1 >= k) || v >= tpz)) atomicMin(&S.rmin, tid);
+        __syncthreads();
+        const int rstar = S.rmin;
+        if (rstar < nc) {
+            fast = true;
+            cutoff = S.sk[rstar];
+        } else if (nc == V) {
+            fast = true;
+            keep_all = true;
+        }
+        __syncthreads();
+    }
+
+    if (!fast && !keep_all) {
+        // the first level's histogram (top 12 key bits)
+        for (int i = tid; i < kMaxBins; i += kRT) {
+            S.cnt[i] = 0;
+            S.mass[i] = 0.0;
+        }
+        __syncthreads();
+        for (int64_t t0 = 0; t0 < V; t0 += kTile) {
+            const int64_t i0 = t0 + tid * 8;
+            load8<DT>(rin, i0, V, vec_ok, x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (i0 + j < V) {
+                    const float e = m == -INFINITY ? 0.f : exp2_scaled(x[j], scl);
+                    const uint32_t d = (value_key(x[j]) >> (32 - KEYBITS)) >> (KEYBITS - 12);
+                    atomicAdd(&S.cnt[d], 1u);
+                    atomicAdd(&S.mass[d], (double)e);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    constexpr int kB1 = 12;
 
     uint32_t cb = 0;                       // entries above the current range
     double mb = 0.0;                       // their mass
     uint32_t prefix = 0;
     int done_bits = 0;
     uint32_t n_tie = 0;
-    bool keep_all = false;
     int nb = 1 << kB1;
     int bits = kB1;
-    while (true) {
+    while (!fast && !keep_all) {
         uint32_t ac, n_in;
         double am;
         const int pick = find_cut(S, nb, k, tpz, cb, mb, ac, am, n_in);
@@ -280,7 +386,7 @@ __global__ __launch_bounds__(kRT) void filter_row_kernel(
     // how many entries equal to v are kept: tie i (index order) iff
     // cb + i < top_k and mb + i * e(v) < top_p * Z
     uint32_t keep_tie = n_tie;
-    if (!keep_all) {
+    if (!fast && !keep_all) {
         if (k > 0) keep_tie = min(keep_tie, (uint32_t)k - cb);
         if (tpz < INFINITY) {
             const uint32_t vb = prefix << (32 - KEYBITS);
@@ -297,7 +403,7 @@ __global__ __launch_bounds__(kRT) void filter_row_kernel(
             keep_tie = min(keep_tie, cp);
         }
     }
-    const bool need_rank = !keep_all && keep_tie < n_tie;
+    const bool need_rank = !fast && !keep_all && keep_tie < n_tie;
 
     // last pass: the output, ties ranked in index order
     uint32_t rank0 = 0;
@@ -309,8 +415,11 @@ __global__ __launch_bounds__(kRT) void filter_row_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t key = value_key(x[j]) >> (32 - KEYBITS);
-            tie[j] = !keep_all && key == prefix && i0 + j < V;
-            keep[j] = keep_all || key > prefix || (tie[j] && !need_rank);
+            tie[j] = !fast && !keep_all && key == prefix && i0 + j < V;
+            keep[j] = keep_all || (!fast && (key > prefix || (tie[j] && !need_rank)));
+            if (fast && !keep_all)
+                keep[j] = (((uint64_t)value_key(x[j]) << 32) |
+                           (uint32_t)(0xFFFFFFFFu - (uint32_t)(i0 + j))) >= cutoff;
             mine += tie[j];
         }
         if (need_rank) {
