@@ -323,7 +323,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path "
-              "shards by request and by KV head with no exchange, see the design notes.",
+              "would shard by request and by KV head with no exchange between GPUs.",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -16,7 +16,7 @@ Sources (web pages, cited by title and section):
   [P4] "Speculative Decoding" (sglang-internals book, part 3, execution model)
   [P5] "把投机采样讲透:以 SGLang 中的 EAGLE-2 为例"
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent:
   * torch.topk's order among equal scores is unstated: rank by (score
     descending, flat index ascending).
   * A node's parent is found through the parent list as
