@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kThreads) void compact_kv_kernel(
     const int b = blockIdx.x;
     const int layer = blockIdx.y;
     const int tid = threadIdx.x;
-    // round 1: the accepted row of move tid, the length, the sequence length
+    // first load round: the accepted row of move tid, the length, the sequence length
     // and (for the free list) verify slot tid, all in flight together
     const int row_j = tid < s1 ? accept_index[(int64_t)b * s1 + tid] : -1;
     const int own_slot = (layer == 0 && tid < n) ? out_cache_loc[(int64_t)b * n + tid] : -1;
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void compact_kv_kernel(
     if (acc < 0) { acc = 0; err |= SPEC_ST_RANGE; }
     if (acc > s1) { acc = s1; err |= SPEC_ST_RANGE; }
     if (tid == 0) s_err = 0;
-    // round 2: thread j resolves move j: source = verify slot of accepted row
+    // second load round: thread j resolves move j: source = verify slot of accepted row
     // j, target = slot of sequence position L + j (-1 when skipped)
     if (tid < s1) {
         int64_t src = -1, tgt = -1;
