@@ -422,7 +422,8 @@ int spec_full_mask(int batch, int num_draft_tokens, const int32_t *seq_lens, int
  *       be NULL.
  *   k_pool, v_pool [num_layers, num_slots, num_kv_heads, head_dim] dtype,
  *       updated in place (16-byte aligned; a row's bytes a multiple of 16,
- *       else SPEC_ERR_UNSUPPORTED); page ids lie in [0, num_slots / page_size)
+ *       else SPEC_ERR_UNSUPPORTED); page ids lie in [0, num_slots / page_size);
+ *       num_slots <= 2^31 - 1 (else SPEC_ERR_UNSUPPORTED)
  *   page_table [batch, max_pages] i32
  * Output: out_cache_loc [batch, topk, num_steps] i32, the slot draft step s
  * of branch j writes (-1 and SPEC_ST_RANGE where a page id is out of

@@ -245,6 +245,7 @@ extern "C" int spec_plan_draft_branches(int batch, int topk, int num_steps, int 
         return SPEC_ERR_SHAPE;
     const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * (dtype == SPEC_BF16 ? 2 : 4);
     if (row_bytes % 16 != 0) return SPEC_ERR_UNSUPPORTED;
+    if (num_slots > INT_MAX) return SPEC_ERR_UNSUPPORTED;    // slots are written as int32
     if (batch == 0) return SPEC_OK;
     if (!k_pool || !v_pool || !seq_lens || !page_table || !out_cache_loc ||
         (topk > 1 && !branch_pages))

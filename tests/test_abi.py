@@ -177,6 +177,7 @@ def test_host_errors_before_launch():
     assert pb(1, 2, 5, 4, 1, 1, 6, 0, *a6, 1024, al16, al16, 8, al16, 2, al16, P0, P0) == -4  # 24-byte rows
     assert pb(1, 2, 5, 4, 1, 8, 128, 1, *a6, 1024, al16, al16, 8, P0, 2, al16, P0, P0) == -1
     assert pb(0, 2, 5, 4, 1, 8, 128, 1, P0, P0, 1024, P0, P0, 8, P0, 2, P0, P0, P0) == 0
+    assert pb(1, 2, 5, 4, 1, 8, 128, 1, *a6, 1 << 31, al16, al16, 8, al16, 2, al16, P0, P0) == -4
     ck = lib.spec_compact_kv
     ck.restype = I
     ck.argtypes = [I] * 8 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, I] + [ctypes.c_void_p] * 9 + [ctypes.c_void_p]
