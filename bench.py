@@ -183,7 +183,8 @@ def op_calls(S, cfg, x, ws_attn, ws_greedy, ws_sample, ws_target=None, ws_draft=
 
     def sampling_filter():
         S.spec_sampling_filter(b, n, cfg.vocab, code, x.tl, x.temperature, mem["top_k"],
-                               mem["top_p"], mem["filtered"], dev_status=x.status)
+                               mem["top_p"], mem["filtered"], workspace=mem["filter_ws"],
+                               dev_status=x.status)
 
     def full_mask():
         S.spec_full_mask(b, n, x.seq_lens, cfg_max_len(cfg), x.tree_mask, True, mem["full_mask"],
@@ -211,7 +212,7 @@ _MAXLEN = {}
 
 def memory_side_buffers(torch, S, cfg, w):
     """Buffers the pre-pass, FULL-mask and branch-planning extra operations
-    share across input copies: the filtered logits, the mask output (n * sum(L + n) bytes) and a one-layer draft
+    share across input copies: the filtered logits and the pre-pass workspace, the mask output (n * sum(L + n) bytes) and a one-layer draft
     KV pool holding the target's page ids plus, per request and branch, the
     pages of a branch region (ids after the target's)."""
     b, n, ps, k = cfg.batch, cfg.num_draft_tokens, cfg.page_size, cfg.topk
@@ -232,6 +233,8 @@ def memory_side_buffers(torch, S, cfg, w):
         "top_k": torch.full((b,), 50, dtype=torch.int32, device="cuda"),
         "top_p": torch.full((b,), 0.9, dtype=torch.float32, device="cuda"),
         "filtered": torch.empty(b * n * cfg.vocab * eb, dtype=torch.uint8, device="cuda"),
+        "filter_ws": torch.empty(max(256, S.spec_sampling_filter_workspace_size(b, n, cfg.vocab)),
+                                 dtype=torch.uint8, device="cuda"),
     }
     return mem
 

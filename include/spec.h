@@ -372,12 +372,20 @@ int spec_compact_kv(int batch, int num_draft_tokens, int accept_width, int num_l
  * that spec_accept_sample / spec_accept_target_only then read with the same
  * temperature.  A greedy request in a sampled batch is top_k = 1.  Masses
  * are float32 exponentials summed in float64: a top-p decision within ~1e-6
- * of top_p may differ from an exact evaluation.  vocab <= 2^31 - 1.  One
- * launch on `stream`, no workspace.
+ * of top_p may differ from an exact evaluation.  vocab <= 2^31 - 1.
+ * workspace: spec_sampling_filter_workspace_size(batch, n, vocab) bytes,
+ *   16-byte aligned, any contents (NULL allowed when that size is 0: vocab
+ *   <= 8192 or > 524288); calls in stream order may share one.  For 8192 <
+ *   vocab <= 524288 three kernels are launched on `stream` (rows x chunks of
+ *   <= 8192 entries, then one workgroup per row, then rows x chunks), else
+ *   one workgroup per row.  A row with top_k in [1, 64] is finished from
+ *   the chunks' top entries; others may be searched whole (slower).
  */
+size_t spec_sampling_filter_workspace_size(int batch, int num_draft_tokens, int64_t vocab);
 int spec_sampling_filter(int batch, int num_draft_tokens, int64_t vocab, int dtype,
                          const void *logits, const float *temperature, const int32_t *top_k,
-                         const float *top_p, void *out, int32_t *dev_status, spec_stream_t stream);
+                         const float *top_p, void *out, void *workspace, size_t workspace_bytes,
+                         int32_t *dev_status, spec_stream_t stream);
 
 /*
  * FULL tree mask.  [P1] 三种 mask 形态 (FULL_MASK) and the fill_prefix_mask

@@ -656,7 +656,9 @@ def filter_logits(logits, dtype, temperature, top_k, top_p, band=1e-6):
     i.e. the smallest top set reaching mass top_p.  Both rules are decided on
     the same p, then one renormalisation: the kept logits are returned as
     they were and the others as -inf, so softmax(filtered / T) is the
-    renormalised distribution.  A greedy request is top_k = 1.
+    renormalised distribution.  A greedy request is top_k = 1.  A row whose
+    logits are all -inf has no distribution: the top-p rule does nothing
+    there and top_k alone decides.
 
     logits [rows, V] (float32 or bf16 bit patterns); temperature, top_k,
     top_p: per row.  Returns (filtered logits in the input's storage type,
@@ -670,11 +672,15 @@ def filter_logits(logits, dtype, temperature, top_k, top_p, band=1e-6):
     for i in range(rows):
         xi = x[i]
         T = float(temperature[i])
-        e = np.exp((xi - xi.max()) / T)
-        p = e / e.sum()
-        order = np.lexsort((np.arange(V), -xi))     # x descending, index ascending
         k = int(top_k[i])
         tp = float(top_p[i])
+        order = np.lexsort((np.arange(V), -xi))     # x descending, index ascending
+        if xi.max() == -np.inf:
+            tp = 1.0                                # no distribution: top-p off
+            p = np.zeros(V)
+        else:
+            e = np.exp((xi - xi.max()) / T)
+            p = e / e.sum()
         before = 0.0
         for r, j in enumerate(order):
             keep = True

@@ -49,7 +49,7 @@ EXPORTS = ("spec_version", "spec_status_string", "spec_mask_word_bytes", "spec_b
            "spec_accept_workspace_size", "spec_accept_greedy", "spec_accept_sample",
            "spec_accept_target_only_workspace_size", "spec_accept_target_only",
            "spec_draft_step_workspace_size", "spec_draft_step",
-           "spec_sampling_filter", "spec_full_mask",
+           "spec_sampling_filter_workspace_size", "spec_sampling_filter", "spec_full_mask",
            "spec_plan_draft_branches",
            "spec_compact_kv")
 
@@ -85,7 +85,8 @@ _decl("spec_accept_target_only", _I, _I, _I, _I, _I64, _I, _P, _P, _F, _F, _P, _
       _P, _P, _P, _P, _P, _SZ, _P, _P)
 _decl("spec_draft_step_workspace_size", _SZ, _I, _I, _I64)
 _decl("spec_draft_step", _I, _I, _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P)
-_decl("spec_sampling_filter", _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P)
+_decl("spec_sampling_filter_workspace_size", _SZ, _I, _I, _I64)
+_decl("spec_sampling_filter", _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _SZ, _P, _P)
 _decl("spec_full_mask", _I, _I, _I, _P, _I, _P, _I, _P, _I64, _P, _P)
 _decl("spec_plan_draft_branches", _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I64, _P, _P, _I, _P,
       _I, _P, _P, _P)
@@ -358,18 +359,28 @@ def spec_draft_step(batch, topk, num_steps, step, vocab, dtype, draft_logits, br
                                                     *args, _stream(stream)))
 
 
+def spec_sampling_filter_workspace_size(batch, num_draft_tokens, vocab) -> int:
+    return _lib.spec_sampling_filter_workspace_size(batch, num_draft_tokens, vocab)
+
+
 def spec_sampling_filter(batch, num_draft_tokens, vocab, dtype, logits, temperature, top_k,
-                         top_p, out, dev_status=None, stream=None):
+                         top_p, out, workspace=None, workspace_bytes=None, dev_status=None,
+                         stream=None):
     dev = _device()
     rows = batch * num_draft_tokens
     lb = rows * vocab * _ELEM.get(dtype, 4)
     none = batch == 0
+    need_ws = spec_sampling_filter_workspace_size(batch, num_draft_tokens, vocab)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [
         _ptr(logits, "logits", dev, nbytes=lb, optional=none),
         _ptr(temperature, "temperature", dev, nbytes=batch * 4, optional=none),
         _ptr(top_k, "top_k", dev, nbytes=batch * 4, optional=none),
         _ptr(top_p, "top_p", dev, nbytes=batch * 4, optional=none),
         _ptr(out, "out", dev, nbytes=lb, optional=none),
+        _ptr(workspace, "workspace", dev, nbytes=need_ws, optional=need_ws == 0),
+        workspace_bytes,
         _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
     ]
     _check("spec_sampling_filter", _lib.spec_sampling_filter(batch, num_draft_tokens, vocab, dtype,

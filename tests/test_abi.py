@@ -147,15 +147,26 @@ def test_host_errors_before_launch():
     assert ds(0, 4, 3, 1, 1000, 0, *([P0] * 8), 0, P0, P0) == 0
     sf = lib.spec_sampling_filter
     sf.restype = I
-    sf.argtypes = [I, I, ctypes.c_int64, I] + [ctypes.c_void_p] * 7
+    sf.argtypes = ([I, I, ctypes.c_int64, I] + [ctypes.c_void_p] * 6
+                   + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p])
     f5 = [ctypes.c_void_p(0x1000)] * 5
-    assert sf(1, 4, 1000, 9, *f5, P0, P0) == -3
-    assert sf(1, 4, 1 << 31, 0, *f5, P0, P0) == -4
-    assert sf(1, 0, 1000, 0, *f5, P0, P0) == -2
+    assert sf(1, 4, 1000, 9, *f5, P0, 0, P0, P0) == -3
+    assert sf(1, 4, 1 << 31, 0, *f5, P0, 0, P0, P0) == -4
+    assert sf(1, 0, 1000, 0, *f5, P0, 0, P0, P0) == -2
     n5 = list(f5)
     n5[2] = P0
-    assert sf(1, 4, 1000, 0, *n5, P0, P0) == -1
-    assert sf(0, 4, 1000, 0, *([P0] * 5), P0, P0) == 0
+    assert sf(1, 4, 1000, 0, *n5, P0, 0, P0, P0) == -1
+    assert sf(0, 4, 1000, 0, *([P0] * 5), P0, 0, P0, P0) == 0
+    sfw = lib.spec_sampling_filter_workspace_size
+    sfw.restype = ctypes.c_size_t
+    sfw.argtypes = [I, I, ctypes.c_int64]
+    need = sfw(1, 4, 128256)      # 16 chunks of 8016 entries per row
+    assert need == 256 + 4 * 16 * 16 + 4 * 16 * 64 * 8
+    assert sfw(1, 4, 8192) == 0 and sfw(1, 4, 524289) == 0 and sfw(0, 4, 128256) == 0
+    assert sfw(1, 4, 8193) > 0 and sfw(1, 4, 524288) > 0
+    assert sf(1, 4, 128256, 0, *f5, P0, 0, P0, P0) == -5                 # no workspace
+    assert sf(1, 4, 128256, 0, *f5, ctypes.c_void_p(0x1000), need - 1, P0, P0) == -5
+    assert sf(1, 4, 128256, 0, *f5, ctypes.c_void_p(0x1008), need, P0, P0) == -5   # misaligned
     fm = lib.spec_full_mask
     fm.restype = I
     fm.argtypes = [I, I, ctypes.c_void_p, I, ctypes.c_void_p, I, ctypes.c_void_p, ctypes.c_int64,

@@ -6,7 +6,12 @@ float32 rows; per-request parameter mixes (off, top_k 1, 20, 500, V-1,
 top_p 0.5 / 0.9 / 0.99, both rules together, temperatures 0.3 to 2); rows
 rounded to a few values so that the cutoff falls inside a run of equal
 logits; vocabularies of 100, 8192, 50000, 128256 and 524288 entries; the
-output written over the input.  Bar: the output logits bit-exact, except
+output written over the input.  Above 8192 entries the pre-pass works in
+chunks and finishes a row from their candidates: rows built so that those
+run short (ascending logits, all equal, a flat row under top_p alone) take
+the whole-row search instead, next to rows that do not, at the smallest and
+largest chunked vocabularies and the first one above; the workspace starts
+filled with garbage.  Bar: the output logits bit-exact, except
 rows the oracle flags near a top-p boundary (within 1e-6 of top_p).  Then
 the sampled accept on the filtered logits equals the oracle's sampled accept
 on its filtered logits, and requests with top_k 1 equal the greedy accept.
@@ -52,7 +57,10 @@ def _gpu_filter(logits, dtype, b, n, V, k, p, t, in_place=False):
     x = G.dev(logits)
     out = x if in_place else torch.empty_like(x)
     st = G.status()
-    S.spec_sampling_filter(b, n, V, code, x, G.dev(t), G.dev(k), G.dev(p), out, dev_status=st)
+    ws = torch.full((max(16, S.spec_sampling_filter_workspace_size(b, n, V)),), 0xA5,
+                    dtype=torch.uint8, device="cuda")
+    S.spec_sampling_filter(b, n, V, code, x, G.dev(t), G.dev(k), G.dev(p), out, workspace=ws,
+                           dev_status=st)
     torch.cuda.synchronize()
     res = G.host(out, np.uint16 if dtype == "bf16" else None)
     return res.reshape(b * n, V), int(G.host(st)[0])
@@ -114,6 +122,54 @@ def test_filter_largest_vocabulary_in_place():
     p = np.array([0.9], np.float32)
     t = np.array([1.0], np.float32)
     _check(logits, "bf16", b, n, V, k, p, t, "v524288 in place", in_place=True)
+
+
+def _structured_rows(V, seed):
+    """Rows whose chunk candidates run short next to rows whose do not, with
+    the parameters of each (one row per request)."""
+    rng = np.random.default_rng(seed)
+    normal = rng.standard_normal(V) * 2
+    peaked = rng.standard_normal(V)
+    peaked[rng.integers(0, V, 3)] = [14.0, 13.0, 12.5]
+    rows = [
+        (np.linspace(-4, 4, V), 50, 1.0, 1.0),          # ascending: the last chunk's tops crowd one wave
+        (np.full(V, 0.5), 20, 1.0, 1.0),                # all equal: ranked by index only
+        (normal, 0, 0.6, 1.0),                          # top_p alone, cutoff far down the row
+        (peaked, 0, 0.9, 1.0),                          # top_p alone, cutoff among the first entries
+        (normal, 64, 1.0, 0.8),                         # the largest top_k ranked from the chunks
+        (normal, 65, 0.95, 1.2),                        # just above it
+        (normal, 1, 1.0, 1.0),                          # greedy
+        (np.round(normal), 37, 0.9, 0.7),               # cut inside a run of equal logits
+        (np.full(V, -np.inf), 5, 0.9, 1.0),             # every entry masked
+    ]
+    x = np.stack([r[0] for r in rows]).astype(np.float32)
+    k = np.array([r[1] for r in rows], np.int32)
+    p = np.array([r[2] for r in rows], np.float32)
+    t = np.array([r[3] for r in rows], np.float32)
+    return x, k, p, t
+
+
+@pytest.mark.parametrize("V", [8193, 16385, 128256, 524288, 524289])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_filter_chunked_rows_and_whole_row_fallback(V, dtype):
+    # 524288: the most chunks per row (64); 524289: one workgroup per row
+    x, k, p, t = _structured_rows(V, 11)
+    b = len(k)
+    logits = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    say(f"[filter] chunked V={V} {dtype} rows={b} ws={S.spec_sampling_filter_workspace_size(b, 1, V)}")
+    _check(logits, dtype, b, 1, V, k, p, t, f"chunked V={V} {dtype}", in_place=(V == 16385))
+
+
+def test_filter_workspace_size_and_refusals():
+    # one chunk (<= 8192) and more than 64 chunks (> 524288) need none
+    assert S.spec_sampling_filter_workspace_size(3, 4, 8192) == 0
+    assert S.spec_sampling_filter_workspace_size(3, 4, 524289) == 0
+    assert S.spec_sampling_filter_workspace_size(3, 4, 8193) > 0
+    x = torch.zeros(2 * 9000, dtype=torch.int16, device="cuda")
+    f = torch.ones(2, dtype=torch.float32, device="cuda")
+    kk = torch.ones(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="workspace"):
+        S.spec_sampling_filter(2, 1, 9000, S.SPEC_BF16, x, f, kk, f, x)
 
 
 @pytest.mark.parametrize("cid", [1, 3])

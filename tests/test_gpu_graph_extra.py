@@ -64,6 +64,8 @@ def test_extra_operations_graph_replay():
     ws_to = torch.zeros(S.spec_accept_target_only_workspace_size(b, n, V), dtype=torch.uint8,
                         device="cuda")
     ws_ds = torch.empty(S.spec_draft_step_workspace_size(b, k, V), dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(max(256, S.spec_sampling_filter_workspace_size(b, n, V)), dtype=torch.uint8,
+                       device="cuda")
     topk_d, topp_d = d(np.array([30, 0], np.int32)), d(np.array([1.0, 0.9], np.float32))
 
     def run():
@@ -76,7 +78,7 @@ def test_extra_operations_graph_replay():
                               out["sc"], out["tk"], out["pa"], out["ns"], out["nt"],
                               workspace=ws_ds, dev_status=out["st"])
         S.spec_sampling_filter(b, n, V, code, tl_d, T, topk_d, topp_d, out["filt"],
-                               dev_status=out["st"])
+                               workspace=ws_f, dev_status=out["st"])
         S.spec_full_mask(b, n, seq, int(np.max(w.seq_lens)), words, True, out["mask"],
                          dev_status=out["st"])
         S.spec_plan_draft_branches(b, k, S_, ps, 1, hkv, hd, code, kpool, vpool, pages * ps,

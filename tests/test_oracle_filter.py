@@ -46,6 +46,17 @@ def test_no_filter_is_identity():
     assert kept.all() and np.array_equal(out, x)
 
 
+def test_all_masked_row_keeps_top_k_by_index():
+    """A row of -inf logits has no distribution: top-p removes nothing, top_k
+    keeps the entries of lowest index (equal logits rank by index)."""
+    x = np.full((3, 10), -np.inf, np.float32)
+    _, kept, near = oracle.filter_logits(x, "f32", [1.0] * 3, [4, 0, 1], [0.5, 0.1, 1.0])
+    assert np.flatnonzero(kept[0]).tolist() == [0, 1, 2, 3]
+    assert kept[1].all()
+    assert np.flatnonzero(kept[2]).tolist() == [0]
+    assert not near.any()
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_invariants_of_the_kept_set(seed):
     """Top-k keeps exactly k entries, none smaller than a removed one; top-p
