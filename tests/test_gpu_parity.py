@@ -102,6 +102,44 @@ ALL_KEPT = {
 }
 
 
+# Selection shapes: one ranking round shared by 1024/ceil64(ncand) threads
+# per candidate (36 candidates: 16 ranges of keys; 114: 8; 968: 1) and
+# several rounds above 1024 candidates (1032); plus scores floored to a
+# coarse grid, so that the cut falls inside runs of equal scores (ranked by
+# index).
+SELECT = {
+    "topk4_s3_n10": dict(topk=4, num_steps=3, num_draft_tokens=10),
+    "topk6_s4_n40": dict(topk=6, num_steps=4, num_draft_tokens=40),
+    "topk8_s16_n64": dict(topk=8, num_steps=16, num_draft_tokens=64),
+    "topk8_s17_n64": dict(topk=8, num_steps=17, num_draft_tokens=64),
+}
+
+
+@pytest.mark.parametrize("ties", [False, True])
+@pytest.mark.parametrize("name", list(SELECT))
+def test_build_tree_selection_shapes(name, ties):
+    cfg = W.shrink(W.CONFIGS[3], batch=3, hist=("fixed", 8), vocab=500, **SELECT[name])
+    w = W.make_workload(cfg, 6, attention=False)
+    if ties:
+        # flooring log2(score) to halves keeps a child's score <= its
+        # parent's, and the parent has the smaller flat index, so the kept
+        # set stays closed
+        lg = np.floor(np.log2(np.maximum(w.scores, 1e-30)) * 2.0) / 2.0
+        w.scores = np.exp2(lg).astype(np.float32)
+    t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                          cfg.num_steps, cfg.num_draft_tokens)
+    b, n = cfg.batch, cfg.num_draft_tokens
+    say(f"[build_tree] {name} ties={ties} ncand={cfg.ncand} n={n}")
+    g = G.build_tree(w, mask_mode=S.SPEC_MASK_QLEN_BITS)
+    assert g["status"] == t["status"]
+    np.testing.assert_array_equal(g["selected"][:b * (n - 1)].reshape(b, n - 1), t["selected"])
+    np.testing.assert_array_equal(g["draft_tokens"], t["draft_tokens"])
+    np.testing.assert_array_equal(g["retrieve_next_token"].reshape(b, n), t["retrieve_next_token"])
+    np.testing.assert_array_equal(g["retrieve_next_sibling"].reshape(b, n),
+                                  t["retrieve_next_sibling"])
+    np.testing.assert_array_equal(g["tree_mask"], oracle.pack_mask(t["mask"], S.SPEC_MASK_QLEN_BITS))
+
+
 @pytest.mark.parametrize("name", list(ALL_KEPT))
 def test_build_tree_all_kept(name):
     cfg = W.shrink(W.CONFIGS[3], batch=3, hist=("fixed", 8), vocab=500, **ALL_KEPT[name])
