@@ -361,7 +361,8 @@ int spec_compact_kv(int batch, int num_draft_tokens, int accept_width, int num_l
  * temperature, then top-k / top-p filtering and renormalisation) and [P1]
  * 三条判定路径.
  *
- *   logits [batch*n, vocab] dtype; row i belongs to request i / n
+ *   logits [batch*n, vocab] dtype, finite or -inf (NaN is not defined);
+ *       row i belongs to request i / n
  *   temperature [batch] f32 > 0; top_k [batch] i32 (< 1 or >= vocab: off);
  *   top_p [batch] f32 (>= 1: off; <= 0 keeps nothing)
  *   out [batch*n, vocab] dtype, may be the same buffer as logits
@@ -370,7 +371,8 @@ int spec_compact_kv(int batch, int num_draft_tokens, int accept_width, int num_l
  * entries ranked above it is < top_p.  out holds the kept logits unchanged
  * and -inf elsewhere, so softmax(out / T) is the renormalised distribution
  * that spec_accept_sample / spec_accept_target_only then read with the same
- * temperature.  A greedy request in a sampled batch is top_k = 1.  Masses
+ * temperature.  A greedy request in a sampled batch is top_k = 1.  A row of
+ * -inf logits has no distribution: top_p does nothing there.  Masses
  * are float32 exponentials summed in float64: a top-p decision within ~1e-6
  * of top_p may differ from an exact evaluation.  vocab <= 2^31 - 1.
  * workspace: spec_sampling_filter_workspace_size(batch, n, vocab) bytes,
