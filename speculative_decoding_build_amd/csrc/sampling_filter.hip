@@ -295,11 +295,13 @@ __device__ __forceinline__ bool cut_among(RowShared &S, int nc, int k, double tp
 // and the row's top K keys, merged from the chunks' sorted top-K lists in
 // pairs (an entry's place in a merged pair is its place in its own list
 // plus the entries of the other list above it; equal keys are zero padding
-// and go to the lower list first).  When the kept set ends among the top K
-// (always when 1 <= top_k <= 64) the cutoff goes to dec for the output
-// launch and true is returned; otherwise dec says the row is done here and
-// the caller runs the whole-row search.
-__device__ __forceinline__ bool merge_chunks(RowShared &S, const ChunkHead *__restrict__ heads,
+// and go to the lower list first).  Returns 0 when the row is decided (the
+// kept set ends among the top K, always when 1 <= top_k <= 64, or both
+// rules are off): the cutoff goes to dec for the output launch.  Otherwise
+// dec says the row is done here and the caller searches the row itself:
+// from scratch (1: a chunk had too many candidates) or from the histogram
+// on, with M in S.wf[0] and Z in S.hz (2).
+__device__ __forceinline__ int merge_chunks(RowShared &S, const ChunkHead *__restrict__ heads,
                                              const uint64_t *__restrict__ keys, int nch,
                                              int64_t row, float T, int k, int K, float tpf,
                                              Decision *__restrict__ dec) {
@@ -340,11 +342,11 @@ __device__ __forceinline__ bool merge_chunks(RowShared &S, const ChunkHead *__re
     if (S.over) {
         if (tid == 0) dec[row] = Decision{0, 1u, 0u};
         __syncthreads();
-        return false;
+        return 1;
     }
     if (k == 0 && !(tpz < INFINITY)) {             // both rules off: every entry kept
         if (tid == 0) dec[row] = Decision{0, 0u, 0u};
-        return true;
+        return 0;
     }
     uint64_t *src = S.la, *dst = S.lb;
     for (int L = nch; L > 1; L = (L + 1) / 2) {
@@ -399,7 +401,7 @@ __device__ __forceinline__ bool merge_chunks(RowShared &S, const ChunkHead *__re
     __syncthreads();
     ok = S.over == 0;
     __syncthreads();
-    return ok;
+    return ok ? 0 : 2;
 }
 
 template <int DT, int KEYBITS>
@@ -420,82 +422,93 @@ __global__ __launch_bounds__(kRT) void filter_row_kernel(
     const char *rin = static_cast<const char *>(in) + row * V * eb;
     char *rout = static_cast<char *>(out) + row * V * eb;
     float x[8];
+    bool known = false;                    // M and Z from the chunks
+    float m = -INFINITY;
+    double z = 0.0;
+    int nc = kCand + 1;                    // no candidates: the fast path is skipped
     if (heads != nullptr) {
         const int K = (k >= 1 && k <= kCapK) ? k : kCapK;
-        if (merge_chunks(S, heads, keys, nch, row, T, k, K, tpf, dec)) return;
+        const int st = merge_chunks(S, heads, keys, nch, row, T, k, K, tpf, dec);
+        if (st == 0) return;
+        if (st == 2) {
+            known = true;
+            m = S.wf[0];
+            z = S.hz;
+        }
         __syncthreads();                   // the search below reuses the shared fields
     }
 
-    // pass 1: the row max and each thread's largest 64-bit key (value
-    // bits, then the complemented index: unique, larger = ranked higher)
-    float m = -INFINITY;
-    uint64_t tk = 0;
-    for (int64_t t0 = 0; t0 < V; t0 += kTile) {
-        const int64_t i0 = t0 + tid * 8;
-        load8<DT>(rin, i0, V, vec_ok, x);
+    if (!known) {
+        // pass 1: the row max and each thread's largest 64-bit key (value
+        // bits, then the complemented index: unique, larger = ranked higher)
+        uint64_t tk = 0;
+        for (int64_t t0 = 0; t0 < V; t0 += kTile) {
+            const int64_t i0 = t0 + tid * 8;
+            load8<DT>(rin, i0, V, vec_ok, x);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (i0 + j < V) {
-                m = fmaxf(m, x[j]);
-                const uint64_t k64 = ((uint64_t)value_key(x[j]) << 32) |
-                                     (uint32_t)(0xFFFFFFFFu - (uint32_t)(i0 + j));
-                tk = k64 > tk ? k64 : tk;
+            for (int j = 0; j < 8; ++j) {
+                if (i0 + j < V) {
+                    m = fmaxf(m, x[j]);
+                    const uint64_t k64 = ((uint64_t)value_key(x[j]) << 32) |
+                                         (uint32_t)(0xFFFFFFFFu - (uint32_t)(i0 + j));
+                    tk = k64 > tk ? k64 : tk;
+                }
             }
         }
-    }
-    m = wave_max(m);
-    if (lane == 0) S.wf[wave] = m;
-    S.tk[tid] = tk;
-    if (tid < kRW) S.w8[tid] = 0;
-    if (tid == 0) {
-        S.nc = 0;
-        S.rmin = INT_MAX;
-    }
-    __syncthreads();
-    m = S.wf[0];
-    for (int w = 1; w < kRW; ++w) m = fmaxf(m, S.wf[w]);
-    const Scale2 scl = make_scale2(m, T);
-    // tau: the least of the waves' 8th largest thread maxima, so at least
-    // 8 x 16 entries are >= tau
-    {
-        int r = 0;
-        const uint64_t *wk = S.tk + wave * SPEC_WAVE;
-        for (int u = 0; u < SPEC_WAVE; ++u) r += wk[u] > tk;
-        if (tk != 0 && r == kWaveTop - 1) S.w8[wave] = tk;
-    }
-    __syncthreads();
-    uint64_t tau = S.w8[0];
-    for (int w = 1; w < kRW; ++w) tau = S.w8[w] < tau ? S.w8[w] : tau;
+        m = wave_max(m);
+        if (lane == 0) S.wf[wave] = m;
+        S.tk[tid] = tk;
+        if (tid < kRW) S.w8[tid] = 0;
+        if (tid == 0) {
+            S.nc = 0;
+            S.rmin = INT_MAX;
+        }
+        __syncthreads();
+        m = S.wf[0];
+        for (int w = 1; w < kRW; ++w) m = fmaxf(m, S.wf[w]);
+        const Scale2 scl1 = make_scale2(m, T);
+        // tau: the least of the waves' 8th largest thread maxima, so at least
+        // 8 x 16 entries are >= tau
+        {
+            int r = 0;
+            const uint64_t *wk = S.tk + wave * SPEC_WAVE;
+            for (int u = 0; u < SPEC_WAVE; ++u) r += wk[u] > tk;
+            if (tk != 0 && r == kWaveTop - 1) S.w8[wave] = tk;
+        }
+        __syncthreads();
+        uint64_t tau = S.w8[0];
+        for (int w = 1; w < kRW; ++w) tau = S.w8[w] < tau ? S.w8[w] : tau;
 
-    // pass 2: Z and the candidates (entries with key >= tau)
-    double z = 0.0;
-    for (int64_t t0 = 0; t0 < V; t0 += kTile) {
-        const int64_t i0 = t0 + tid * 8;
-        load8<DT>(rin, i0, V, vec_ok, x);
+        // pass 2: Z and the candidates (entries with key >= tau)
+        for (int64_t t0 = 0; t0 < V; t0 += kTile) {
+            const int64_t i0 = t0 + tid * 8;
+            load8<DT>(rin, i0, V, vec_ok, x);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (i0 + j < V) {
-                const float e = m == -INFINITY ? 0.f : exp2_scaled(x[j], scl);
-                z += (double)e;
-                const uint64_t k64 = ((uint64_t)value_key(x[j]) << 32) |
-                                     (uint32_t)(0xFFFFFFFFu - (uint32_t)(i0 + j));
-                if (k64 >= tau) {
-                    const int slot = atomicAdd(&S.nc, 1);
-                    if (slot < kCand) {
-                        S.ck[slot] = k64;
-                        S.cm[slot] = (double)e;
+            for (int j = 0; j < 8; ++j) {
+                if (i0 + j < V) {
+                    const float e = m == -INFINITY ? 0.f : exp2_scaled(x[j], scl1);
+                    z += (double)e;
+                    const uint64_t k64 = ((uint64_t)value_key(x[j]) << 32) |
+                                         (uint32_t)(0xFFFFFFFFu - (uint32_t)(i0 + j));
+                    if (k64 >= tau) {
+                        const int slot = atomicAdd(&S.nc, 1);
+                        if (slot < kCand) {
+                            S.ck[slot] = k64;
+                            S.cm[slot] = (double)e;
+                        }
                     }
                 }
             }
         }
+        z = wave_sum_d(z);
+        if (lane == 0) S.wm[wave] = z;
+        __syncthreads();
+        z = 0.0;
+        for (int w = 0; w < kRW; ++w) z += S.wm[w];
+        nc = S.nc;
+        __syncthreads();
     }
-    z = wave_sum_d(z);
-    if (lane == 0) S.wm[wave] = z;
-    __syncthreads();
-    z = 0.0;
-    for (int w = 0; w < kRW; ++w) z += S.wm[w];
-    const int nc = S.nc;
-    __syncthreads();
+    const Scale2 scl = make_scale2(m, T);
     // a row of -inf logits (Z = 0) has no distribution: top-p does nothing
     const double tpz = tpf < 1.f && z > 0.0 ? (double)tpf * z : INFINITY;
 
