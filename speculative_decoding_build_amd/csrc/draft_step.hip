@@ -124,8 +124,10 @@ __device__ __forceinline__ void load_elems(const void *base, int64_t start, int6
     }
 }
 
-constexpr int kRegPer = 2;                 // chunk items per merge thread with keys in registers
+constexpr int kRegPer = 2;                 // register path: up to kRegPer x 256 chunk items a request
 constexpr int kRegChunks = kRegPer * kThreads;
+constexpr int kMT = 512;                   // threads of a merge workgroup (one item each in registers)
+constexpr int kMW = kMT / SPEC_WAVE;
 
 struct ChunkShared {
     uint64_t tkey[kThreads];               // thread maxima
@@ -300,28 +302,28 @@ __device__ void finish_request(const DraftArgs &A, MergeShared<CAP> &S, int r, i
 
 // Request r's chunk items (rows x chunks, at most CAP of them) -> each
 // row's max, normaliser and top-k keys; then the step's outputs.  REG: at
-// most kRegPer items per thread, whose keys stay in registers; otherwise
-// the candidate chunks' keys are read again.
+// most kRegChunks items, one per thread, whose keys stay in registers;
+// otherwise the candidate chunks' keys are read again.
 template <int CAP, bool REG>
 __device__ void merge_request(const DraftArgs &A, MergeShared<CAP> &S, int r) {
-    constexpr int P = kRegPer;
+    constexpr int P = kRegChunks / kMT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = A.topk, R = A.rows, nch = A.nchunks, nq = R * nch, nw = 2 + K;
     const uint64_t *items = A.items + (int64_t)r * nq * kItemWords;
     float bsv = 0.f;
     if (wave == 0 && A.step > 0 && lane < K * K) bsv = A.branch_scores[(int64_t)r * K + lane / K];
     uint64_t w[P][kItemWords];
-    for (int q0 = 0; q0 < nq; q0 += P * kThreads) {
+    for (int q0 = 0; q0 < nq; q0 += P * kMT) {
 #pragma unroll
         for (int i = 0; i < P; ++i) {
-            const int q = q0 + tid + i * kThreads;
+            const int q = q0 + tid + i * kMT;
 #pragma unroll
             for (int u = 0; u < kItemWords; ++u)
                 w[i][u] = (q < nq && u < nw) ? items[(int64_t)q * kItemWords + u] : 0;
         }
 #pragma unroll
         for (int i = 0; i < P; ++i) {
-            const int q = q0 + tid + i * kThreads;
+            const int q = q0 + tid + i * kMT;
             if (q < nq) {
                 S.cs[q] = __builtin_bit_cast(double, w[i][1]);
                 S.bk[q] = w[i][2];
@@ -336,7 +338,7 @@ __device__ void merge_request(const DraftArgs &A, MergeShared<CAP> &S, int r) {
     if (wave == 0) S.bs[lane] = bsv;
     __syncthreads();
     // each row's max (its largest chunk best) and tau (its k-th largest)
-    for (int q = tid; q < nq; q += kThreads) {
+    for (int q = tid; q < nq; q += kMT) {
         const int j = q / nch;
         const uint64_t mine = S.bk[q];
         const int rank = count_greater(S.bk + j * nch, nch, mine);
@@ -345,7 +347,7 @@ __device__ void merge_request(const DraftArgs &A, MergeShared<CAP> &S, int r) {
     }
     __syncthreads();
     // each row's normaliser (a wave per row)
-    for (int j = wave; j < R; j += kWaves) {
+    for (int j = wave; j < R; j += kMW) {
         const Scale2 scl = make_scale2(S.M[j], 1.0f);
         double z = 0.0;
         for (int c = lane; c < nch; c += SPEC_WAVE) {
@@ -360,7 +362,7 @@ __device__ void merge_request(const DraftArgs &A, MergeShared<CAP> &S, int r) {
     if (REG) {
 #pragma unroll
         for (int i = 0; i < P; ++i) {
-            const int q = tid + i * kThreads;
+            const int q = tid + i * kMT;
             if (q < nq) {
                 const int j = q / nch;
                 const uint64_t tau = S.rtau[j];
@@ -373,7 +375,7 @@ __device__ void merge_request(const DraftArgs &A, MergeShared<CAP> &S, int r) {
             }
         }
     } else {
-        for (int q = tid; q < nq; q += kThreads) {
+        for (int q = tid; q < nq; q += kMT) {
             const int j = q / nch;
             const uint64_t tau = S.rtau[j];
             const uint64_t *it = items + (int64_t)q * kItemWords;
@@ -386,7 +388,7 @@ __device__ void merge_request(const DraftArgs &A, MergeShared<CAP> &S, int r) {
         }
     }
     __syncthreads();
-    for (int q = tid; q < R * kMaxK * kMaxK; q += kThreads) {
+    for (int q = tid; q < R * kMaxK * kMaxK; q += kMT) {
         const int j = q / (kMaxK * kMaxK), c = q % (kMaxK * kMaxK);
         const int n = S.rn[j];
         if (c < n) {
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void draft_chunk_kernel(DraftArgs A) {
 }
 
 template <int CAP, bool REG>
-__global__ __launch_bounds__(kThreads) void draft_merge_kernel(DraftArgs A) {
+__global__ __launch_bounds__(kMT) void draft_merge_kernel(DraftArgs A) {
     __shared__ MergeShared<CAP> S;
     merge_request<CAP, REG>(A, S, blockIdx.x);
 }
@@ -432,10 +434,11 @@ void launch(const DraftArgs &A, int64_t items, int chunk, hipStream_t st) {
     else
         hipLaunchKernelGGL((draft_chunk_kernel<DT, kLargeE>), dim3((unsigned)items), b, 0, st, A);
     if (A.rows * A.nchunks <= kRegChunks)
-        hipLaunchKernelGGL((draft_merge_kernel<kRegChunks, true>), dim3((unsigned)A.batch), b, 0, st, A);
+        hipLaunchKernelGGL((draft_merge_kernel<kRegChunks, true>), dim3((unsigned)A.batch), dim3(kMT), 0,
+                           st, A);
     else
-        hipLaunchKernelGGL((draft_merge_kernel<kMergeChunks, false>), dim3((unsigned)A.batch), b, 0, st,
-                           A);
+        hipLaunchKernelGGL((draft_merge_kernel<kMergeChunks, false>), dim3((unsigned)A.batch), dim3(kMT),
+                           0, st, A);
 }
 
 }  // namespace
