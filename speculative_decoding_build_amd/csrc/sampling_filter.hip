@@ -59,6 +59,9 @@ __device__ __forceinline__ uint32_t value_key(float v) {
 constexpr int kCapK = 64;                  // the largest K: a chunk stores its top K keys
 constexpr int kChunkCand = 512;            // candidates a chunk ranks (more: the row is searched whole)
 constexpr int kMaxChunks = 64;             // chunks per row of the three-launch path
+// calls of at most this many logit bytes re-read the row in the output
+// launch (measured faster there than a launch of stores alone)
+constexpr int64_t kReadOutBytes = 32ll << 20;
 
 struct ChunkHead {                         // one chunk of one row (16 bytes)
     float m;                               // chunk max
@@ -68,8 +71,9 @@ struct ChunkHead {                         // one chunk of one row (16 bytes)
 
 struct Decision {                          // one row (16 bytes)
     uint64_t cutoff;                       // kept iff key >= cutoff
-    uint32_t mode;                         // 0: the output launch writes the row; 1: done
-    uint32_t pad;
+    uint32_t mode;                         // 0: every entry kept; 1: the row step wrote the row;
+                                           // 2: the first nkeep keys of the row's kept list
+    uint32_t nkeep;
 };
 
 // chunks of a row for the three-launch path (0: one workgroup per row), and
@@ -304,7 +308,8 @@ __device__ __forceinline__ bool cut_among(RowShared &S, int nc, int k, double tp
 __device__ __forceinline__ int merge_chunks(RowShared &S, const ChunkHead *__restrict__ heads,
                                              const uint64_t *__restrict__ keys, int nch,
                                              int64_t row, float T, int k, int K, float tpf,
-                                             Decision *__restrict__ dec) {
+                                             Decision *__restrict__ dec,
+                                             uint64_t *__restrict__ kept) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // the chunks' lists, K keys each (stored with a stride of kCapK), loaded
     // together with the chunk heads
@@ -388,13 +393,17 @@ __device__ __forceinline__ int merge_chunks(RowShared &S, const ChunkHead *__res
             if (lane >= o) v += u;
         }
         const uint64_t hit = __ballot(lane < K && key != 0 && ((k > 0 && lane + 1 >= k) || v >= tpz));
+        int rs = -1;
         if (hit != 0) {
-            const int rs = __builtin_ctzll(hit);
+            rs = __builtin_ctzll(hit);
             ok = true;
             cutoff = __shfl(key, rs, SPEC_WAVE);
         }
+        // the kept entries are the top rs + 1 keys: the output launch writes
+        // them from the keys, without reading the row again
+        if (lane <= rs) kept[row * kCapK + lane] = key;
         if (lane == 0) {
-            dec[row] = Decision{ok ? cutoff : 0, ok ? 0u : 1u, 0u};
+            dec[row] = ok ? Decision{cutoff, 2u, (uint32_t)(rs + 1)} : Decision{0, 1u, 0u};
             S.over = ok ? 0 : 2;
         }
     }
@@ -409,7 +418,8 @@ __global__ __launch_bounds__(kRT) void filter_row_kernel(
     const void *in, void *out, int64_t V, bool vec_ok, int n,
     const float *__restrict__ temperature, const int32_t *__restrict__ top_k,
     const float *__restrict__ top_p, const ChunkHead *__restrict__ heads,
-    const uint64_t *__restrict__ keys, int nch, Decision *__restrict__ dec) {
+    const uint64_t *__restrict__ keys, int nch, Decision *__restrict__ dec,
+    uint64_t *__restrict__ kept) {
     __shared__ RowShared S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t row = blockIdx.x;
@@ -428,7 +438,7 @@ __global__ __launch_bounds__(kRT) void filter_row_kernel(
     int nc = kCand + 1;                    // no candidates: the fast path is skipped
     if (heads != nullptr) {
         const int K = (k >= 1 && k <= kCapK) ? k : kCapK;
-        const int st = merge_chunks(S, heads, keys, nch, row, T, k, K, tpf, dec);
+        const int st = merge_chunks(S, heads, keys, nch, row, T, k, K, tpf, dec, kept);
         if (st == 0) return;
         if (st == 2) {
             known = true;
@@ -857,71 +867,116 @@ __global__ __launch_bounds__(kSweepThreads, 4) void filter_chunk_kernel(
     }
 }
 
-// Three-launch path, output step: the same work items as the chunk step;
-// rows the row step finished itself are skipped.  out may be in.
+// Eight output entries from e0 (chunk end c1): 16-byte stores when aligned.
 template <int DT>
+__device__ __forceinline__ void store8(char *rout, int64_t e0, int64_t c1, bool vec_ok,
+                                       const float (&v)[8]) {
+    if (DT == SPEC_BF16) {
+        uint16_t *o16 = reinterpret_cast<uint16_t *>(rout);
+        uint16_t h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = (uint16_t)(__float_as_uint(v[j]) >> 16);   // bf16 values
+        if (vec_ok && e0 + 8 <= c1) {
+            uint4 w;
+            w.x = h[0] | ((uint32_t)h[1] << 16);
+            w.y = h[2] | ((uint32_t)h[3] << 16);
+            w.z = h[4] | ((uint32_t)h[5] << 16);
+            w.w = h[6] | ((uint32_t)h[7] << 16);
+            *reinterpret_cast<uint4 *>(o16 + e0) = w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (e0 + j < c1) o16[e0 + j] = h[j];
+        }
+    } else {
+        float *o32 = reinterpret_cast<float *>(rout);
+        if (vec_ok && e0 + 8 <= c1) {
+            *reinterpret_cast<float4 *>(o32 + e0) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4 *>(o32 + e0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (e0 + j < c1) o32[e0 + j] = v[j];
+        }
+    }
+}
+
+// Three-launch path, output step: the same work items as the chunk step.
+// Rows the row step finished itself are skipped; a row with both rules off
+// is copied.  Otherwise, RD: the chunk is read again and an entry kept iff
+// its key is >= the cutoff; !RD: the chunk is written as -inf except the
+// row's kept entries that fall in it, whose values come from their keys
+// (no read: less traffic, but a launch of stores alone was measured slower
+// while the whole call is small).  out may be in.
+template <int DT, bool RD>
 __global__ __launch_bounds__(kSweepThreads) void filter_out_kernel(
     const void *in, void *out, int64_t V, int64_t C, bool vec_ok, int nch,
-    const Decision *__restrict__ dec) {
-    const int tid = threadIdx.x;
+    const Decision *__restrict__ dec, const uint64_t *__restrict__ kept) {
+    __shared__ int kl[kCapK];              // chunk-relative indices of the kept entries here
+    __shared__ float kx[kCapK];            // their values
+    __shared__ int nk;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int64_t item = blockIdx.x;
     const int64_t row = item / nch;
     const int c = (int)(item % nch);
     const size_t eb = DT == SPEC_BF16 ? 2 : 4;
     const int64_t c0 = (int64_t)c * C, c1 = V < c0 + C ? V : c0 + C;
-    Packed<DT> x;
-    x.load(static_cast<const char *>(in) + row * V * eb, c0, c1, vec_ok, tid);
     const Decision d = dec[row];
-    if (d.mode != 0) return;
-    const bool all = d.cutoff == 0;                // both rules off
-    const float cv = key_value(d.cutoff);
-    const int64_t cd = key_index(d.cutoff) - c0;
-    const int ci = cd < 0 ? -1 : (cd > kChunk ? kChunk : (int)cd);
+    // the whole kept list slot, loaded together with the decision (entries
+    // past nkeep are ignored)
+    uint64_t key = tid < SPEC_WAVE ? kept[row * kCapK + tid] : 0;
+    if (d.mode == 1) return;
     char *rout = static_cast<char *>(out) + row * V * eb;
+    if (RD || d.mode == 0) {               // mode 0: both rules off, every entry kept
+        Packed<DT> x;
+        x.load(static_cast<const char *>(in) + row * V * eb, c0, c1, vec_ok, tid);
+        const bool all = d.mode == 0;
+        const float cv = key_value(d.cutoff);
+        const int64_t cd = key_index(d.cutoff) - c0;
+        const int ci = cd < 0 ? -1 : (cd > kChunk ? kChunk : (int)cd);
 #pragma unroll
-    for (int g = 0; g < kPerThread / 8; ++g) {
-        const int64_t e0 = c0 + (int64_t)g * kSweepThreads * 8 + tid * 8;
-        bool keep[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            keep[j] = all || at_or_above(x[g * 8 + j], local_index(tid, g * 8 + j), cv, ci);
-        if (DT == SPEC_BF16) {
-            uint16_t *o16 = reinterpret_cast<uint16_t *>(rout);
-            uint16_t h[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                h[j] = keep[j] ? (uint16_t)(__float_as_uint(x[g * 8 + j]) >> 16) : (uint16_t)0xFF80u;
-            if (vec_ok && e0 + 8 <= c1) {
-                uint4 v;
-                v.x = h[0] | ((uint32_t)h[1] << 16);
-                v.y = h[2] | ((uint32_t)h[3] << 16);
-                v.z = h[4] | ((uint32_t)h[5] << 16);
-                v.w = h[6] | ((uint32_t)h[7] << 16);
-                *reinterpret_cast<uint4 *>(o16 + e0) = v;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (e0 + j < c1) o16[e0 + j] = h[j];
-            }
-        } else {
-            float *o32 = reinterpret_cast<float *>(rout);
+        for (int g = 0; g < kPerThread / 8; ++g) {
+            const int l0 = local_index(tid, g * 8);
             float v[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = keep[j] ? x[g * 8 + j] : -INFINITY;
-            if (vec_ok && e0 + 8 <= c1) {
-                *reinterpret_cast<float4 *>(o32 + e0) = make_float4(v[0], v[1], v[2], v[3]);
-                *reinterpret_cast<float4 *>(o32 + e0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (e0 + j < c1) o32[e0 + j] = v[j];
-            }
+            for (int j = 0; j < 8; ++j)
+                v[j] = all || at_or_above(x[g * 8 + j], l0 + j, cv, ci) ? x[g * 8 + j] : -INFINITY;
+            store8<DT>(rout, c0 + l0, c1, vec_ok, v);
         }
+        return;
+    }
+    if (tid < SPEC_WAVE) {
+        key = tid < (int)d.nkeep ? key : 0;
+        const int64_t i = key_index(key);
+        const bool here = key != 0 && i >= c0 && i < c1;
+        const uint64_t bal = __ballot(here);
+        if (here) {
+            const int pos = __popcll(bal & ((1ull << lane) - 1ull));
+            kl[pos] = (int)(i - c0);
+            kx[pos] = key_value(key);
+        }
+        if (tid == 0) nk = __popcll(bal);
+    }
+    __syncthreads();
+    const int n_here = nk;
+#pragma unroll
+    for (int g = 0; g < kPerThread / 8; ++g) {
+        const int l0 = local_index(tid, g * 8);
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = -INFINITY;
+        for (int t = 0; t < n_here; ++t) {
+            const int dl = kl[t] - l0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (dl == j) v[j] = kx[t];
+        }
+        store8<DT>(rout, c0 + l0, c1, vec_ok, v);
     }
 }
 
 struct FilterWs {
-    size_t dec, heads, keys, total;
+    size_t dec, heads, keys, kept, total;
 };
 
 FilterWs filter_ws(int64_t rows, int nch) {
@@ -929,7 +984,8 @@ FilterWs filter_ws(int64_t rows, int nch) {
     w.dec = 0;
     w.heads = align_up((size_t)rows * sizeof(Decision), 256);
     w.keys = w.heads + align_up((size_t)rows * nch * sizeof(ChunkHead), 256);
-    w.total = w.keys + align_up((size_t)rows * nch * kCapK * sizeof(uint64_t), 256);
+    w.kept = w.keys + align_up((size_t)rows * nch * kCapK * sizeof(uint64_t), 256);
+    w.total = w.kept + align_up((size_t)rows * kCapK * sizeof(uint64_t), 256);
     return w;
 }
 
@@ -941,7 +997,7 @@ void launch_filter(const void *logits, void *out, int64_t V, bool vec_ok, int n,
         hipLaunchKernelGGL((filter_row_kernel<DT, KEYBITS>), dim3((unsigned)rows), dim3(kRT), 0, st,
                            logits, out, V, vec_ok, n, temperature, top_k, top_p,
                            (const ChunkHead *)nullptr, (const uint64_t *)nullptr, 0,
-                           (Decision *)nullptr);
+                           (Decision *)nullptr, (uint64_t *)nullptr);
         return;
     }
     const FilterWs w = filter_ws(rows, nch);
@@ -949,15 +1005,22 @@ void launch_filter(const void *logits, void *out, int64_t V, bool vec_ok, int n,
     Decision *dec = reinterpret_cast<Decision *>(ws + w.dec);
     ChunkHead *heads = reinterpret_cast<ChunkHead *>(ws + w.heads);
     uint64_t *keys = reinterpret_cast<uint64_t *>(ws + w.keys);
+    uint64_t *kept = reinterpret_cast<uint64_t *>(ws + w.kept);
     const int64_t C = filter_chunk_size(V, nch);
     const unsigned items = (unsigned)(rows * nch);
     hipLaunchKernelGGL((filter_chunk_kernel<DT>), dim3(items), dim3(kSweepThreads), 0, st, logits, V,
                        C, vec_ok, n, nch, temperature, top_k, top_p, heads, keys);
     hipLaunchKernelGGL((filter_row_kernel<DT, KEYBITS>), dim3((unsigned)rows), dim3(kRT), 0, st,
                        logits, out, V, vec_ok, n, temperature, top_k, top_p,
-                       (const ChunkHead *)heads, (const uint64_t *)keys, nch, dec);
-    hipLaunchKernelGGL((filter_out_kernel<DT>), dim3(items), dim3(kSweepThreads), 0, st, logits, out,
-                       V, C, vec_ok, nch, (const Decision *)dec);
+                       (const ChunkHead *)heads, (const uint64_t *)keys, nch, dec, kept);
+    if ((int64_t)rows * V * (DT == SPEC_BF16 ? 2 : 4) <= kReadOutBytes)
+        hipLaunchKernelGGL((filter_out_kernel<DT, true>), dim3(items), dim3(kSweepThreads), 0, st,
+                           logits, out, V, C, vec_ok, nch, (const Decision *)dec,
+                           (const uint64_t *)kept);
+    else
+        hipLaunchKernelGGL((filter_out_kernel<DT, false>), dim3(items), dim3(kSweepThreads), 0, st,
+                           logits, out, V, C, vec_ok, nch, (const Decision *)dec,
+                           (const uint64_t *)kept);
 }
 
 }  // namespace

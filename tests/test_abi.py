@@ -161,7 +161,7 @@ def test_host_errors_before_launch():
     sfw.restype = ctypes.c_size_t
     sfw.argtypes = [I, I, ctypes.c_int64]
     need = sfw(1, 4, 128256)      # 16 chunks of 8016 entries per row
-    assert need == 256 + 4 * 16 * 16 + 4 * 16 * 64 * 8
+    assert need == 256 + 4 * 16 * 16 + 4 * 16 * 64 * 8 + 4 * 64 * 8
     assert sfw(1, 4, 8192) == 0 and sfw(1, 4, 524289) == 0 and sfw(0, 4, 128256) == 0
     assert sfw(1, 4, 8193) > 0 and sfw(1, 4, 524288) > 0
     assert sf(1, 4, 128256, 0, *f5, P0, 0, P0, P0) == -5                 # no workspace

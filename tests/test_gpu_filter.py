@@ -160,6 +160,26 @@ def test_filter_chunked_rows_and_whole_row_fallback(V, dtype):
     _check(logits, dtype, b, 1, V, k, p, t, f"chunked V={V} {dtype}", in_place=(V == 16385))
 
 
+@pytest.mark.parametrize("in_place", [False, True])
+def test_filter_above_32mb_writes_from_kept_keys(in_place):
+    """Above 32 MB of logits per call the output launch writes each row from
+    its kept keys without re-reading it: 2 requests x 64 rows x 128256 bf16
+    (32.8 MB), one request at top_k 50 / top_p 0.9 and one at top-p alone."""
+    rng = np.random.default_rng(21)
+    b, n, V = 2, 64, 128256
+    x = (rng.standard_normal((b * n, V)) * 2).astype(np.float32)
+    x[n // 2:n, :V // 3] = -np.inf                  # partly masked rows
+    logits = W.f32_to_bf16_bits(x)
+    k = np.array([50, 0], np.int32)
+    p = np.array([0.9, 0.5], np.float32)
+    t = np.array([1.0, 0.8], np.float32)
+    say(f"[filter] kept-key output b={b} n={n} V={V} in_place={in_place}")
+    _check(logits, "bf16", b, n, V, k, p, t, "kept keys", in_place=in_place)
+    k2 = np.array([1, 0], np.int32)
+    p2 = np.array([1.0, 1.0], np.float32)          # greedy rows, then rows kept whole
+    _check(logits, "bf16", b, n, V, k2, p2, t, "kept keys greedy / all", in_place=in_place)
+
+
 def test_filter_workspace_size_and_refusals():
     # one chunk (<= 8192) and more than 64 chunks (> 524288) need none
     assert S.spec_sampling_filter_workspace_size(3, 4, 8192) == 0
