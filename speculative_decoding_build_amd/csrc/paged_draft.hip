@@ -86,7 +86,12 @@ __global__ __launch_bounds__(kThreads) void full_mask_kernel(
 #pragma unroll
       for (int h = 0; h < kMaskPer; ++h) {
         const int64_t A = (a0 & ~(int64_t)15) + (int64_t)part * kRowSpan + (h * kThreads + tid) * 16;
-        if (A < end && A + 16 > a0) {
+        if (A >= a0 && A + 16 <= a0 + L && A + 16 <= end) {
+            // inside the prefix: sixteen ones, no per-byte work
+            u32x4 u;
+            u.x = u.y = u.z = u.w = 0x01010101u;
+            __builtin_nontemporal_store(u, reinterpret_cast<u32x4 *>(out + A));
+        } else if (A < end && A + 16 > a0) {
             uint8_t v[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
