@@ -3,13 +3,16 @@
 One step = one pass of every operation of the path over one batch of
 synthetic input: tree build -> verify attention -> greedy accept -> sampled
 accept -> accepted-KV compaction, all through the C-ABI library.  The
-default workload is the single-request Llama-3-8B-shaped tree (batch 1,
-topk 8, 5 steps, 64 draft tokens, 32 query / 8 KV heads, head dim 128, bf16
-KV, 4096 cached tokens, vocab 128256); ``--config`` picks another.
+default workload is the largest one that fits one GPU: the long-context tree
+at a 70B attention shape (batch 4, topk 8, 6 steps, 64 draft tokens, 64 query
+/ 8 KV heads, head dim 128, bf16 paged KV with page size 16, 131072 cached
+tokens per request, vocab 128256); ``--config`` picks another.
 
 Inputs are resident in HBM before timing starts.  Several copies of them are
-rotated through the steps so that each step reads cold memory (the 256 MB
-last-level cache cannot hold the rotation).
+rotated through the steps and through each operation's own timing, so that
+every HBM-bound operation (verify attention, the greedy vocabulary sweep)
+reads at least twice the 256 MB last-level cache between two reads of the
+same bytes.
 
 Timing.  ``--mode graph`` (default) captures each copy's step once into a
 HIP graph and times K replays, so the GPU runs the step's kernels back to
@@ -45,7 +48,9 @@ import workloads as W
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
-ROTATION_BYTES = 768 << 20     # rotate at least this many bytes of inputs
+MALL_BYTES = 256 << 20         # last-level cache (Infinity Cache) of the part
+MAX_COPIES = 64
+MAX_ROTATION_BYTES = 64 << 30  # device memory the input copies may take
 
 
 def parse():
@@ -53,10 +58,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=sorted(W.CONFIGS))
+    ap.add_argument("--config", type=int, default=5, choices=sorted(W.CONFIGS))
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="graph: each input copy's step is captured once into a HIP graph and "
                          "the timed steps replay the graphs (no host launch cost between "
@@ -248,66 +253,121 @@ EXTRA_OPS = ("accept_target_only", "draft_steps", "sampling_filter", "full_mask"
              "plan_draft_branches")
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, w, tl, dl, budget_s):
-    """The CPU oracle on the same host arrays, single BLAS thread.  Tree
-    build, both accepts and compaction run whole; attention runs on a subset
-    of (row, head) vectors sized to the time budget and is scaled to the
-    whole batch."""
+    """The CPU oracle as it stands, on the same host arrays.
+
+    Tree build, both accepts and compaction run whole, once each, in one
+    thread (they are KB- to MB-scale).  Verify attention, the bulk of the
+    work, runs on a sample of (row, head) vectors: the (request, KV head)
+    units are independent, so a pool of T threads (T = the cores this
+    process may use) each takes one unit's sampled vectors, with one BLAS
+    thread per worker.  The threaded figure is the median of three runs; a
+    one-thread run of one unit's sample is reported beside it.  When the
+    sample is not the whole batch, its time is scaled by the vector count.
+    """
+    from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):
-        return _cpu_baseline(cfg, w, tl, dl, budget_s)
-
-
-def _cpu_baseline(cfg, w, tl, dl, budget_s):
     import oracle
+
+    threads = len(os.sched_getaffinity(0))
     b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
-    t0 = time.perf_counter()
-    t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
-                          cfg.num_steps, n)
-    t_build = time.perf_counter() - t0
-    # attention: time a growing subset until the budget share is used
-    pairs_total = b * n * cfg.num_q_heads
-    rng = np.random.default_rng(0)
-    want = max(1, min(pairs_total, 8))
-    spent, done = 0.0, 0
-    while True:
-        rows = [(int(r), int(h)) for r, h in zip(rng.integers(0, b * n, want),
-                                                   rng.integers(0, cfg.num_q_heads, want))]
+    G, hkv = cfg.group, cfg.num_kv_heads
+    with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        oracle.verify_attention(w.q, w.k_pool[0], w.v_pool[0], w.page_table, w.seq_lens,
-                                w.out_cache_loc, t["mask"], cfg.num_q_heads, cfg.num_kv_heads,
-                                cfg.page_size, cfg.dtype, rows=rows)
-        spent += time.perf_counter() - t0
-        done += want
-        if spent > 0.5 * budget_s or done >= pairs_total:
-            break
-        want = min(pairs_total - done, want * 4)
-    t_attn = spent / done * pairs_total
-    t0 = time.perf_counter()
-    g = oracle.accept_greedy(tl, t["draft_tokens"], t["retrieve_index"], t["retrieve_next_token"],
+        t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                              cfg.num_steps, n)
+        t_build = time.perf_counter() - t0
+
+        def attn(rows):
+            oracle.verify_attention(w.q, w.k_pool[0], w.v_pool[0], w.page_table, w.seq_lens,
+                                    w.out_cache_loc, t["mask"], cfg.num_q_heads, hkv,
+                                    cfg.page_size, cfg.dtype, rows=rows)
+
+        # units (request, KV head) and their vectors (row, head)
+        units = [(r, g) for r in range(b) for g in range(hkv)]
+        rng = np.random.default_rng(0)
+        rng.shuffle(units)
+        unit_vecs = lambda r, g: [(r * n + k, h) for k in range(n)
+                                  for h in range(g * G, (g + 1) * G)]
+        total_vecs = b * n * cfg.num_q_heads
+        # probe: two vectors of one unit, one thread
+        r0, g0 = units[0]
+        probe = unit_vecs(r0, g0)[:2]
+        t0 = time.perf_counter()
+        attn(probe)
+        per_vec = (time.perf_counter() - t0) / len(probe)
+        # each threaded run should take about budget / 6 of wall time
+        per_run = budget_s / 6.0
+        nunits = min(threads, len(units))
+        k = int(max(1, min(n * G, per_run / max(per_vec, 1e-9))))
+        whole = per_vec * total_vecs / max(1, min(threads, len(units))) <= per_run
+        if whole:
+            work = [unit_vecs(r, g) for r, g in units]
+        else:
+            work = []
+            for r, g in units[:nunits]:
+                vecs = unit_vecs(r, g)
+                pick = np.sort(rng.choice(len(vecs), size=k, replace=False))
+                work.append([vecs[i] for i in pick])
+        sampled = sum(len(x) for x in work)
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                list(ex.map(attn, work))
+            runs.append(time.perf_counter() - t0)
+        t_attn = float(np.median(runs)) * total_vecs / sampled
+        t0 = time.perf_counter()
+        attn(work[0])
+        t_attn_1 = (time.perf_counter() - t0) * total_vecs / len(work[0])
+
+        t0 = time.perf_counter()
+        g = oracle.accept_greedy(tl, t["draft_tokens"], t["retrieve_index"],
+                                 t["retrieve_next_token"], t["retrieve_next_sibling"], b, n, s1,
+                                 cfg.dtype)
+        t_greedy = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.accept_sample(tl, dl, w.temperature, w.uniforms, w.final_uniforms,
+                             t["draft_tokens"], t["retrieve_index"], t["retrieve_next_token"],
                              t["retrieve_next_sibling"], b, n, s1, cfg.dtype)
-    t_greedy = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.accept_sample(tl, dl, w.temperature, w.uniforms, w.final_uniforms, t["draft_tokens"],
-                         t["retrieve_index"], t["retrieve_next_token"], t["retrieve_next_sibling"],
-                         b, n, s1, cfg.dtype)
-    t_sample = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.compact_kv(w.k_pool, w.v_pool, w.page_table, w.seq_lens, w.out_cache_loc,
-                      g["accept_index"], g["accept_length"], b, n, cfg.page_size)
-    t_compact = time.perf_counter() - t0
-    total = t_build + t_attn + t_greedy + t_sample + t_compact
+        t_sample = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.compact_kv(w.k_pool, w.v_pool, w.page_table, w.seq_lens, w.out_cache_loc,
+                          g["accept_index"], g["accept_length"], b, n, cfg.page_size)
+        t_compact = time.perf_counter() - t0
+    rest = t_build + t_greedy + t_sample + t_compact
+    total = rest + t_attn
+    if whole:
+        sample = (f"whole step; verify attention over all {total_vecs} (row, head) vectors in "
+                  f"{threads} threads (one per (request, KV head) unit at a time), median of 3; "
+                  f"tree build, accepts and compaction whole in one thread; float64 numpy")
+    else:
+        sample = (f"tree build, both accepts and compaction whole in one thread; verify "
+                  f"attention on {sampled} of {total_vecs} (row, head) vectors ({k} from each "
+                  f"of {len(work)} (request, KV head) units, one unit per thread, {threads} "
+                  f"threads), median of 3 runs, scaled by vector count; float64 numpy")
     return {
         "value": b * n / total,
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": ("whole step, float64 numpy, one thread" if done >= pairs_total else
-                   f"whole step except verify attention, which ran {done} of {pairs_total} "
-                   f"(row, head) vectors and was scaled up; float64 numpy, one thread"),
+        "sample": sample,
+        "cpu_model": _cpu_model(),
+        "value_1thread": b * n / (rest + t_attn_1),
+        "attention_runs_s": runs,
         "op_seconds": {"build_tree": t_build, "verify_attention": t_attn,
-                       "accept_greedy": t_greedy, "accept_sample": t_sample,
-                       "compact_kv": t_compact},
+                       "verify_attention_1thread": t_attn_1, "accept_greedy": t_greedy,
+                       "accept_sample": t_sample, "compact_kv": t_compact},
     }
 
 
@@ -315,11 +375,27 @@ def _traffic(cfg):
     """HBM bytes per verify-attention call (both launches) from the committed
     counter summary of this workload, or None when there is none or it was
     taken on another version of the kernel source."""
-    from speculative_decoding_build_amd.profile_summary import read_traffic
+    from rocprof_summary import read_traffic
     root = os.path.dirname(os.path.abspath(__file__))
     return read_traffic(os.path.join(root, "profiles", f"verify_attention_{cfg.name}_hbm.md"),
                         os.path.join(root, "speculative_decoding_build_amd", "csrc",
                                      "verify_attention.hip"))
+
+
+def _log(msg):
+    """Progress of the run on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def rotation_copies(cfg, base_bytes, attn_bytes):
+    """Input copies to rotate: enough that the smaller of the two HBM-bound
+    operations' own inputs (the attention call's K/V stream, the greedy
+    sweep's logits) spans twice the last-level cache, within the memory cap."""
+    eb = 2 if cfg.dtype == "bf16" else 4
+    own = min(attn_bytes, cfg.batch * cfg.num_draft_tokens * cfg.vocab * eb)
+    want = math.ceil(2 * MALL_BYTES / max(1, own))
+    fit = max(1, MAX_ROTATION_BYTES // max(1, base_bytes))
+    return int(max(1, min(want, MAX_COPIES, fit)))
 
 
 def main():
@@ -329,11 +405,25 @@ def main():
               "would shard by request and by KV head with no exchange between GPUs.",
               file=sys.stderr)
         sys.exit(2)
+    import gc
+    import torch
+    line = run(args)
+    # Release every graph, input copy and workspace, and let the device
+    # drain, before the interpreter tears down the runtime (and a profiler
+    # attached to it): nothing of the library's is left to free at exit.
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    print(json.dumps(line), flush=True)
+
+
+def run(args):
     import torch
     import speculative_decoding_build_amd as S
 
     cfg = W.CONFIGS[args.config]
     seed = args.seed if args.seed is not None else 1000 * args.config + 1
+    _log(f"building workload {cfg.name} (seed {seed})")
     w = W.make_workload(cfg, seed)
     _MAXLEN[cfg.name] = int(w.seq_lens.max())
     b, n = cfg.batch, cfg.num_draft_tokens
@@ -373,9 +463,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    copies = max(1, min(16, math.ceil(ROTATION_BYTES / max(1, base.nbytes()))))
+    attn_bytes = W.attention_bytes(cfg, w.seq_lens)
+    copies = rotation_copies(cfg, base.nbytes(), attn_bytes)
     xs = [base] + [base.clone(torch) for _ in range(copies - 1)]
     torch.cuda.synchronize()
+    _log(f"{copies} input copies resident ({copies * base.nbytes() / 1e9:.1f} GB)")
 
     for i in range(args.warmup):
         run_ops(S, cfg, xs[i % copies], ws_attn, ws_greedy, ws_sample)
@@ -429,6 +521,7 @@ def main():
             torch.cuda.synchronize()
             extra_ms[op] = e0.elapsed_time(e1) / k_ev
 
+    _log("per-operation timing done")
     # eager steps (every launch from Python)
     k_e = max(5, min(args.steps, 20))
     torch.cuda.synchronize()
@@ -475,15 +568,37 @@ def main():
     wall = time.perf_counter() - t0
     step_ms = wall * 1e3 / args.steps
     status = int(base.status.cpu()[0])
+    _log(f"timed {args.steps} steps: {step_ms:.4f} ms per step")
 
     acc_len = base.accept_length.cpu().numpy() if "greedy" in cfg.accept else \
         base.saccept_length.cpu().numpy()
-    attn_bytes = W.attention_bytes(cfg, w.seq_lens)
-    sweep_g = b * n * cfg.vocab * (2 if cfg.dtype == "bf16" else 4)
-    draft_bytes = b * cfg.npar * cfg.vocab * (2 if cfg.dtype == "bf16" else 4)
-    attn_gbs = attn_bytes / (op_ms["verify_attention"] * 1e-3) / 1e9
+    depth = (base.positions.cpu().numpy().reshape(b, n) - w.seq_lens[:, None]).astype(np.int64)
+    eb = 2 if cfg.dtype == "bf16" else 4
+    attn_flops = W.attention_flops(cfg, w.seq_lens, depth)
+    sweep_g = b * n * cfg.vocab * eb
+    draft_bytes = b * cfg.npar * cfg.vocab * eb
+    t_attn = op_ms["verify_attention"] * 1e-3
+    attn_gbs = attn_bytes / t_attn / 1e9
+    attn_tflops = attn_flops / t_attn / 1e12
     greedy_gbs = sweep_g / (op_ms["accept_greedy"] * 1e-3) / 1e9
     accept_op = "accept_greedy" if "greedy" in cfg.accept else "accept_sample"
+    # the binding roof: matrix cores when the call's flops per algorithmic
+    # byte exceed the ridge (peak flops / peak bandwidth), else HBM
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_bound = cfg.dtype == "bf16" and attn_flops / attn_bytes > ridge
+    traffic = _traffic(cfg)
+    if mfma_bound:
+        roof = {"kernel": "spec_verify_attention (split-KV MFMA + merge launches)",
+                "bound": "mfma", "achieved": attn_tflops, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": attn_tflops / BF16_PEAK_TFLOPS, "traffic": traffic,
+                "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes,
+                "hbm_gbs": attn_gbs, "frac_hbm": attn_gbs / HBM_PEAK_GBS}
+    else:
+        roof = {"kernel": "spec_verify_attention (split-KV MFMA + merge launches)",
+                "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": attn_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                "algorithmic_bytes": attn_bytes, "algorithmic_flops": attn_flops,
+                "tflops": attn_tflops, "frac_mfma": attn_tflops / BF16_PEAK_TFLOPS}
 
     line = {
         "metric": "verified tree tokens/s (whole path per step)",
@@ -513,6 +628,8 @@ def main():
         "op_ms": op_ms,
         "verify_attn_gbs": attn_gbs,
         "verify_attn_frac_hbm": attn_gbs / HBM_PEAK_GBS,
+        "verify_attn_tflops": attn_tflops,
+        "verify_attn_frac_mfma": attn_tflops / BF16_PEAK_TFLOPS,
         "accept_greedy_sweep_gbs": greedy_gbs,
         "extra_op_ms": extra_ms,
         "accept_target_only_sweep_gbs": sweep_g / (extra_ms["accept_target_only"] * 1e-3) / 1e9,
@@ -523,14 +640,17 @@ def main():
         "draft_steps_sweep_gbs": draft_bytes / (extra_ms["draft_steps"] * 1e-3) / 1e9,
         "mean_accept_length": float(acc_len.mean()),
         "dev_status": status,
-        "roofline": {"kernel": "spec_verify_attention (split-KV MFMA + merge launches)",
-                     "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
-                     "traffic": _traffic(cfg), "algorithmic_bytes": attn_bytes},
+        "roofline": roof,
+        "roofline_accept_sweep": {"kernel": "spec_accept_greedy (vocabulary sweep + walk)",
+                                  "bound": "hbm", "achieved": greedy_gbs,
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": greedy_gbs / HBM_PEAK_GBS,
+                                  "algorithmic_bytes": sweep_g},
     }
     if not args.no_cpu_baseline:
+        _log("CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(cfg, w, tl, dl, args.cpu_budget_s)
-    print(json.dumps(line), flush=True)
+    return line
 
 
 if __name__ == "__main__":

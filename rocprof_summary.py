@@ -3,7 +3,7 @@ profiles/.
 
 Kernel trace (per-kernel launch count and average / min / max duration):
 
-    python -m speculative_decoding_build_amd.profile_summary <db or dir> [title] [command]
+    python rocprof_summary.py <db or dir> [title] [command]
 
 HBM byte counters (FETCH_SIZE / WRITE_SIZE, KiB per dispatch) of chosen
 kernels, scaled by what the same counter reads for a plain device copy of
@@ -11,7 +11,7 @@ known size in the same run (the copy bench.py makes with
 --calibrate-copy-mb), with the SHA-1 of the kernels' source so a reader can
 tell whether the figures still describe the code:
 
-    python -m speculative_decoding_build_amd.profile_summary --counters \
+    python rocprof_summary.py --counters \
         --db <fetch run> --db <write run> --copy-bytes N --kernels a,b \
         --source <file> --title ... --command ... --command ...
 """
@@ -91,7 +91,7 @@ def counters_report(dbs, copy_bytes, kernels, source, title, commands):
             per_launch += scaled
     sha = hashlib.sha1(open(source, "rb").read()).hexdigest()
     out += ["", f"traffic_bytes_per_launch: {per_launch:.0f}",
-            f"source: {os.path.relpath(source, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))}",
+            f"source: {os.path.relpath(source, os.path.dirname(os.path.abspath(__file__)))}",
             f"source_sha1: {sha}"]
     return "\n".join(out) + "\n"
 

@@ -201,19 +201,9 @@ __global__ __launch_bounds__(kSweepThreads) void greedy_walk_kernel(GreedyArgs A
 
 // Workgroups of the fused kernel the device holds at once (0 if unknown).
 template <int DT>
-int fused_capacity(int dev) {
-    static int cached_device = -1, cap = 0;
-    if (dev != cached_device) {
-        int cus = 0, per = 0;
-        const bool ok =
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per, reinterpret_cast<const void *>(greedy_kernel<DT, true>), kSweepThreads, 0) ==
-                hipSuccess;
-        cap = ok ? cus * per : 0;
-        cached_device = dev;
-    }
-    return cap;
+int fused_capacity() {
+    return spec::resident_capacity(reinterpret_cast<const void *>(greedy_kernel<DT, true>),
+                                   kSweepThreads);
 }
 
 }  // namespace
@@ -272,10 +262,8 @@ extern "C" int spec_accept_greedy(int batch, int n, int s1, int64_t vocab, int d
     A.status = dev_status;
     A.slots = static_cast<uint64_t *>(workspace);
     const dim3 grid((unsigned)items);
-    int dev = 0;
-    const bool fused = hipGetDevice(&dev) == hipSuccess &&
-                       batch < (dtype == SPEC_BF16 ? fused_capacity<SPEC_BF16>(dev)
-                                                   : fused_capacity<SPEC_F32>(dev));
+    const bool fused = batch < (dtype == SPEC_BF16 ? fused_capacity<SPEC_BF16>()
+                                                   : fused_capacity<SPEC_F32>());
     if (fused) {
         if (dtype == SPEC_BF16)
             hipLaunchKernelGGL((greedy_kernel<SPEC_BF16, true>), grid, dim3(kSweepThreads), 0, st, A);

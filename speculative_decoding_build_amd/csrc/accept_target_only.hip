@@ -480,25 +480,14 @@ __global__ __launch_bounds__(kSweepThreads) void target_only_walk_kernel(TargetA
 
 // Workgroups of the fused kernel the device holds at once (0 if unknown).
 template <int DT>
-int fused_capacity(int dev) {
-    static int cached_device = -1, cap = 0;
-    if (dev != cached_device) {
-        int cus = 0, per = 0;
-        const bool ok =
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per, reinterpret_cast<const void *>(target_only_kernel<DT, true>), kSweepThreads,
-                0) == hipSuccess;
-        cap = ok ? cus * per : 0;
-        cached_device = dev;
-    }
-    return cap;
+int fused_capacity() {
+    return spec::resident_capacity(
+        reinterpret_cast<const void *>(target_only_kernel<DT, true>), kSweepThreads);
 }
 
 template <int DT>
 void launch(const TargetArgs &A, int64_t items, hipStream_t st) {
-    int dev = 0;
-    const bool fused = hipGetDevice(&dev) == hipSuccess && A.batch < fused_capacity<DT>(dev);
+    const bool fused = A.batch < fused_capacity<DT>();
     const dim3 grid((unsigned)items);
     if (fused) {
         hipLaunchKernelGGL((target_only_kernel<DT, true>), grid, dim3(kSweepThreads), 0, st, A);

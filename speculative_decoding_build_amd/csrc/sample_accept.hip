@@ -827,28 +827,17 @@ struct CoopPlan {
 // Workgroups of one cooperative-walk kernel that fit on the device at once
 // (0 if cooperative launch is unavailable).
 template <int DT, bool CACHE>
-int coop_capacity(int dev) {
-    static int cached_device = -1, cap = 0;
-    if (dev != cached_device) {
-        int coop = 0, cus = 0, per = 0;
-        bool ok = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess;
-        ok = ok && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
-        ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                       &per, reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true, CACHE>),
-                       kCoopThreads, 0) == hipSuccess;
-        cap = (ok && coop) ? cus * per : 0;
-        cached_device = dev;
-    }
-    return cap;
+int coop_capacity() {
+    return spec::resident_capacity(
+        reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true, CACHE>),
+        kCoopThreads, true);
 }
 
 // Workgroups per request for the cooperative walk, or G = 0 when the grid
 // cannot be co-resident (or cooperative launch is unavailable).
 template <int DT>
 CoopPlan coop_plan(int batch, int64_t vocab) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return CoopPlan{0, 0, false};
-    const int cap = std::min(coop_capacity<DT, true>(dev), coop_capacity<DT, false>(dev));
+    const int cap = std::min(coop_capacity<DT, true>(), coop_capacity<DT, false>());
     int64_t G = group_cap(batch, vocab);
     G = std::min<int64_t>(G, cap / std::max(batch, 1));
     if (G < 2) return CoopPlan{0, 0, false};

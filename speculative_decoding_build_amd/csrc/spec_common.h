@@ -59,4 +59,22 @@ inline int launch_status() {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workgroups of `kernel` (launched with `threads` threads, no dynamic LDS)
+// that the current device holds at once, or 0 when that is unknown (or, with
+// need_coop, when the device has no cooperative launch).  Evaluated on every
+// call: the library keeps no state between calls.
+inline int resident_capacity(const void *kernel, int threads, bool need_coop = false) {
+    int dev = 0, cus = 0, per = 0, coop = 1;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (need_coop &&
+        (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+         coop == 0))
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess)
+        return 0;
+    return cus * per;
+}
+
 }  // namespace spec
