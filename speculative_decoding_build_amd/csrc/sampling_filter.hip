@@ -953,7 +953,18 @@ __global__ __launch_bounds__(kSweepThreads) void filter_out_kernel(
         if (here) {
             const int pos = __popcll(bal & ((1ull << lane) - 1ull));
             kl[pos] = (int)(i - c0);
-            kx[pos] = key_value(key);
+            float xv = key_value(key);
+            // the key holds -0 as +0 (equal logits rank by index alone): a
+            // kept zero takes its sign from the input, read before any store
+            // of this chunk (the one workgroup that writes it), so in place
+            // is safe too
+            if (xv == 0.f) {
+                const char *src = static_cast<const char *>(in) + (row * V + i) * eb;
+                xv = DT == SPEC_BF16
+                    ? spec::bf16_to_f32(*reinterpret_cast<const uint16_t *>(src))
+                    : *reinterpret_cast<const float *>(src);
+            }
+            kx[pos] = xv;
         }
         if (tid == 0) nk = __popcll(bal);
     }

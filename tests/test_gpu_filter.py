@@ -70,7 +70,10 @@ def _check(logits, dtype, b, n, V, k, p, t, label, in_place=False):
     got, st = _gpu_filter(logits, dtype, b, n, V, k, p, t, in_place)
     want, kept, near = oracle.filter_logits(logits.reshape(b * n, V), dtype, np.repeat(t, n),
                                             np.repeat(k, n), np.repeat(p, n))
-    bad = [i for i in range(b * n) if not near[i] and not np.array_equal(got[i], want[i])]
+    # bit patterns: float compares would take -0 for +0
+    gb = got.view(np.uint32) if got.dtype == np.float32 else got
+    wb = np.ascontiguousarray(want).view(np.uint32) if want.dtype == np.float32 else want
+    bad = [i for i in range(b * n) if not near[i] and not np.array_equal(gb[i], wb[i])]
     say(f"    {label}: rows {b * n} near {int(near.sum())} kept/row {kept.sum(1)[:6].tolist()} "
         f"mismatched {bad[:6]}")
     assert st == 0
@@ -160,24 +163,48 @@ def test_filter_chunked_rows_and_whole_row_fallback(V, dtype):
     _check(logits, dtype, b, 1, V, k, p, t, f"chunked V={V} {dtype}", in_place=(V == 16385))
 
 
+KEPT_KEY_BYTES = 32 << 20   # 32 MiB = 33,554,432 bytes of logits per call
+
+
+@pytest.mark.parametrize("dtype,b", [("bf16", 3), ("f32", 2)])
 @pytest.mark.parametrize("in_place", [False, True])
-def test_filter_above_32mb_writes_from_kept_keys(in_place):
-    """Above 32 MB of logits per call the output launch writes each row from
-    its kept keys without re-reading it: 2 requests x 64 rows x 128256 bf16
-    (32.8 MB), one request at top_k 50 / top_p 0.9 and one at top-p alone."""
+def test_filter_above_32mb_writes_from_kept_keys(dtype, b, in_place):
+    """Calls above 32 MiB (33,554,432 bytes) of logits take the output form
+    that writes each row from its kept keys without reading the row again:
+    3 requests x 64 rows x 128256 bf16 (49.3 MB) and 2 x 64 x 128256 float32
+    (65.7 MB).  Requests: top_k 50 / top_p 0.9, top-p alone, and one whose
+    rows keep only zeros of both signs (the key of -0 equals that of +0, so
+    the written -0 must come from the input's bits)."""
     rng = np.random.default_rng(21)
-    b, n, V = 2, 64, 128256
+    n, V = 64, 128256
+    eb = 2 if dtype == "bf16" else 4
+    assert b * n * V * eb > KEPT_KEY_BYTES
     x = (rng.standard_normal((b * n, V)) * 2).astype(np.float32)
     x[n // 2:n, :V // 3] = -np.inf                  # partly masked rows
-    logits = W.f32_to_bf16_bits(x)
-    k = np.array([50, 0], np.int32)
-    p = np.array([0.9, 0.5], np.float32)
-    t = np.array([1.0, 0.8], np.float32)
-    say(f"[filter] kept-key output b={b} n={n} V={V} in_place={in_place}")
-    _check(logits, "bf16", b, n, V, k, p, t, "kept keys", in_place=in_place)
-    k2 = np.array([1, 0], np.int32)
-    p2 = np.array([1.0, 1.0], np.float32)          # greedy rows, then rows kept whole
-    _check(logits, "bf16", b, n, V, k2, p2, t, "kept keys greedy / all", in_place=in_place)
+    # last request: negative rows whose top entries are signed zeros
+    z = slice((b - 1) * n, b * n)
+    x[z] = -np.abs(x[z]) - 1.0
+    cols = np.stack([rng.choice(V, size=6, replace=False) for _ in range(n)])
+    for r in range(n):
+        x[(b - 1) * n + r, cols[r, :3]] = -0.0
+        x[(b - 1) * n + r, cols[r, 3:]] = 0.0
+    logits = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    # (top_k, top_p, temperature) per request; the zero rows' request is last
+    par = [(50, 0.9, 1.0), (0, 0.5, 0.8), (4, 1.0, 1.0)]
+    par = par if b == 3 else [par[0], par[2]]
+    k = np.array([q[0] for q in par], np.int32)
+    p = np.array([q[1] for q in par], np.float32)
+    t = np.array([q[2] for q in par], np.float32)
+    say(f"[filter] kept-key output {dtype} b={b} n={n} V={V} in_place={in_place}")
+    got = _check(logits, dtype, b, n, V, k, p, t, "kept keys", in_place=in_place)
+    # each zero row kept four of its six zeros (the lowest indices), so at
+    # least one -0 per row, written with its sign
+    bits = got.view(np.uint16 if dtype == "bf16" else np.uint32)[z]
+    neg = 0x8000 if dtype == "bf16" else 0x80000000
+    assert all((bits[r, cols[r, :3]] == neg).any() for r in range(n))
+    k2 = np.array([1, 0, 1] if b == 3 else [1, 1], np.int32)
+    p2 = np.ones(b, np.float32)                     # greedy rows, then rows kept whole
+    _check(logits, dtype, b, n, V, k2, p2, t, "kept keys greedy / all", in_place=in_place)
 
 
 def test_filter_workspace_size_and_refusals():
