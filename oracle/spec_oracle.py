@@ -236,6 +236,38 @@ def verify_attention(q, k_pool, v_pool, page_table, seq_lens, out_cache_loc, mas
     return out
 
 
+def verify_attention_unit(q, k_pool, v_pool, page_table, seq_lens, out_cache_loc, mask,
+                          num_q_heads, num_kv_heads, page_size, dtype, r, g, sm_scale=None):
+    """The same definition as verify_attention ([P5] 4.2 / 4.3), evaluated
+    for every query of one (request r, KV head g) unit at once: the n tree
+    nodes times the G query heads of the group form the rows of one score
+    matrix against the request's keys (history, then tree nodes); a tree key
+    a node's mask row does not allow scores -inf; each row's softmax weights
+    V.  Matrix products stand in for the per-vector dot products; nothing is
+    split or reordered beyond that.
+
+    Returns float64 [n, G, d]: out[k, j] is query head g * G + j of node k.
+    """
+    b, n, _ = mask.shape
+    d = q.shape[-1]
+    G = num_q_heads // num_kv_heads
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    L = int(seq_lens[r])
+    hist = np.array([slot_of(page_table, page_size, r, p) for p in range(L)], np.int64)
+    tree = np.asarray(out_cache_loc[r * n:(r + 1) * n], np.int64)
+    slots = np.concatenate([hist, tree])
+    K = widen(k_pool[slots, g], dtype)                       # [L + n, d]
+    V = widen(v_pool[slots, g], dtype)
+    Q = widen(q[r * n:(r + 1) * n, g * G:(g + 1) * G], dtype).reshape(n * G, d)
+    s = scale * (Q @ K.T)                                    # [n * G, L + n]
+    allow = np.repeat(np.asarray(mask[r], bool), G, axis=0)  # row k * G + j: node k's mask row
+    s[:, L:][~allow] = -np.inf
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return (p @ V).reshape(n, G, d)
+
+
 # ---------------------------------------------------------------------------
 # C3  Greedy accept
 # ---------------------------------------------------------------------------
@@ -313,9 +345,10 @@ def accept_sample(target_logits, draft_logits, temperature, uniforms, final_unif
     uniform.  [P5] 5.6: the walk is the greedy walk's.
 
     Also returns, per request, how close each decision came to its
-    boundary: ``margin`` = smallest |u - min(1, ratio)| over the tests made
-    (and the smallest residual mass Z), ``draw_margin`` = the final uniform's
-    distance to the nearest CDF edge, relative to the residual mass.  A
+    boundary: ``ratio_margin`` = smallest |u - min(1, ratio)| over the tests
+    made, ``z_min`` = the smallest residual mass Z, ``margin`` = the smaller
+    of the two, ``draw_margin`` = the final uniform's distance to the nearest
+    CDF edge, relative to the residual mass.  A
     request is ``exempt`` from bit-exact comparison when margin < ``band``
     (the 1e-6 band stated for the ratio test) or draw_margin < ``draw_band``
     (the terminal draw has no stated band; 2e-8 covers float32 evaluation of
@@ -329,6 +362,8 @@ def accept_sample(target_logits, draft_logits, temperature, uniforms, final_unif
     accept_index = np.full((b, s1), -1, np.int64)
     accept_length = np.zeros(b, np.int64)
     margin = np.full(b, np.inf)
+    ratio_margin = np.full(b, np.inf)
+    z_min = np.full(b, np.inf)
     draw_margin = np.full(b, np.inf)
     status = 0
     for r in range(b):
@@ -351,12 +386,14 @@ def accept_sample(target_logits, draft_logits, temperature, uniforms, final_unif
                 thr = min(1.0, ratio)
                 u = float(uniforms[r, c])
                 margin[r] = min(margin[r], abs(u - thr))
+                ratio_margin[r] = min(ratio_margin[r], abs(u - thr))
                 if u < thr:
                     hit = c
                     break
                 resid = np.maximum(R - q, 0.0)
                 Z = resid.sum()
                 margin[r] = min(margin[r], Z)
+                z_min[r] = min(z_min[r], Z)
                 if Z > 0:
                     R = resid / Z
                 else:
@@ -382,7 +419,7 @@ def accept_sample(target_logits, draft_logits, temperature, uniforms, final_unif
         predict[row] = x
         accept_length[r] = cnt + 1
     return dict(predict=predict, accept_index=accept_index, accept_length=accept_length,
-                margin=margin, draw_margin=draw_margin,
+                margin=margin, ratio_margin=ratio_margin, z_min=z_min, draw_margin=draw_margin,
                 exempt=(margin < band) | (draw_margin < draw_band), status=status)
 
 
@@ -416,6 +453,8 @@ def accept_target_only(target_logits, temperature, threshold_single, threshold_a
     accept_index = np.full((b, s1), -1, np.int64)
     accept_length = np.zeros(b, np.int64)
     margin = np.full(b, np.inf)
+    ratio_margin = np.full(b, np.inf)
+    z_min = np.full(b, np.inf)
     draw_margin = np.full(b, np.inf)
     status = 0
     for r in range(b):
@@ -467,7 +506,7 @@ def accept_target_only(target_logits, temperature, threshold_single, threshold_a
         predict[row] = x
         accept_length[r] = cnt + 1
     return dict(predict=predict, accept_index=accept_index, accept_length=accept_length,
-                margin=margin, draw_margin=draw_margin,
+                margin=margin, ratio_margin=ratio_margin, z_min=z_min, draw_margin=draw_margin,
                 exempt=(margin < band) | (draw_margin < draw_band), status=status)
 
 

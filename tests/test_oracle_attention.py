@@ -144,3 +144,51 @@ def test_softmax_scale_default():
     want = W.decode(cfg, w.v_pool[0, slots, 0]).astype(np.float64).mean(axis=0)
     np.testing.assert_allclose(out[r * n + k, 0], want, rtol=1e-12)
     assert math.isclose(1 / math.sqrt(cfg.head_dim), 0.125)
+
+
+def _unit(w, mask, r, g):
+    cfg = w.cfg
+    return oracle.verify_attention_unit(w.q, w.k_pool[0], w.v_pool[0], w.page_table, w.seq_lens,
+                                        w.out_cache_loc, mask, cfg.num_q_heads, cfg.num_kv_heads,
+                                        cfg.page_size, cfg.dtype, r, g)
+
+
+@pytest.mark.parametrize("cid,cfg", list(_cases()), ids=lambda x: str(x) if isinstance(x, int) else "")
+def test_unit_form_path_equivalence_sdpa(cid, cfg):
+    """The whole-unit evaluation (all n * G queries of one request and KV
+    head as one score matrix) against torch's attention along each node's
+    path, and against the per-vector evaluation."""
+    w = W.make_workload(cfg, 1000 * cid + 5)
+    t = _tree(w)
+    per_vec = _run(w, t["mask"])
+    n, G = cfg.num_draft_tokens, cfg.group
+    q, K, V = _f64(w, w.q), _f64(w, w.k_pool[0]), _f64(w, w.v_pool[0])
+    for r in range(cfg.batch):
+        L = int(w.seq_lens[r])
+        hist = [w.slot(r, p) for p in range(L)]
+        for g in range(cfg.num_kv_heads):
+            u = _unit(w, t["mask"], r, g)
+            np.testing.assert_allclose(u.reshape(n, G, -1),
+                                       per_vec[r * n:(r + 1) * n, g * G:(g + 1) * G],
+                                       rtol=1e-11, atol=1e-12)
+            for k in range(n):
+                path = _path(t["parent"][r], k)
+                slots = hist + [int(w.out_cache_loc[r * n + j]) for j in path]
+                kk = K[slots, g].unsqueeze(0).unsqueeze(0)
+                vv = V[slots, g].unsqueeze(0).unsqueeze(0)
+                qq = q[r * n + k, g * G:(g + 1) * G].unsqueeze(0).unsqueeze(2)   # [1, G, 1, d]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qq, kk.expand(1, G, -1, -1), vv.expand(1, G, -1, -1))[0, :, 0]
+                np.testing.assert_allclose(u[k], ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_unit_form_planted_mask_error_fails():
+    """A unit evaluation that lets every node see every tree key differs from
+    the per-vector evaluation (the pin above would catch it)."""
+    cfg = W.shrink(W.CONFIGS[5], batch=1, hist=("fixed", 10), vocab=64)
+    w = W.make_workload(cfg, 31)
+    t = _tree(w)
+    full = np.ones_like(t["mask"])
+    a = _unit(w, t["mask"], 0, 0)
+    bad = _unit(w, full, 0, 0)
+    assert np.abs(a - bad).max() > 1e-3
