@@ -30,6 +30,22 @@
  *   - -1 means "none" in retrieve_* and accept_index ([P1] 邻接表:retrieve_* 三兄弟).
  *   - Tree node k of request b occupies flattened verify row b*n + k.
  *   - bf16 tensors are raw bfloat16 (16-bit) values; f32 are IEEE binary32.
+ *   - Every call may be recorded into a HIP graph (stream capture).  A
+ *     recorded call may later run beside other streams' kernels, and a graph
+ *     does not keep a cooperative launch's co-residency guarantee, so the
+ *     accepts record forms whose outputs never depend on other workgroups
+ *     being scheduled: the greedy and target-only tree walks run as a kernel
+ *     of their own after the vocabulary sweep; the sampled walk runs its
+ *     co-resident form as an ordinary kernel followed by a recovery kernel
+ *     that walks again, one workgroup per request, every request whose
+ *     wait gave up.  Recorded calls therefore never raise SPEC_ST_SYNC.
+ *     Eager calls use the one-launch forms: a cooperative launch (sampled),
+ *     or walkers fewer than the device holds at once that wait only on
+ *     sweep work (greedy, target-only).
+ *   - Waits between workgroups are bounded: after SPEC_POLL_LIMIT polls of
+ *     one slot (environment variable read on every call, decimal, default
+ *     1048576, about a second) a wait gives up; in an eager call it raises
+ *     SPEC_ST_SYNC.
  */
 #ifndef SPECMI_SPEC_H
 #define SPECMI_SPEC_H

@@ -38,6 +38,7 @@ SPEC_ST_RANGE = 1
 SPEC_ST_NOT_CLOSED = 2
 SPEC_ST_DEPTH = 4
 SPEC_ST_ZERO_RESIDUAL = 8
+SPEC_ST_SYNC = 16
 
 SPEC_F32 = 0
 SPEC_BF16 = 1

@@ -16,15 +16,15 @@
 // `batch` workgroups of the grid walk a request each after their own chunk.
 // A walker waits only for chunk work, which never waits, and fewer walkers
 // than the device holds at once always leave room for the chunk workgroups
-// still to run, in whatever order they are dispatched.  Otherwise a second
-// launch walks (its polls find every slot written).
+// still to run, in whatever order they are dispatched.  Otherwise, and
+// whenever the call is recorded into a graph (where other streams' kernels
+// may hold the device), a second launch walks: its polls find every slot
+// written.
 #include "sweep_common.h"
 
 using namespace spec;
 
 namespace {
-
-constexpr unsigned kSpinLimit = 1u << 20;   // polls of one slot before giving up
 
 // A row's best entry as one 64-bit key: the value's order-preserving bits
 // above, 0xFFFFFFFF - index below, so a larger key is a larger value or,
@@ -49,6 +49,7 @@ struct GreedyArgs {
     const int32_t *cand, *r_index, *r_next, *r_sib;
     int32_t *predict, *accept_index, *accept_length, *target_predict, *status;
     uint64_t *slots;     // [batch * n][nchunks] chunk keys, written once per call
+    unsigned poll_limit; // polls of one slot before giving up
 };
 
 // The best entry of chunk t % nchunks of verify row t / nchunks into slot t.
@@ -117,7 +118,7 @@ __device__ void walk_request(const GreedyArgs &A, int b) {
             if (j >= nslots) continue;
             uint64_t k = k4[u];
             for (unsigned spins = 0; k == 0; ++spins) {
-                if (spins >= kSpinLimit || (__hip_atomic_load(&s_err, __ATOMIC_RELAXED,
+                if (spins >= A.poll_limit || (__hip_atomic_load(&s_err, __ATOMIC_RELAXED,
                                                              __HIP_MEMORY_SCOPE_WORKGROUP) &
                                             SPEC_ST_SYNC)) {
                     atomicOr(&s_err, SPEC_ST_SYNC);
@@ -261,8 +262,10 @@ extern "C" int spec_accept_greedy(int batch, int n, int s1, int64_t vocab, int d
     A.target_predict = target_predict;
     A.status = dev_status;
     A.slots = static_cast<uint64_t *>(workspace);
+    A.poll_limit = spec::poll_limit();
     const dim3 grid((unsigned)items);
-    const bool fused = batch < (dtype == SPEC_BF16 ? fused_capacity<SPEC_BF16>()
+    const bool fused = !spec::stream_capturing(st) &&
+                       batch < (dtype == SPEC_BF16 ? fused_capacity<SPEC_BF16>()
                                                    : fused_capacity<SPEC_F32>());
     if (fused) {
         if (dtype == SPEC_BF16)

@@ -25,14 +25,14 @@
 // polled and cleared before the walker ends (the workspace is zero after
 // every call).  Walkers wait only for chunk work, which never waits; with
 // fewer walkers than the device holds at once, one launch suffices,
-// otherwise a second launch walks.
+// otherwise (and whenever the call is recorded into a graph, where other
+// streams' kernels may hold the device) a second launch walks.
 #include "sweep_common.h"
 
 using namespace spec;
 
 namespace {
 
-constexpr unsigned kSpinLimit = 1u << 20;   // polls of one slot before giving up
 constexpr uint64_t kCode = 0x7FF4DEAD0BADF00Dull;   // XOR code: a NaN pattern no
                                                     // max or sum takes
 constexpr int kScanPer = kChunk / kSweepThreads;   // entries per thread, terminal scan
@@ -54,6 +54,7 @@ struct TargetArgs {
     const int32_t *cand, *r_index, *r_next, *r_sib;
     int32_t *predict, *accept_index, *accept_length, *status;
     uint64_t *slots;                    // [batch * n][nchunks][2] (max bits, sum bits), coded
+    unsigned poll_limit;                // polls of one slot before giving up
 };
 
 template <int DT>
@@ -142,11 +143,12 @@ __device__ __forceinline__ void chunk_item(const TargetArgs &A, int64_t t, float
 }
 
 // Both words of a slot, polled until written (bounded); false on timeout.
-__device__ __forceinline__ bool read_slot(const uint64_t *slot, float &m, double &s) {
+__device__ __forceinline__ bool read_slot(const uint64_t *slot, unsigned limit, float &m,
+                                          double &s) {
     uint64_t w0 = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint64_t w1 = __hip_atomic_load(slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (unsigned spins = 0; w0 == 0 || w1 == 0; ++spins) {
-        if (spins >= kSpinLimit) {
+        if (spins >= limit) {
             m = -INFINITY;
             s = 0.0;
             return false;
@@ -252,7 +254,7 @@ __device__ void walk_request(const TargetArgs &A, int b) {
             cm[k] = -INFINITY;
             cs[k] = 0.0;
             if (j0 + k < nch) {
-                sync_ok &= read_slot(A.slots + 2 * (row * nch + j0 + k), cm[k], cs[k]);
+                sync_ok &= read_slot(A.slots + 2 * (row * nch + j0 + k), A.poll_limit, cm[k], cs[k]);
                 S.cmax[j0 + k] = cm[k];
             }
             mloc = fmaxf(mloc, cm[k]);
@@ -449,7 +451,7 @@ __device__ void walk_request(const TargetArgs &A, int b) {
     for (int q = tid; q < nslots; q += blockDim.x) {
         float m;
         double sv;
-        ok &= read_slot(rs + 2 * q, m, sv);
+        ok &= read_slot(rs + 2 * q, A.poll_limit, m, sv);
         __hip_atomic_store(rs + 2 * q, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(rs + 2 * q + 1, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -487,7 +489,7 @@ int fused_capacity() {
 
 template <int DT>
 void launch(const TargetArgs &A, int64_t items, hipStream_t st) {
-    const bool fused = A.batch < fused_capacity<DT>();
+    const bool fused = !spec::stream_capturing(st) && A.batch < fused_capacity<DT>();
     const dim3 grid((unsigned)items);
     if (fused) {
         hipLaunchKernelGGL((target_only_kernel<DT, true>), grid, dim3(kSweepThreads), 0, st, A);
@@ -551,6 +553,7 @@ extern "C" int spec_accept_target_only(int batch, int n, int s1, int64_t vocab, 
     A.accept_length = accept_length;
     A.status = dev_status;
     A.slots = static_cast<uint64_t *>(workspace);
+    A.poll_limit = spec::poll_limit();
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (dtype == SPEC_BF16) launch<SPEC_BF16>(A, items, st);
     else launch<SPEC_F32>(A, items, st);

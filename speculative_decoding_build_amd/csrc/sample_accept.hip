@@ -29,7 +29,19 @@
 // used, so the workspace is zero again after every call.  Every thread of
 // every workgroup of a request evaluates the same decisions from the same
 // data, so decisions need no communication.  When the grid cannot be
-// co-resident the walk runs as one 1024-thread workgroup per request.
+// co-resident the walk runs as one 1024-thread workgroup per request, which
+// never waits on another workgroup.
+//
+// Launch forms.  Eager calls launch the co-resident form cooperatively (the
+// runtime guarantees co-residency; a wait that still gives up raises
+// SPEC_ST_SYNC).  A graph does not record the cooperative guarantee, and a
+// recorded kernel may run beside other streams' kernels, so a recorded call
+// launches the co-resident form as an ordinary kernel followed by a recovery
+// kernel of one workgroup per request: a request whose wait gave up in the
+// first kernel is flagged there, and the recovery kernel walks it again
+// alone (overwriting whatever the first kernel wrote for it); unflagged
+// requests return at once.  Neither kernel waits without bound, and every
+// request ends with a complete walk.
 //
 // Per-entry probabilities are float32 exponentials (the hardware base-2
 // exponential) of the argument (x - max) log2(e) / T carried as a float
@@ -44,7 +56,6 @@ namespace {
 
 constexpr int kSoloThreads = 1024;
 constexpr int kCoopThreads = 256;
-constexpr unsigned kSpinLimit = 1u << 20;      // polls of one slot before giving up
 constexpr int kCoopGridTarget = 512;           // workgroups of a cooperative walk, all requests
 constexpr int kMaxGroups = 64;                 // slices per request (one wave gathers them)
 constexpr int kCacheEntries = 16;              // row entries a walk thread keeps in registers
@@ -279,6 +290,8 @@ struct WalkArgs {
     int E;              // exchanges a request may make
     uint64_t *xch;      // [batch][E][G][kSlotWords] exchange slots (G > 1)
     unsigned *done;     // [batch] workgroups finished (G > 1)
+    unsigned *redo;     // [batch] recorded form: requests to walk again; else null
+    unsigned poll_limit;  // polls of one slot before giving up
 };
 
 template <int NT>
@@ -311,8 +324,9 @@ __device__ __forceinline__ void load_words(const uint64_t *slot, uint64_t (&w)[W
 // a time (more polls in flight only add traffic to the lines every
 // workgroup is polling, and arrive later).
 template <int W>
-__device__ __forceinline__ bool read_slot(const uint64_t *slot, uint64_t (&bits)[W]) {
-    for (unsigned spins = 0; spins < kSpinLimit; ++spins) {
+__device__ __forceinline__ bool read_slot(const uint64_t *slot, unsigned limit,
+                                          uint64_t (&bits)[W]) {
+    for (unsigned spins = 0; spins < limit; ++spins) {
         uint64_t w[W];
         load_words<W>(slot, w);
         bool all = true;
@@ -346,6 +360,8 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     const int req = COOP ? blockIdx.x / G : blockIdx.x;
     const int g = COOP ? blockIdx.x % G : 0;
     const int tid = threadIdx.x;
+    // the recovery kernel walks only the requests the first kernel flagged
+    if (!COOP && A.redo != nullptr && A.redo[req] == 0) return;
     const int n = A.n;
     const int base = req * n;
     const size_t eb = DT == SPEC_BF16 ? 2 : 4;
@@ -457,7 +473,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                     double jst = 0.0, jsd = 0.0;
                     if (tid < G) {
                         uint64_t w[kWords];
-                        if (!read_slot<kWords>(slot(e, tid), w)) {
+                        if (!read_slot<kWords>(slot(e, tid), A.poll_limit, w)) {
                             atomicOr(&S.err, SPEC_ST_SYNC);
                         } else {
                             jmt = __uint_as_float((uint32_t)w[0]);
@@ -508,7 +524,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             sj = 0.0;
             uint64_t w[1];
             if (tid < G) {
-                if (read_slot<1>(slot(e, tid), w)) sj = __builtin_bit_cast(double, w[0]);
+                if (read_slot<1>(slot(e, tid), A.poll_limit, w)) sj = __builtin_bit_cast(double, w[0]);
                 else atomicOr(&S.err, SPEC_ST_SYNC);
             }
             const double tot = full_wave_sum_d(sj);
@@ -776,7 +792,15 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
             A.accept_index[(int64_t)req * A.s1 + j] = (j <= cnt) ? S.ai[j] : -1;
         if (tid == 0) A.accept_length[req] = cnt + 1;
     }
-    if (tid == 0) raise_status(A.status, S.err);
+    if (COOP && A.redo != nullptr && (S.err & SPEC_ST_SYNC)) {
+        // a wait gave up: the recovery kernel walks this request again and
+        // reports its status
+        if (tid == 0)
+            __hip_atomic_store(A.redo + req, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (tid == 0) {
+        raise_status(A.status, S.err);
+    }
+    if (!COOP && A.redo != nullptr && tid == 0) A.redo[req] = 0;
 
     // the last workgroup of the request to get here clears the request's
     // slots: every other one has read all it will read
@@ -848,12 +872,16 @@ CoopPlan coop_plan(int batch, int64_t vocab) {
     return CoopPlan{(int)G, slice, slice / kCoopThreads <= kCacheEntries};
 }
 
-size_t sample_workspace_layout(int batch, int n, int64_t vocab, size_t *off_done) {
+// [exchange slots][done counters][recovery flags], each 256-byte aligned
+size_t sample_workspace_layout(int batch, int n, int64_t vocab, size_t *off_done,
+                               size_t *off_redo) {
     const size_t xch = spec::align_up((size_t)batch * exchanges_per_request(n) *
                                           group_cap(batch, vocab) * kSlotWords * sizeof(uint64_t),
                                       256);
+    const size_t per_req = spec::align_up((size_t)batch * sizeof(unsigned), 256);
     if (off_done) *off_done = xch;
-    return xch + spec::align_up((size_t)batch * sizeof(unsigned), 256);
+    if (off_redo) *off_redo = xch + per_req;
+    return xch + 2 * per_req;
 }
 
 template <int DT>
@@ -862,8 +890,8 @@ int launch_sample(int batch, int n, int s1, int64_t vocab, const void *tl, const
                   const int32_t *cand, const int32_t *ri, const int32_t *rn, const int32_t *rs,
                   int32_t *predict, int32_t *ai, int32_t *al, void *workspace,
                   int32_t *dev_status, hipStream_t st) {
-    size_t off_done = 0;
-    sample_workspace_layout(batch, n, vocab, &off_done);
+    size_t off_done = 0, off_redo = 0;
+    sample_workspace_layout(batch, n, vocab, &off_done, &off_redo);
     const size_t eb = DT == SPEC_BF16 ? 2 : 4;
     WalkArgs A{};
     A.n = n;
@@ -887,32 +915,40 @@ int launch_sample(int batch, int n, int s1, int64_t vocab, const void *tl, const
     A.E = exchanges_per_request(n);
     A.xch = static_cast<uint64_t *>(workspace);
     A.done = reinterpret_cast<unsigned *>(static_cast<char *>(workspace) + off_done);
+    A.poll_limit = spec::poll_limit();
+    A.redo = nullptr;
     const CoopPlan pl = coop_plan<DT>(batch, vocab);
+    const int64_t solo_slice =
+        ((vocab + kSoloThreads - 1) / kSoloThreads + 7) / 8 * 8 * kSoloThreads;
     if (pl.G >= 2) {
         A.G = pl.G;
         A.slice = pl.slice;
         const dim3 grid((unsigned)(batch * pl.G)), block(kCoopThreads);
-        const void *fn = pl.cache
-            ? reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true, true>)
-            : reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true, false>);
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive) {
-            // recorded into a graph: an ordinary launch of a grid sized to
-            // what the device holds at once
+        if (spec::stream_capturing(st)) {
+            // recorded: the co-resident form as an ordinary launch, then the
+            // recovery kernel for requests whose wait gave up
+            A.redo = reinterpret_cast<unsigned *>(static_cast<char *>(workspace) + off_redo);
             if (pl.cache)
                 hipLaunchKernelGGL((sample_walk_kernel<DT, kCoopThreads, true, true>), grid, block,
                                    0, st, A);
             else
                 hipLaunchKernelGGL((sample_walk_kernel<DT, kCoopThreads, true, false>), grid, block,
                                    0, st, A);
+            A.G = 1;
+            A.slice = solo_slice;
+            hipLaunchKernelGGL((sample_walk_kernel<DT, kSoloThreads, false, false>), dim3(batch),
+                               dim3(kSoloThreads), 0, st, A);
             return launch_status();
         }
+        const void *fn = pl.cache
+            ? reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true, true>)
+            : reinterpret_cast<const void *>(sample_walk_kernel<DT, kCoopThreads, true, false>);
         void *args[] = {&A};
         if (hipLaunchCooperativeKernel(fn, grid, block, args, 0, st) == hipSuccess) return SPEC_OK;
         (void)hipGetLastError();   // fall back below
     }
     A.G = 1;
-    A.slice = ((vocab + kSoloThreads - 1) / kSoloThreads + 7) / 8 * 8 * kSoloThreads;
+    A.slice = solo_slice;
     hipLaunchKernelGGL((sample_walk_kernel<DT, kSoloThreads, false, false>), dim3(batch),
                        dim3(kSoloThreads), 0, st, A);
     return launch_status();
@@ -923,7 +959,7 @@ int launch_sample(int batch, int n, int s1, int64_t vocab, const void *tl, const
 extern "C" size_t spec_accept_workspace_size(int batch, int n, int64_t vocab, int sampled) {
     if (batch <= 0 || n <= 0 || vocab <= 0) return 0;
     if (!sampled) return spec_greedy_workspace_bytes(batch, n, vocab);
-    return sample_workspace_layout(batch, n, vocab, nullptr);
+    return sample_workspace_layout(batch, n, vocab, nullptr, nullptr);
 }
 
 extern "C" int spec_accept_sample(int batch, int n, int s1, int64_t vocab, int dtype,

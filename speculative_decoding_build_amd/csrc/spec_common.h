@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "../../include/spec.h"
 
@@ -75,6 +76,28 @@ inline int resident_capacity(const void *kernel, int threads, bool need_coop = f
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess)
         return 0;
     return cus * per;
+}
+
+// Polls of one exchange or key slot before a wait gives up and raises
+// SPEC_ST_SYNC: 2^20 (about a second), or the value of the environment
+// variable SPEC_POLL_LIMIT when it holds a decimal number up to 2^30.  Read
+// on every call; a small value forces the time-out path from the host.
+inline unsigned poll_limit() {
+    constexpr unsigned kDefault = 1u << 20;
+    const char *s = getenv("SPEC_POLL_LIMIT");
+    if (s == nullptr || *s == 0) return kDefault;
+    char *end = nullptr;
+    const unsigned long v = strtoul(s, &end, 10);
+    if (*end != 0 || v > (1ul << 30)) return kDefault;
+    return (unsigned)v;
+}
+
+// True while `st` records into a graph.  A recorded kernel may run beside
+// kernels of other streams, so forms whose workgroups wait on each other are
+// not recorded.
+inline bool stream_capturing(hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
 }
 
 }  // namespace spec

@@ -23,6 +23,7 @@ import pytest
 import torch
 
 import oracle
+from _bands import assert_only_ratio_band
 import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -246,6 +247,7 @@ def test_sampled_accept_on_filtered_logits(cid):
     greedy = oracle.accept_greedy(tl, *args)
     say(f"[filter+sample] cfg{cid}: lengths {o['accept_length'].tolist()} greedy "
         f"{greedy['accept_length'].tolist()}")
+    assert_only_ratio_band(o, f"filtered cfg{cid}")
     for r in range(b):
         if o["exempt"][r] or near[r * n:(r + 1) * n].any():
             continue

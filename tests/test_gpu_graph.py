@@ -5,9 +5,10 @@ The five operations are captured once (torch.cuda.CUDAGraph on the stream
 the binding launches on) and the graph is replayed three times.  Between
 replays the program does its own eager work: it restores the KV pools that
 compaction moved, refills every output with a marker, runs an eager tree
-build on other buffers and synchronises.  Under capture the sampled walk is
-launched as an ordinary kernel whose grid fits on the device at once (a
-cooperative launch is not recorded), so this also checks that launch form.
+build on other buffers and synchronises.  Recorded, the accepts take their
+graph forms (the greedy walk as a kernel of its own after the sweep; the
+sampled walk's co-resident form as an ordinary launch followed by its
+recovery kernel), so this also checks that those give the eager results.
 """
 import sys
 
