@@ -221,28 +221,17 @@ int spec_check_accept_args(int batch, int n, int s1, int64_t vocab, int dtype) {
     return SPEC_OK;
 }
 
-extern "C" int spec_accept_greedy(int batch, int n, int s1, int64_t vocab, int dtype,
-                                  const void *target_logits, const int32_t *candidates,
-                                  const int32_t *retrieve_index,
-                                  const int32_t *retrieve_next_token,
-                                  const int32_t *retrieve_next_sibling, int32_t *predict,
-                                  int32_t *accept_index, int32_t *accept_length,
-                                  int32_t *target_predict, void *workspace,
-                                  size_t workspace_bytes, int32_t *dev_status,
-                                  spec_stream_t stream) {
-    int rc = spec_check_accept_args(batch, n, s1, vocab, dtype);
-    if (rc != SPEC_OK) return rc;
-    if (batch == 0) return SPEC_OK;
-    if (!target_logits || !candidates || !retrieve_index || !retrieve_next_token ||
-        !retrieve_next_sibling || !predict || !accept_index || !accept_length)
-        return SPEC_ERR_NULL;
-    if (!workspace || workspace_bytes < spec_greedy_workspace_bytes(batch, n, vocab) ||
-        reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
-        return SPEC_ERR_WORKSPACE;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+namespace {
+
+// Validated launch of the greedy accept over the key slots `slots` (zero on
+// entry; left zero unless a wait gave up).
+int launch_greedy(int batch, int n, int s1, int64_t vocab, int dtype, const void *target_logits,
+                  const int32_t *candidates, const int32_t *retrieve_index,
+                  const int32_t *retrieve_next_token, const int32_t *retrieve_next_sibling,
+                  int32_t *predict, int32_t *accept_index, int32_t *accept_length,
+                  int32_t *target_predict, uint64_t *slots, int32_t *dev_status, hipStream_t st) {
     const int nch = num_chunks(vocab);
     const int64_t items = (int64_t)batch * n * nch;
-    if (items > INT_MAX) return SPEC_ERR_UNSUPPORTED;
     const size_t eb = dtype == SPEC_BF16 ? 2 : 4;
     GreedyArgs A{};
     A.logits = target_logits;
@@ -261,7 +250,7 @@ extern "C" int spec_accept_greedy(int batch, int n, int s1, int64_t vocab, int d
     A.accept_length = accept_length;
     A.target_predict = target_predict;
     A.status = dev_status;
-    A.slots = static_cast<uint64_t *>(workspace);
+    A.slots = slots;
     A.poll_limit = spec::poll_limit();
     const dim3 grid((unsigned)items);
     const bool fused = !spec::stream_capturing(st) &&
@@ -282,3 +271,43 @@ extern "C" int spec_accept_greedy(int batch, int n, int s1, int64_t vocab, int d
     return spec::launch_status();
 }
 
+// Host checks shared by both entry points: SPEC_OK, a SPEC_ERR_* code, or 1
+// for a valid empty call.
+int check_greedy(int batch, int n, int s1, int64_t vocab, int dtype, const void *target_logits,
+                 const int32_t *candidates, const int32_t *retrieve_index,
+                 const int32_t *retrieve_next_token, const int32_t *retrieve_next_sibling,
+                 const int32_t *predict, const int32_t *accept_index,
+                 const int32_t *accept_length) {
+    int rc = spec_check_accept_args(batch, n, s1, vocab, dtype);
+    if (rc != SPEC_OK) return rc;
+    if (batch == 0) return 1;
+    if (!target_logits || !candidates || !retrieve_index || !retrieve_next_token ||
+        !retrieve_next_sibling || !predict || !accept_index || !accept_length)
+        return SPEC_ERR_NULL;
+    if ((int64_t)batch * n * num_chunks(vocab) > INT_MAX) return SPEC_ERR_UNSUPPORTED;
+    return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" int spec_accept_greedy(int batch, int n, int s1, int64_t vocab, int dtype,
+                                  const void *target_logits, const int32_t *candidates,
+                                  const int32_t *retrieve_index,
+                                  const int32_t *retrieve_next_token,
+                                  const int32_t *retrieve_next_sibling, int32_t *predict,
+                                  int32_t *accept_index, int32_t *accept_length,
+                                  int32_t *target_predict, void *workspace,
+                                  size_t workspace_bytes, int32_t *dev_status,
+                                  spec_stream_t stream) {
+    const int rc = check_greedy(batch, n, s1, vocab, dtype, target_logits, candidates,
+                                retrieve_index, retrieve_next_token, retrieve_next_sibling,
+                                predict, accept_index, accept_length);
+    if (rc != SPEC_OK) return rc == 1 ? SPEC_OK : rc;
+    if (!workspace || workspace_bytes < spec_greedy_workspace_bytes(batch, n, vocab) ||
+        reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
+        return SPEC_ERR_WORKSPACE;
+    return launch_greedy(batch, n, s1, vocab, dtype, target_logits, candidates, retrieve_index,
+                         retrieve_next_token, retrieve_next_sibling, predict, accept_index,
+                         accept_length, target_predict, static_cast<uint64_t *>(workspace),
+                         dev_status, reinterpret_cast<hipStream_t>(stream));
+}
