@@ -222,6 +222,29 @@ int spec_accept_greedy(int batch, int num_draft_tokens, int accept_width, int64_
                        spec_stream_t stream);
 
 /*
+ * spec_accept_greedy without a workspace, for callers that cannot allocate
+ * device memory: code under graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments, outputs and errors as
+ * spec_accept_greedy.  The chunk keys live in a fixed array inside the
+ * library (1 MiB on each device the library runs on, held until the
+ * process ends): a call needs batch * n * ceil(vocab / 8192) <= 131072
+ * keys, else SPEC_ERR_WORKSPACE (e.g. up to 128 requests of 64 nodes at
+ * vocabulary 128256).  Each call first clears the keys it uses (a kernel on
+ * `stream`, no memset), then runs the accept.  Every call on one device
+ * shares that device's array: calls that may overlap on one device
+ * (different streams, or host threads without ordering) race.  The first
+ * call on a device looks the array's address up with that device current
+ * (SPEC_ERR_HIP if the lookup fails).
+ */
+int spec_accept_greedy_noalloc(int batch, int num_draft_tokens, int accept_width, int64_t vocab,
+                               int dtype, const void *target_logits, const int32_t *candidates,
+                               const int32_t *retrieve_index, const int32_t *retrieve_next_token,
+                               const int32_t *retrieve_next_sibling, int32_t *predict,
+                               int32_t *accept_index, int32_t *accept_length,
+                               int32_t *target_predict, int32_t *dev_status,
+                               spec_stream_t stream);
+
+/*
  * Rejection-sampled tree accept.  [P4] 接受/拒绝 and [P2] 四 (Classic
  * Rejection Sampling); [P5] 5.6 (same walk, other test).
  *

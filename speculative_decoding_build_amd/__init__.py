@@ -47,7 +47,8 @@ SPEC_MASK_QLEN_BITS = 2
 
 EXPORTS = ("spec_version", "spec_status_string", "spec_mask_word_bytes", "spec_build_tree",
            "spec_verify_attention_workspace_size", "spec_verify_attention",
-           "spec_accept_workspace_size", "spec_accept_greedy", "spec_accept_sample",
+           "spec_accept_workspace_size", "spec_accept_greedy", "spec_accept_greedy_noalloc",
+           "spec_accept_sample",
            "spec_accept_target_only_workspace_size", "spec_accept_target_only",
            "spec_draft_step_workspace_size", "spec_draft_step",
            "spec_sampling_filter_workspace_size", "spec_sampling_filter", "spec_full_mask",
@@ -79,6 +80,8 @@ _decl("spec_verify_attention", _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _
 _decl("spec_accept_workspace_size", _SZ, _I, _I, _I64, _I)
 _decl("spec_accept_greedy", _I, _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
       _SZ, _P, _P)
+_decl("spec_accept_greedy_noalloc", _I, _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+      _P, _P, _P)
 _decl("spec_accept_sample", _I, _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
       _P, _P, _P, _SZ, _P, _P)
 _decl("spec_accept_target_only_workspace_size", _SZ, _I, _I, _I64)
@@ -253,6 +256,30 @@ def spec_accept_greedy(batch, num_draft_tokens, accept_width, vocab, dtype, targ
     ]
     _check("spec_accept_greedy", _lib.spec_accept_greedy(batch, n, accept_width, vocab, dtype,
                                                           *args, _stream(stream)))
+
+
+def spec_accept_greedy_noalloc(batch, num_draft_tokens, accept_width, vocab, dtype,
+                               target_logits, candidates, retrieve_index, retrieve_next_token,
+                               retrieve_next_sibling, predict, accept_index, accept_length,
+                               target_predict=None, dev_status=None, stream=None):
+    dev = _device()
+    n = num_draft_tokens
+    bn = batch * n
+    args = [
+        _ptr(target_logits, "target_logits", dev, nbytes=bn * vocab * _ELEM.get(dtype, 4)),
+        _ptr(candidates, "candidates", dev, nbytes=bn * 4),
+        _ptr(retrieve_index, "retrieve_index", dev, nbytes=bn * 4),
+        _ptr(retrieve_next_token, "retrieve_next_token", dev, nbytes=bn * 4),
+        _ptr(retrieve_next_sibling, "retrieve_next_sibling", dev, nbytes=bn * 4),
+        _ptr(predict, "predict", dev, nbytes=bn * 4),
+        _ptr(accept_index, "accept_index", dev, nbytes=batch * accept_width * 4),
+        _ptr(accept_length, "accept_length", dev, nbytes=batch * 4),
+        _ptr(target_predict, "target_predict", dev, nbytes=bn * 4, optional=True),
+        _ptr(dev_status, "dev_status", dev, nbytes=4, optional=True),
+    ]
+    _check("spec_accept_greedy_noalloc",
+           _lib.spec_accept_greedy_noalloc(batch, n, accept_width, vocab, dtype, *args,
+                                           _stream(stream)))
 
 
 def spec_accept_sample(batch, num_draft_tokens, accept_width, vocab, dtype, target_logits,

@@ -20,6 +20,9 @@
 // whenever the call is recorded into a graph (where other streams' kernels
 // may hold the device), a second launch walks: its polls find every slot
 // written.
+#include <algorithm>
+#include <mutex>
+
 #include "sweep_common.h"
 
 using namespace spec;
@@ -310,4 +313,67 @@ extern "C" int spec_accept_greedy(int batch, int n, int s1, int64_t vocab, int d
                          retrieve_next_token, retrieve_next_sibling, predict, accept_index,
                          accept_length, target_predict, static_cast<uint64_t *>(workspace),
                          dev_status, reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing: the key slots live in a fixed
+// array of the library, one copy per device.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int64_t kNoAllocSlots = 131072;   // 1 MiB of 64-bit keys
+static __device__ __align__(256) uint64_t scratch[kNoAllocSlots];
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+uint64_t *scratch_ptr[kMaxDevices];         // written once per device, under scratch_once
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with it current), or null if the lookup failed.  The
+// array's host-side name is not a device address and is never passed on.
+uint64_t *scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(scratch_once[dev], [dev] {
+        void *p = nullptr;
+        scratch_ptr[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess
+                               ? static_cast<uint64_t *>(p) : nullptr;
+    });
+    return scratch_ptr[dev];
+}
+
+__global__ __launch_bounds__(256) void clear_slots_kernel(uint64_t *slots, int64_t count) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * 256)
+        slots[i] = 0;
+}
+
+}  // namespace
+
+extern "C" int spec_accept_greedy_noalloc(int batch, int n, int s1, int64_t vocab, int dtype,
+                                          const void *target_logits, const int32_t *candidates,
+                                          const int32_t *retrieve_index,
+                                          const int32_t *retrieve_next_token,
+                                          const int32_t *retrieve_next_sibling,
+                                          int32_t *predict, int32_t *accept_index,
+                                          int32_t *accept_length, int32_t *target_predict,
+                                          int32_t *dev_status, spec_stream_t stream) {
+    const int rc = check_greedy(batch, n, s1, vocab, dtype, target_logits, candidates,
+                                retrieve_index, retrieve_next_token, retrieve_next_sibling,
+                                predict, accept_index, accept_length);
+    if (rc != SPEC_OK) return rc == 1 ? SPEC_OK : rc;
+    const int64_t used = (int64_t)batch * n * num_chunks(vocab);
+    if (used > kNoAllocSlots) return SPEC_ERR_WORKSPACE;
+    uint64_t *slots = scratch_address();
+    if (slots == nullptr) return SPEC_ERR_HIP;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // the array keeps the last call's contents (a call whose wait gave up
+    // may leave keys behind): the slots this call uses start at zero
+    const unsigned blocks = (unsigned)std::min<int64_t>((used + 255) / 256, 512);
+    hipLaunchKernelGGL(clear_slots_kernel, dim3(blocks), dim3(256), 0, st, slots, used);
+    if (hipPeekAtLastError() != hipSuccess) return spec::launch_status();
+    return launch_greedy(batch, n, s1, vocab, dtype, target_logits, candidates, retrieve_index,
+                         retrieve_next_token, retrieve_next_sibling, predict, accept_index,
+                         accept_length, target_predict, slots, dev_status, st);
 }

@@ -106,6 +106,16 @@ def test_host_errors_before_launch():
     assert ag(1, 6, 4, 32, 9, *([P0] * 10), 0, P0, P0) == -3
     assert ag(1, 6, 4, 32, 0, *([P0] * 10), 0, P0, P0) == -1
     assert ag(0, 6, 4, 32, 0, *([P0] * 10), 0, P0, P0) == 0
+    na = lib.spec_accept_greedy_noalloc
+    na.restype = I
+    na.argtypes = [I, I, I, ctypes.c_int64, I] + [ctypes.c_void_p] * 11
+    f10 = [ctypes.c_void_p(0x1000)] * 9 + [P0, P0]
+    assert na(1, 6, 4, 32, 9, *f10) == -3
+    assert na(1, 6, 4, 32, 0, *([P0] * 11)) == -1
+    assert na(0, 6, 4, 32, 0, *([P0] * 11)) == 0
+    # 200 requests x 64 nodes x 16 chunks of a 128256 vocabulary: more keys
+    # than the library's fixed array holds (131072)
+    assert na(200, 64, 7, 128256, 1, *f10) == -5
     asm = lib.spec_accept_sample
     asm.restype = I
     asm.argtypes = [I, I, I, ctypes.c_int64, I] + [ctypes.c_void_p] * 12 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
