@@ -166,10 +166,11 @@ int spec_build_tree(int batch, int topk, int num_steps, int num_draft_tokens, in
  * softmax and accumulation are fp32 (online softmax); bf16 operands use the
  * matrix cores.
  * workspace: at least spec_verify_attention_workspace_size(...) bytes, any
- * contents.  Slots or page ids out of range raise SPEC_ST_RANGE and read as
- * zero vectors.
+ * contents.  Slots or page ids out of range raise SPEC_ST_RANGE; the output
+ * is then unspecified (no read leaves the pools).
  * Limits: 1 <= n <= 64; head_dim 64 or 128; num_q_heads % num_kv_heads == 0;
- * page_size >= 1; num_slots <= 2^31 - 1 (else SPEC_ERR_UNSUPPORTED).
+ * page_size >= 1; num_slots <= 2^31 - 1 (else SPEC_ERR_UNSUPPORTED);
+ * num_slots >= 1 when batch > 0 (else SPEC_ERR_SHAPE).
  */
 size_t spec_verify_attention_workspace_size(int batch, int num_draft_tokens, int num_q_heads,
                                             int num_kv_heads, int head_dim, int max_seq_len,

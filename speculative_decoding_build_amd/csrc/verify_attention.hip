@@ -223,21 +223,23 @@ __device__ void plan_split(const AttnParams &P, int j, bool store, int *out) {
 //
 // One workgroup: NW waves, each owning 32 query rows (one 32x32 MFMA column
 // block).  Per 64-key tile the pipeline is
+//     compute tile t (S^T = K Q^T, softmax, O^T += V^T P^T)
 //     write tile t+1 (registers -> LDS, V transposed)
 //     issue the global loads of tile t+3 (slots read from the LDS slot ring)
-//     compute tile t (S^T = K Q^T, softmax, O^T += V^T P^T)
 //     barrier
-// so two tiles of K/V are in flight while one is computed.  The slot ring
-// holds two chunks of 8 tiles; a chunk's page-table entries are loaded 7
-// tiles before the first load that needs them, so no tile waits on the page
-// table.
+// so two tiles of K/V are in flight while one is computed, and the wait for
+// tile t+1's loads comes after tile t's math.  A tile wholly inside the
+// split loads without per-key conditions.  The slot ring holds two chunks
+// of 8 tiles; a chunk's page-table entries are loaded 7 tiles before the
+// first load that needs them, so no tile waits on the page table.
 //
 // Softmax runs in the log2 domain on raw scores: p = exp2(s*C - m) with
-// C = scale*log2(e).  The running max m is raised (and O, l rescaled) only
-// when a score exceeds it by more than kLazy, so probabilities stay below
-// 2^kLazy and most tiles skip the rescale.
-
-constexpr float kLazy = 8.0f;
+// C = scale*log2(e).  A column's running max m is set by its first
+// sub-block with a visible key; later sub-blocks take no max: a score far
+// above m shows as a probability of 2^64 or more (or an infinite one), and
+// only then is m raised to that sub-block's max and O, l rescaled.  The
+// softmax is exact at any common offset, so probabilities up to 2^64 are
+// kept as they are.
 
 // KH = 2: the waves come in pairs that own the same 32 query rows and take
 // the two 32-key halves of every tile; the pair merges its (max, sum, O)
@@ -394,6 +396,34 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
     uint4 vreg0[VPER][4], vreg1[VPER][4];
     auto issue = [&](uint4 (&kr)[KPER], uint4 (&vr)[VPER][4], int t) {
         const int32_t *sl = &s_ring[(t / kChunkTiles) & 1][(t % kChunkTiles) * kTileKeys];
+        if (kb + (t + 1) * kTileKeys <= ke) {
+            // every key of the tile is in the split: unconditional loads (a
+            // slot the ring marks invalid, -1 after a range error, reads slot
+            // 0, which exists: the host refuses an empty pool; the call has
+            // then raised SPEC_ST_RANGE and its output is unspecified)
+#pragma unroll
+            for (int i = 0; i < KPER; ++i) {
+                const int u = tid + i * NT;
+                if (KUNITS % NT == 0 || u < KUNITS) {
+                    const int32_t slot = max(sl[u / (D / 8)], 0);
+                    kr[i] = *reinterpret_cast<const uint4 *>(
+                        kpool + ((int64_t)slot * P.hkv + kvh) * D + (u % (D / 8)) * 8);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < VPER; ++i) {
+                const int u = tid + i * NT;
+                if (VUNITS % NT == 0 || u < VUNITS) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int32_t slot = max(sl[(u % (kTileKeys / 4)) * 4 + j], 0);
+                        vr[i][j] = *reinterpret_cast<const uint4 *>(
+                            vpool + ((int64_t)slot * P.hkv + kvh) * D + (u / (kTileKeys / 4)) * 8);
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < KPER; ++i) {
             const int u = tid + i * NT;
@@ -483,8 +513,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
         const int tile_base = kb + it * kTileKeys;
         // write tile it+1 (registers -> LDS stage (it+1)&1), then reuse its
         // registers for tile it+LEAD
-        if (it + 1 < ntiles) stash(kr, vr, (it + 1) & 1);
-        if (it + LEAD < ntiles) issue(kr, vr, it + LEAD);
         if (it % kChunkTiles == kChunkTiles - LEAD) {
             const int cbase = kb + ((it + kChunkTiles + LEAD) / kChunkTiles) * kChunkKeys;
             if (cbase < ke) {
@@ -526,31 +554,43 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
                         sv[i] = vis ? sv[i] : -INFINITY;
                     }
                 }
-                float mx = sv[0];
+                // probabilities at the running max (set here by a column's
+                // first sub-block with a visible key; raised only when some
+                // probability reaches 2^64)
+                auto colmax = [&]() {
+                    float mx = sv[0];
 #pragma unroll
-                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * C;
-                // lazy rescale: raise the running max only when it is exceeded
-                // by more than kLazy (decided per wave, applied per lane)
-                const bool raise = mx > m_run + kLazy;
-                if (__ballot(raise)) {
-                    const float m_new = raise ? mx : m_run;
-                    const float alpha = (m_new == m_run) ? 1.f : exp2f(m_run - m_new);
+                    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+                    return fmaxf(mx, __shfl_xor(mx, 32, 64)) * C;
+                };
+                if (__ballot(m_run == -INFINITY)) {
+                    const float mx = colmax();
+                    if (m_run == -INFINITY) m_run = mx;
+                }
+                bf16x8 pf[2];
+                auto probs = [&](float mneg) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[i], C, mneg));
+                        const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[8 + i], C, mneg));
+                        s += e0 + e1;
+                        pf[0][i] = static_cast<__bf16>(e0);
+                        pf[1][i] = static_cast<__bf16>(e1);
+                    }
+                    return s;
+                };
+                float lsum = probs(m_run == -INFINITY ? 0.f : -m_run);
+                if (__ballot(!(lsum < 0x1p64f))) {
+                    const float mx = colmax();
+                    const float m_new = fmaxf(m_run, mx);
+                    const float alpha = (m_new == m_run || m_run == -INFINITY)
+                                            ? 1.f : exp2f(m_run - m_new);
                     l_run *= alpha;
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
                     m_run = m_new;
-                }
-                const float mneg = (m_run == -INFINITY) ? 0.f : -m_run;
-                float lsum = 0.f;
-                bf16x8 pf[2];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[i], C, mneg));
-                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[8 + i], C, mneg));
-                    lsum += e0 + e1;
-                    pf[0][i] = static_cast<__bf16>(e0);
-                    pf[1][i] = static_cast<__bf16>(e1);
+                    lsum = probs(m_run == -INFINITY ? 0.f : -m_run);
                 }
                 l_run += lsum;
 #pragma unroll
@@ -567,6 +607,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
                 }
             }
         }
+        // after the tile's math: the next tile into LDS (its loads have had
+        // two steps), then this register set's next loads
+        if (it + 1 < ntiles) stash(kr, vr, (it + 1) & 1);
+        if (it + LEAD < ntiles) issue(kr, vr, it + LEAD);
         if (it % kChunkTiles == kChunkTiles - 1 - LEAD && it >= 2 * kChunkTiles - 1 - LEAD) {
             const int c = (it + LEAD + 1) / kChunkTiles;
             const int cbase = kb + c * kChunkKeys;
@@ -968,6 +1012,7 @@ extern "C" int spec_verify_attention(int batch, int n, int hq, int hkv, int d, i
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
     if ((int64_t)max_pages * page_size < (int64_t)max_seq_len && max_seq_len > 0) return SPEC_ERR_SHAPE;
     if (batch == 0) return SPEC_OK;
+    if (num_slots == 0) return SPEC_ERR_SHAPE;   // the tree keys alone need slots
     if (!q || !k_pool || !v_pool || !seq_lens || !out_cache_loc || !tree_mask || !out)
         return SPEC_ERR_NULL;
     if (max_seq_len > 0 && !page_table) return SPEC_ERR_NULL;
