@@ -67,12 +67,23 @@ __device__ __forceinline__ void chunk_item(const GreedyArgs &A, int64_t t, uint6
     load_chunk<DT>(rowp, start, end, A.vec_ok, tid, x);
     float bv = -INFINITY;
     int bi = -1;
+    if (end - start == kChunk) {
+        // a whole chunk: the thread's maximum, then the first of its entries
+        // (they ascend in index with e) equal to it
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {       // e increases with element index
-        const int64_t idx = elem_index(start, tid, e);
-        if (idx < end && (bi < 0 || x[e] > bv)) {
-            bv = x[e];
-            bi = (int)idx;
+        for (int e = 0; e < kPerThread; ++e) bv = fmaxf(bv, x[e]);
+        int be = 0;
+#pragma unroll
+        for (int e = kPerThread - 1; e >= 0; --e) be = x[e] == bv ? e : be;
+        bi = (int)elem_index(start, tid, be);
+    } else {
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {   // e increases with element index
+            const int64_t idx = elem_index(start, tid, e);
+            if (idx < end && (bi < 0 || x[e] > bv)) {
+                bv = x[e];
+                bi = (int)idx;
+            }
         }
     }
     uint64_t key = arg_key(bv, bi);
