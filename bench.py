@@ -581,6 +581,16 @@ def run(args):
     attn_gbs = attn_bytes / t_attn / 1e9
     attn_tflops = attn_flops / t_attn / 1e12
     greedy_gbs = sweep_g / (op_ms["accept_greedy"] * 1e-3) / 1e9
+    # the sampled walk reads only the rows it visits: a request's root row and
+    # each accepted node's row (accept_length rows), target and draft
+    sample_fields = {}
+    if "sample" in cfg.accept:
+        visited = int(base.saccept_length.cpu().numpy().sum())
+        vbytes = visited * 2 * cfg.vocab * eb
+        sample_fields = {"accept_sample_visited_rows": visited,
+                         "accept_sample_visited_bytes": vbytes,
+                         "accept_sample_visited_gbs":
+                             vbytes / (op_ms["accept_sample"] * 1e-3) / 1e9}
     accept_op = "accept_greedy" if "greedy" in cfg.accept else "accept_sample"
     # the binding roof: matrix cores when the call's flops per algorithmic
     # byte exceed the ridge (peak flops / peak bandwidth), else HBM
@@ -631,6 +641,7 @@ def run(args):
         "verify_attn_tflops": attn_tflops,
         "verify_attn_frac_mfma": attn_tflops / BF16_PEAK_TFLOPS,
         "accept_greedy_sweep_gbs": greedy_gbs,
+        **sample_fields,
         "extra_op_ms": extra_ms,
         "accept_target_only_sweep_gbs": sweep_g / (extra_ms["accept_target_only"] * 1e-3) / 1e9,
         "draft_step_calls": cfg.num_steps,

@@ -5,6 +5,12 @@ Kernel trace (per-kernel launch count and average / min / max duration):
 
     python rocprof_summary.py <db or dir> [title] [command]
 
+Other counters of chosen kernels, averaged per dispatch, with the matrix
+cores' busy fraction:
+
+    python rocprof_summary.py --pmc --db <run> [--db <run>] --kernels a,b \
+        --title ... --command ...
+
 HBM byte counters (FETCH_SIZE / WRITE_SIZE, KiB per dispatch) of chosen
 kernels, scaled by what the same counter reads for a plain device copy of
 known size in the same run (the copy bench.py makes with
@@ -96,6 +102,35 @@ def counters_report(dbs, copy_bytes, kernels, source, title, commands):
     return "\n".join(out) + "\n"
 
 
+def pmc_report(dbs, kernels, title, commands, simds=1024, xcds=8):
+    """Per-kernel averages of every counter in the given runs, and for the
+    matrix-core counters the busy fraction: SQ_VALU_MFMA_BUSY_CYCLES over
+    (SIMDs x GRBM_GUI_ACTIVE / XCDs), GRBM_GUI_ACTIVE being summed over the
+    XCDs (MI355X: 256 CUs x 4 SIMDs, 8 XCDs)."""
+    agg = counter_table(dbs)
+    out = [f"# {title}", ""]
+    out += ["commands:", ""] + ["    " + c for c in commands] + [""]
+    out += ["| kernel | counter | dispatches | average per dispatch |", "|---|---|---|---|"]
+    per = {}
+    for (k, cname), vals in sorted(agg.items()):
+        if not any(k.startswith(p) for p in kernels):
+            continue
+        avg = sum(vals) / len(vals)
+        per.setdefault(k, {})[cname] = avg
+        out.append(f"| {k} | {cname} | {len(vals)} | {avg:.4g} |")
+    out.append("")
+    for k, c in sorted(per.items()):
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c and c["GRBM_GUI_ACTIVE"] > 0:
+            cyc = c["GRBM_GUI_ACTIVE"] / xcds
+            out.append(f"- {k}: {cyc:.4g} cycles per XCD; matrix cores busy "
+                       f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (simds * cyc):.3f} of the SIMD cycles")
+            if c.get("SQ_INSTS_MFMA"):
+                out.append(f"  ({c['SQ_VALU_MFMA_BUSY_CYCLES'] / c['SQ_INSTS_MFMA']:.1f} busy "
+                           f"cycles per MFMA instruction; {c.get('SQ_INSTS_VALU', 0) / c['SQ_INSTS_MFMA']:.2f}"
+                           " VALU instructions per MFMA)")
+    return "\n".join(out) + "\n"
+
+
 def read_traffic(path, source):
     """traffic_bytes_per_launch from a counters summary, or None when the
     summary is missing or was taken on another version of `source`."""
@@ -138,6 +173,15 @@ def main(argv):
         a = ap.parse_args(argv[1:])
         print(counters_report(a.db, a.copy_bytes, a.kernels.split(","), a.source, a.title,
                               a.command), end="")
+        return 0
+    if argv and argv[0] == "--pmc":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("--db", action="append", required=True)
+        ap.add_argument("--kernels", required=True)
+        ap.add_argument("--title", default="")
+        ap.add_argument("--command", action="append", default=[])
+        a = ap.parse_args(argv[1:])
+        print(pmc_report(a.db, a.kernels.split(","), a.title, a.command), end="")
         return 0
     print(summarize(argv[0], *(argv[1:3])), end="")
     return 0
