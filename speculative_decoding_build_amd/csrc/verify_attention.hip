@@ -693,6 +693,396 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA split kernel with K/V loaded straight into LDS (head dim 128,
+// page size 16, one wave per 32-row block)
+// ---------------------------------------------------------------------------
+//
+// The 8-wave form above without its register staging: each 64-key tile
+// travels from HBM into LDS by buffer loads whose destination is the LDS
+// (no registers, no ALU work, no LDS writes of the workgroup's own), with
+// four tiles in flight.  A tile buffer holds 64 rows of 256 bytes (K, and V
+// as it is stored); the 16-byte piece c of key k sits at piece c ^ swz(k),
+// so the 32 keys one K fragment read touches and the 4 keys x 32 bytes one
+// transposing V read touches fall on distinct banks.  V^T fragments come
+// from ds_read_b64_tr_b16, four keys of one dimension per lane and read.
+// Each wave loads 8 keys of a tile (two 1 KB runs of K, two of V) with
+// indexed loads (record = one slot's row of all KV heads, so no 64-bit
+// address per lane; a bad slot is an index past the records, which reads
+// zeros).  The 8 keys lie in one 16-slot page; the split's page ids are
+// copied into LDS before the loop, which then loads nothing but tiles.  Tile t sits in buffer t % 4, a static buffer per
+// unrolled step, so the compiler can tell one buffer's loads from another's
+// reads; the wait for tile t is explicit (this wave's vector-memory count,
+// then a barrier).  Scores, softmax and the PV product are the 8-wave form's.
+
+constexpr int kDmaTile = kTileKeys * 128 * 2;          // 16 KB: K (or V) of one tile
+constexpr int kDmaMaxPages = 2048;                     // page ids of a split held in LDS
+constexpr uint32_t kRsrcWord3 = 0x00020000u;           // raw buffer access, gfx9 format
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+// four tile buffers, each a K tile and a V tile (distinct arrays)
+__shared__ __attribute__((aligned(1024))) char dma_k0[kDmaTile];
+__shared__ __attribute__((aligned(1024))) char dma_k1[kDmaTile];
+__shared__ __attribute__((aligned(1024))) char dma_k2[kDmaTile];
+__shared__ __attribute__((aligned(1024))) char dma_k3[kDmaTile];
+__shared__ __attribute__((aligned(1024))) char dma_v0[kDmaTile];
+__shared__ __attribute__((aligned(1024))) char dma_v1[kDmaTile];
+__shared__ __attribute__((aligned(1024))) char dma_v2[kDmaTile];
+__shared__ __attribute__((aligned(1024))) char dma_v3[kDmaTile];
+
+template <int S>
+__device__ __forceinline__ char *dma_kbuf() {
+    if constexpr (S == 0) return dma_k0;
+    else if constexpr (S == 1) return dma_k1;
+    else if constexpr (S == 2) return dma_k2;
+    else return dma_k3;
+}
+
+template <int S>
+__device__ __forceinline__ char *dma_vbuf() {
+    if constexpr (S == 0) return dma_v0;
+    else if constexpr (S == 1) return dma_v1;
+    else if constexpr (S == 2) return dma_v2;
+    else return dma_v3;
+}
+
+// position of 16-byte piece c of key k in its row is c ^ piece_swz(k)
+__device__ __forceinline__ int piece_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
+
+// wait until at most n (8, 4 or 0) vector-memory operations of this wave are
+// in flight, then a workgroup barrier; memory accesses are not moved across
+// either
+__device__ __forceinline__ void wait_tiles_barrier(int n) {
+    if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+}
+
+template <int V> using ic = std::integral_constant<int, V>;
+
+__global__ __launch_bounds__(512, 1) void attn_dma_kernel(AttnParams P, int xcd_remap) {
+    constexpr int D = 128, NT = 512, DK = D / 16, DT = D / 32;
+    constexpr int kOpsPerTile = 4;        // loads per wave and tile: two K runs, two V runs
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int half = lane >> 5;
+    const int col = lane & 31;
+
+    int b, kvh, split, rg, nsp, kb, span;
+    int64_t slot_j;                        // split slot of the partials
+    if (P.dyn) {
+        const int total = P.slots * P.rowgroups * P.hkv;
+        int w = blockIdx.x;
+        if (xcd_remap) w = (w % 8) * (total / 8) + w / 8;
+        rg = w % P.rowgroups;
+        w /= P.rowgroups;
+        const int j = w % P.slots;
+        kvh = w / P.slots;
+        __shared__ int s_plan[4];
+        if (wave == 0) plan_split(P, j, blockIdx.x == 0, s_plan);
+        __syncthreads();
+        b = s_plan[0];
+        if (b < 0) return;                 // unused slot: no keys, no partials
+        split = s_plan[1];
+        nsp = s_plan[2];
+        const int t = s_plan[3];
+        const int tlo = (int)((int64_t)split * t / nsp), thi = (int)((int64_t)(split + 1) * t / nsp);
+        kb = tlo * kTileKeys;
+        span = (thi - tlo) * kTileKeys;
+        slot_j = j;
+    } else {
+        const Work wk = decode_work(P, blockIdx.x, xcd_remap != 0);
+        b = wk.b; kvh = wk.kvh; split = wk.split; rg = wk.rg;
+        nsp = P.nsplit;
+        kb = split * P.split_len;
+        span = P.split_len;
+        slot_j = (int64_t)b * P.nsplit + split;
+    }
+    // all of these are the workgroup's: kept in scalar registers, so the
+    // page-id loads below are scalar loads
+    b = __builtin_amdgcn_readfirstlane(b);
+    kvh = __builtin_amdgcn_readfirstlane(kvh);
+    split = __builtin_amdgcn_readfirstlane(split);
+    rg = __builtin_amdgcn_readfirstlane(rg);
+    nsp = __builtin_amdgcn_readfirstlane(nsp);
+    kb = __builtin_amdgcn_readfirstlane(kb);
+    span = __builtin_amdgcn_readfirstlane(span);
+    __shared__ int32_t s_tree[kMaxTreeNodes];
+    __shared__ int32_t s_pages[kDmaMaxPages];
+    int pre_tree = -1;
+    if (tid < P.n) pre_tree = P.out_cache_loc[(int64_t)b * P.n + tid];
+    const int L = P.seq_lens[b];
+    int err = 0;
+    if (L < 0 || L > P.max_seq_len) {
+        if (tid == 0 && split == 0 && rg == 0) spec::raise_status(P.status, SPEC_ST_RANGE);
+        mark_empty_split(P, b, kvh, split, rg);
+        return;
+    }
+    const int ke = min(L + P.n, kb + span);
+    if (kb >= ke) {
+        mark_empty_split(P, b, kvh, split, rg);
+        return;
+    }
+    const int ntiles = (ke - kb + kTileKeys - 1) / kTileKeys;
+    if (tid < P.n) s_tree[tid] = pre_tree;
+    // the split's page-table entries into LDS (history keys kb .. min(L, ke)
+    // - 1; the host plans splits of at most kDmaMaxPages pages), so the loop
+    // makes no other memory loads than the tiles'
+    {
+        const int hist_end = min(L, ke);
+        const int npg = hist_end > kb ? (hist_end - kb + 15) / 16 : 0;
+        if (npg > kDmaMaxPages) {
+            if (tid == 0) spec::raise_status(P.status, SPEC_ST_RANGE);
+            mark_empty_split(P, b, kvh, split, rg);
+            return;
+        }
+        for (int i = tid; i < npg; i += NT)
+            s_pages[i] = P.page_table[(int64_t)b * P.max_pages + kb / 16 + i];
+    }
+
+    // ---- query fragments (B operand of S^T = K Q^T) ------------------------
+    const int rho = rg * P.rows_per_group + wave * 32 + col;
+    const bool wave_active = rg * P.rows_per_group + wave * 32 < P.rows;
+    bf16x8 qf[DK];
+    uint64_t mword = 0;
+    if (rho < P.rows) {
+        const int node = rho / P.group;
+        const int h = kvh * P.group + rho % P.group;
+        const __bf16 *qp = static_cast<const __bf16 *>(P.q) +
+                           (((int64_t)b * P.n + node) * P.hq + h) * D + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8 *>(qp + kk * 16);
+        mword = load_mask_word(P.mask + ((int64_t)b * P.n + node) * P.word_bytes, P.word_bytes);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) qf[kk] = bf16x8{};
+    }
+
+    // ---- loads: this lane's two keys of a tile are kl0 and kl0 + 4 ----------
+    const int kl0 = 8 * wave + (lane >> 4);
+    uint32_t voff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int piece = (lane & 15) ^ piece_swz(kl0 + 4 * j);
+        voff[j] = (uint32_t)((kvh * D + piece * 8) * 2);
+    }
+    const int stride = P.hkv * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(P.k_pool), (short)stride, (int)P.num_slots, (int)kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(P.v_pool), (short)stride, (int)P.num_slots, (int)kRsrcWord3);
+    // page id of this wave's 8 keys of tile t (-1 when its first key is not
+    // a history key), from the LDS copy of the split's page-table entries
+    auto wave_page = [&](int t) -> int {
+        const int p = kb + t * kTileKeys + 8 * wave_u;
+        if (t >= ntiles || p >= L) return -1;
+        return s_pages[(p - kb) / 16];
+    };
+    auto dma_tile = [&](char *kdst, char *vdst, int t, int page) {
+        uint32_t idx[2];
+        const int tb = kb + t * kTileKeys;
+        if (tb + kTileKeys <= min(L, ke)) {
+            // a tile of history keys only: the wave's page (uniform), then
+            // the lane's slot within it
+            page = __builtin_amdgcn_readfirstlane(page);
+            const bool ok = page >= 0 && (int64_t)page * 16 + 16 <= P.num_slots;
+            if (!ok) err |= SPEC_ST_RANGE;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                idx[j] = ok ? (uint32_t)(page * 16 + ((kl0 + 4 * j) & 15)) : 0xFFFFFFFFu;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int p = tb + kl0 + 4 * j;
+                int64_t slot = -1;
+                if (p < L) slot = page < 0 ? -1 : (int64_t)page * 16 + (p & 15);
+                else if (p < ke) slot = s_tree[p - L];
+                const bool ok = slot >= 0 && slot < P.num_slots;
+                if (!ok && p < ke) err |= SPEC_ST_RANGE;
+                idx[j] = ok ? (uint32_t)slot : 0xFFFFFFFFu;
+            }
+        }
+        char *kd = kdst + wave * 2048;
+        char *vd = vdst + wave * 2048;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_struct_ptr_buffer_load_lds(rk, (lds_void_t *)(kd + j * 1024), 16,
+                                                        idx[j], voff[j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_struct_ptr_buffer_load_lds(rv, (lds_void_t *)(vd + j * 1024), 16,
+                                                        idx[j], voff[j], 0, 0, 0);
+    };
+
+    // ---- LDS read addresses (bytes from a tile buffer) ---------------------
+    uint32_t kaddr[DK];
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+        kaddr[kk] = (uint32_t)(col * 256 + (((2 * kk + half) ^ piece_swz(col)) * 16));
+    uint32_t vaddr[DT][2];
+    {
+        const int g = lane >> 4, r = lane & 15, m = r >> 2, i = r & 3;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int key = 4 * (g >> 1) + 8 * e + m;
+                const int pc = (4 * dt + 2 * (g & 1) + (i >> 1)) ^ piece_swz(key);
+                vaddr[dt][e] = (uint32_t)(key * 256 + pc * 16 + (i & 1) * 8);
+            }
+    }
+
+    floatx16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = floatx16{};
+    float m_run = -INFINITY;   // running max, log2 domain (already times C)
+    float l_run = 0.f;         // this lane-half's share of the softmax sum
+    const float C = P.scale_log2;
+
+    // ---- prologue: tiles 0..2 loading ---------------------------------------
+    __syncthreads();                       // s_tree
+    if (0 < ntiles) dma_tile(dma_k0, dma_v0, 0, wave_page(0));
+    if (1 < ntiles) dma_tile(dma_k1, dma_v1, 1, wave_page(1));
+    if (2 < ntiles) dma_tile(dma_k2, dma_v2, 2, wave_page(2));
+
+    auto step = [&](auto stage, int it) {
+        constexpr int S = decltype(stage)::value;
+        constexpr int SN = (S + 3) & 3;    // buffer of tile it + 3 (tile it - 1's)
+        // tile it has landed once at most the loads of tiles it+1, it+2 are
+        // in flight; the barrier also ends every wave's use of tile it-1
+        wait_tiles_barrier(kOpsPerTile * min(2, ntiles - 1 - it));
+        if (it + 3 < ntiles) dma_tile(dma_kbuf<SN>(), dma_vbuf<SN>(), it + 3, wave_page(it + 3));
+        if (!wave_active) return;
+        const char *kt = dma_kbuf<S>();
+        const char *vt = dma_vbuf<S>();
+        const int tile_base = kb + it * kTileKeys;
+        const bool edge = (tile_base + kTileKeys > ke) || (tile_base + kTileKeys > L);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            floatx16 sacc = floatx16{};
+#pragma unroll
+            for (int kk = 0; kk < DK; ++kk) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kt + sub * 8192 + kaddr[kk]);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc, 0, 0, 0);
+            }
+            // lane holds keys sub*32 + 8*(i/4) + 4*half + i%4 of query col
+            float sv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
+            if (edge) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int p = tile_base + sub * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                    const int rel = p - L;
+                    const uint32_t sh = (uint32_t)max(rel, 0) & 63u;
+                    const bool bit = ((mword >> sh) & 1ull) != 0;
+                    const bool vis = (p < ke) & ((rel < 0) | bit);
+                    sv[i] = vis ? sv[i] : -INFINITY;
+                }
+            }
+            // probabilities at the running max (set here by a column's
+            // first sub-block with a visible key; raised only when some
+            // probability reaches 2^64)
+            auto colmax = [&]() {
+                float mx = sv[0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+                return fmaxf(mx, __shfl_xor(mx, 32, 64)) * C;
+            };
+            if (__ballot(m_run == -INFINITY)) {
+                const float mx = colmax();
+                if (m_run == -INFINITY) m_run = mx;
+            }
+            bf16x8 pf[2];
+            auto probs = [&](float mneg) {
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[i], C, mneg));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[8 + i], C, mneg));
+                    s += e0 + e1;
+                    pf[0][i] = static_cast<__bf16>(e0);
+                    pf[1][i] = static_cast<__bf16>(e1);
+                }
+                return s;
+            };
+            float lsum = probs(m_run == -INFINITY ? 0.f : -m_run);
+            if (__ballot(!(lsum < 0x1p64f))) {
+                const float mx = colmax();
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = (m_new == m_run || m_run == -INFINITY)
+                                        ? 1.f : exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+                m_run = m_new;
+                lsum = probs(m_run == -INFINITY ? 0.f : -m_run);
+            }
+            l_run += lsum;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    // V^T rows dt*32 .. +31, keys sub*32 + 16*st + 4*half +
+                    // {0..3, 8..11}: two transposing reads
+                    const char *vb = vt + sub * 8192 + st * 4096;
+                    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_short4v *)(vb + vaddr[dt][0]));
+                    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_short4v *)(vb + vaddr[dt][1]));
+                    const short4v v8[2] = {lo, hi};
+                    const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], oacc[dt],
+                                                                       0, 0, 0);
+                }
+            }
+        }
+    };
+    for (int it = 0; it < ntiles; it += 4) {
+        step(ic<0>{}, it);
+        if (it + 1 < ntiles) step(ic<1>{}, it + 1);
+        if (it + 2 < ntiles) step(ic<2>{}, it + 2);
+        if (it + 3 < ntiles) step(ic<3>{}, it + 3);
+    }
+
+    // ---- epilogue -------------------------------------------------------------
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (rho < P.rows) {
+        const int node = rho / P.group;
+        const int h = kvh * P.group + rho % P.group;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        __bf16 *op;
+        if (nsp == 1) {
+            op = static_cast<__bf16 *>(P.out) + (((int64_t)b * P.n + node) * P.hq + h) * D;
+        } else {
+            const int64_t pidx = (slot_j * P.hkv + kvh) * P.rows + rho;
+            op = static_cast<__bf16 *>(P.part_o) + pidx * D;
+            if (half == 0) P.part_ml[pidx] = make_float2(m_run, l_tot);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                uint32_t hv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    hv[j] = __builtin_bit_cast(uint16_t,
+                                               static_cast<__bf16>(oacc[dt][4 * j4 + j] * inv));
+                *reinterpret_cast<uint2 *>(op + dt * 32 + 8 * j4 + 4 * half) =
+                    make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+            }
+    }
+    for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, 64);
+    if (lane == 0) spec::raise_status(P.status, err);
+}
+
+// ---------------------------------------------------------------------------
 // f32 split kernel (vector ALUs): one wavefront per query row at a time
 // ---------------------------------------------------------------------------
 
@@ -900,6 +1290,7 @@ struct Plan {
     int rows_per_group, rowgroups;
     int split_len, nsplit;  // static plan: every request cut at max_seq_len's splits
     int dyn, slots;         // length-balanced plan over `slots` split slots (bf16, batch > 1)
+    int max_span_tiles;     // an upper bound of any split's tiles
 };
 
 Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
@@ -950,6 +1341,16 @@ Plan make_plan(int batch, int n, int hq, int hkv, int max_seq_len, int dtype) {
             pl.slots = S;
         }
     }
+    // Longest split: the static plan's split_len; for the length-balanced
+    // plan, request b's s_b is t_b / 4 (splits of at most 7 tiles), 64
+    // (t_b / 64 tiles) or 1 + floor((S - batch) t_b / T) >= (S - batch) t_b
+    // / T (at most T / (S - batch) <= batch t_max / (S - batch) tiles, plus
+    // one for rounding).
+    pl.max_span_tiles = tiles_per;
+    if (pl.dyn)
+        pl.max_span_tiles = std::max({7, (tiles + kMaxSplits - 1) / kMaxSplits,
+                                      (int)(((int64_t)batch * tiles + (pl.slots - batch) - 1) /
+                                            (pl.slots - batch)) + 1});
     // A grid of 4-wave workgroups that fits one workgroup per CU leaves
     // every SIMD one wave: give each 32-row block two waves instead, each
     // taking one 32-key half of every tile.
@@ -976,10 +1377,23 @@ size_t workspace_bytes_for(const Plan &pl, int batch, int n, int hq, int hkv, in
     return o_plan + (pl.dyn ? spec::align_up((size_t)batch * sizeof(int2), 256) : 0);
 }
 
+// The LDS-load form serves 8-wave workgroups of one wave per 32-row block
+// at head dim 128 and page size 16, when a slot's row of all KV heads fits
+// a buffer record (stride below 2^14 bytes), the pool fits 32-bit buffer
+// offsets and no split spans more pages than the kernel holds in LDS.
+bool dma_form(const Plan &pl, const AttnParams &P, int d) {
+    const int64_t stride = (int64_t)P.hkv * d * 2;
+    return d == 128 && pl.nw == 8 && pl.kh == 1 && P.page_size == 16 && stride < (1 << 14) &&
+           P.num_slots * stride < (int64_t(1) << 32) &&
+           (int64_t)pl.max_span_tiles * (kTileKeys / 16) <= kDmaMaxPages;
+}
+
 template <int D>
 void launch_mfma(const Plan &pl, const AttnParams &P, unsigned groups, hipStream_t st) {
     const int remap = groups % 8 == 0 ? 1 : 0;
-    if (pl.kh == 2)
+    if (D == 128 && dma_form(pl, P, D))
+        hipLaunchKernelGGL(attn_dma_kernel, dim3(groups), dim3(512), 0, st, P, remap);
+    else if (pl.kh == 2)
         hipLaunchKernelGGL((attn_split_mfma_kernel<D, 8, 2>), dim3(groups), dim3(512), 0, st, P, remap);
     else if (pl.nw == 4)
         hipLaunchKernelGGL((attn_split_mfma_kernel<D, 4, 1>), dim3(groups), dim3(256), 0, st, P, remap);

@@ -339,6 +339,43 @@ LONG_SPLIT_CASES = {
 }
 
 
+# Shapes of the LDS-load form (8-wave workgroups, one wave per 32-row block,
+# page size 16): the length-balanced plan over ragged lengths (history ends
+# inside a page and inside a wave's 8 keys; tree keys share its page), and
+# the static plan of one request.  Every output vector is compared.
+DMA_CASES = {
+    "b4_Lu_ragged": W.shrink(W.CONFIGS[5], batch=4, hist=("uniform", 9001, 17003), vocab=1000),
+    "b1_L50005": W.shrink(W.CONFIGS[5], batch=1, hist=("fixed", 50005), vocab=1000),
+    "b3_L8195": W.shrink(W.CONFIGS[5], batch=3, hist=("fixed", 8195), vocab=1000),
+}
+
+
+@pytest.mark.parametrize("name", list(DMA_CASES))
+def test_verify_attention_lds_load_form(name):
+    cfg = DMA_CASES[name]
+    w = W.make_workload(cfg, 29)
+    t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                          cfg.num_steps, cfg.num_draft_tokens)
+    b, n, hq, hkv = cfg.batch, cfg.num_draft_tokens, cfg.num_q_heads, cfg.num_kv_heads
+    G_ = hq // hkv
+    say(f"[attention, LDS-load form] {name} b={b} L={w.seq_lens.tolist()}")
+    words = oracle.pack_mask(t["mask"], oracle.MASK_QLEN_BITS)
+    got, st = G.verify_attention(w, words)
+    assert st == 0
+    assert np.isfinite(got).all()
+    err = 0.0
+    for r in range(b):
+        for g in range(hkv):
+            ref = oracle.verify_attention_unit(w.q, w.k_pool[0], w.v_pool[0], w.page_table,
+                                               w.seq_lens, w.out_cache_loc, t["mask"], hq, hkv,
+                                               cfg.page_size, cfg.dtype, r, g)
+            mine = got[r * n:(r + 1) * n, g * G_:(g + 1) * G_]
+            err = max(err, _attn_err(mine.reshape(-1, mine.shape[-1]),
+                                     ref.reshape(-1, ref.shape[-1])))
+    say(f"    max rel err {err:.3e} over {b * hkv * n * G_} vectors")
+    assert err <= ATTN_TOL[cfg.dtype]
+
+
 @pytest.mark.parametrize("name", list(LONG_SPLIT_CASES))
 def test_verify_attention_long_splits_sampled(name):
     cfg = LONG_SPLIT_CASES[name]
