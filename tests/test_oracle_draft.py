@@ -114,3 +114,51 @@ def test_reproduces_the_generators_draft_loop(cid):
     np.testing.assert_array_equal(tokens, w.tokens)
     np.testing.assert_array_equal(parents, w.parents)
     np.testing.assert_allclose(scores, w.scores, rtol=2e-6)
+
+
+def _probs_f32(logits_row):
+    """softmax of one row in float64, rounded to float32 (written out here)."""
+    x = np.asarray(logits_row, np.float64)
+    e = np.exp(x - x.max())
+    return (e / e.sum()).astype(np.float32)
+
+
+@pytest.mark.parametrize("topk,V,seed", [(4, 50, 1), (8, 200, 2), (2, 9, 3), (1, 30, 4)])
+def test_next_branches_equal_brute_force_global_ranking(topk, V, seed):
+    """The two-stage selection (each branch's top-k, then the top-k of the
+    topk^2 products) must equal ranking every (branch, token) product of the
+    whole vocabulary at once: a branch's (topk+1)-th token is beaten by its
+    own topk better ones, so no global top-k entry is lost in stage one.
+    Inputs are continuous random values (no ties)."""
+    rng = np.random.default_rng(seed)
+    steps = 3
+    # step 0: the root distribution's top-k by a full sort
+    root = rng.normal(0, 2, (1, 1, V)).astype(np.float32)
+    o0 = oracle.draft_step(root, None, 0, topk, steps, "f32")
+    p0 = _probs_f32(root[0, 0])
+    order = sorted(range(V), key=lambda v: (-float(p0[v]), v))[:topk]
+    assert o0["next_tokens"][0].tolist() == order
+    np.testing.assert_array_equal(o0["next_scores"][0], p0[order])
+    # later steps: every (branch, token) product ranked at once
+    bs = o0["next_scores"]
+    for step in (1, 2):
+        logits = rng.normal(0, 2, (1, topk, V)).astype(np.float32)
+        o = oracle.draft_step(logits, bs, step, topk, steps, "f32")
+        probs = [_probs_f32(logits[0, j]) for j in range(topk)]
+        prods = [(float(np.float32(bs[0, j] * probs[j][v])), j, v)
+                 for j in range(topk) for v in range(V)]
+        prods.sort(key=lambda e: (-e[0], e[1], e[2]))
+        top = prods[:topk]
+        assert len({e[0] for e in prods[:topk + 1]}) == topk + 1   # no ties at the cut
+        assert o["next_tokens"][0].tolist() == [v for _, _, v in top]
+        np.testing.assert_array_equal(o["next_scores"][0],
+                                      np.array([s for s, _, _ in top], np.float32))
+        # parents: flat index j*topk + (rank of v in branch j's top-k), offset
+        # by topk^2 (step - 1) + topk
+        par = []
+        for _, j, v in top:
+            rank = sorted(range(V), key=lambda u: (-float(probs[j][u]), u)).index(v)
+            assert rank < topk
+            par.append(j * topk + rank + topk * topk * (step - 1) + topk)
+        assert o["parents"][0].tolist() == par
+        bs = o["next_scores"]
