@@ -460,3 +460,36 @@ def test_full_attention_vector_complete(cid):
             say(f"    request {r} done, max rel err so far {err:.3e}")
     say(f"    max rel err {err:.3e} over {len(units) * n * G_} vectors")
     assert err <= ATTN_TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("lds_load_form", DMA_CASES["b3_L8195"]),
+    ("register_staged", W.shrink(W.CONFIGS[3], batch=3, hist=("fixed", 2000), vocab=1000)),
+])
+def test_verify_attention_bad_slots(name, cfg):
+    """Page ids and tree slots out of range in requests 1 and 2: the call
+    raises SPEC_ST_RANGE, every kernel ends, and request 0 (untouched) is
+    still exact."""
+    w = W.make_workload(cfg, 31)
+    t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                          cfg.num_steps, cfg.num_draft_tokens)
+    b, n, hq, hkv = cfg.batch, cfg.num_draft_tokens, cfg.num_q_heads, cfg.num_kv_heads
+    say(f"[attention, bad slots] {name} b={b} L={w.seq_lens.tolist()}")
+    nslots = w.k_pool.shape[1]
+    w.page_table[1, 5] = -1
+    w.page_table[2, 10] = nslots // cfg.page_size + 100
+    w.out_cache_loc[2 * n + 3] = nslots + 7
+    words = oracle.pack_mask(t["mask"], oracle.MASK_QLEN_BITS)
+    got, st = G.verify_attention(w, words)
+    say(f"    status {st}")
+    assert st & S.SPEC_ST_RANGE
+    G_ = hq // hkv
+    err = 0.0
+    for g in range(hkv):
+        ref = oracle.verify_attention_unit(w.q, w.k_pool[0], w.v_pool[0], w.page_table,
+                                           w.seq_lens, w.out_cache_loc, t["mask"], hq, hkv,
+                                           cfg.page_size, cfg.dtype, 0, g)
+        mine = got[0:n, g * G_:(g + 1) * G_]
+        err = max(err, _attn_err(mine.reshape(-1, mine.shape[-1]), ref.reshape(-1, ref.shape[-1])))
+    say(f"    request 0: max rel err {err:.3e}")
+    assert err <= ATTN_TOL[cfg.dtype]
