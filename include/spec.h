@@ -34,14 +34,15 @@
  *     recorded call may later run beside other streams' kernels, and a graph
  *     does not keep a cooperative launch's co-residency guarantee, so the
  *     accepts record forms whose outputs never depend on other workgroups
- *     being scheduled: the greedy and target-only tree walks run as a kernel
- *     of their own after the vocabulary sweep; the sampled walk runs its
+ *     being scheduled: the greedy accept always runs its tree walk as a
+ *     kernel of its own after the vocabulary sweep (it never waits), and
+ *     so does the recorded target-only accept; the sampled walk runs its
  *     co-resident form as an ordinary kernel followed by a recovery kernel
  *     that walks again, one workgroup per request, every request whose
  *     wait gave up.  Recorded calls therefore never raise SPEC_ST_SYNC.
  *     Eager calls use the one-launch forms: a cooperative launch (sampled),
  *     or walkers fewer than the device holds at once that wait only on
- *     sweep work (greedy, target-only).
+ *     sweep work (target-only).
  *   - Waits between workgroups are bounded: after SPEC_POLL_LIMIT polls of
  *     one slot (environment variable read on every call, decimal, default
  *     1048576, about a second) a wait gives up; in an eager call it raises
@@ -205,12 +206,13 @@ int spec_verify_attention(int batch, int num_draft_tokens, int num_q_heads, int 
  *   accept_length [batch] i32    accepted drafts + 1
  *   target_predict [batch*n] i32 (optional, NULL to skip) every row's choice
  * A path that would exceed accept_width raises SPEC_ST_DEPTH and stops there.
+ * Two launches (the vocabulary sweep folds each chunk's best entry into its
+ * row's key with an atomic max; the walk reads the keys); no workgroup
+ * waits for another, so the call never raises SPEC_ST_SYNC.
  * workspace: spec_accept_workspace_size(batch, n, vocab, 0) bytes (a 64-bit
- *   key per verify row and 8192-entry chunk), 8-byte
- *   aligned and zero-filled before its first use; every call leaves it
- *   zero-filled again, so one workspace serves any number of calls in stream
- *   order (concurrent calls need one each).  After a call that raised
- *   SPEC_ST_SYNC, zero it again before the next call.
+ *   key per verify row), 8-byte aligned and zero-filled before its first
+ *   use; every call leaves it zero-filled again, so one workspace serves any
+ *   number of calls in stream order (concurrent calls need one each).
  * Logits must not be NaN.
  */
 size_t spec_accept_workspace_size(int batch, int num_draft_tokens, int64_t vocab, int sampled);
@@ -226,12 +228,12 @@ int spec_accept_greedy(int batch, int num_draft_tokens, int accept_width, int64_
  * spec_accept_greedy without a workspace, for callers that cannot allocate
  * device memory: code under graph capture, tight serving loops, harnesses
  * that forbid allocation.  Arguments, outputs and errors as
- * spec_accept_greedy.  The chunk keys live in a fixed array inside the
- * library (1 MiB on each device the library runs on, held until the
- * process ends): a call needs batch * n * ceil(vocab / 8192) <= 131072
- * keys, else SPEC_ERR_WORKSPACE (e.g. up to 128 requests of 64 nodes at
- * vocabulary 128256).  Each call first clears the keys it uses (a kernel on
- * `stream`, no memset), then runs the accept.  Every call on one device
+ * spec_accept_greedy.  The row keys live in a fixed array inside the
+ * library (256 KiB on each device the library runs on, held until the
+ * process ends): a call needs batch * n <= 32768 keys, else
+ * SPEC_ERR_WORKSPACE (e.g. up to 512 requests of 64 nodes).  Each call
+ * first clears the keys it uses (a kernel on `stream`, no memset), then
+ * runs the accept.  Every call on one device
  * shares that device's array: calls that may overlap on one device
  * (different streams, or host threads without ordering) race.  The first
  * call on a device looks the array's address up with that device current

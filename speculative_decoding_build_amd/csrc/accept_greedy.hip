@@ -5,21 +5,17 @@
 // 行到最终输出路径" (三: accept_index holds verify rows; the last row's target
 // choice is the terminal token).
 //
-// Work item t (verify row t / nchunks, 8192-entry chunk t % nchunks) is
-// workgroup t of the grid: the chunk is loaded once with 16-byte loads and
-// its best entry is written, as one 64-bit key, to write-once slot t.  A slot
-// is 0 until written (a key is never 0), so the walker that reads a
-// request's slots needs no fence: it polls until all are non-zero, then
-// clears them for the next call (the workspace is zero after every call).
-//
-// One launch when the requests' walkers fit on the device at once: the last
-// `batch` workgroups of the grid walk a request each after their own chunk.
-// A walker waits only for chunk work, which never waits, and fewer walkers
-// than the device holds at once always leave room for the chunk workgroups
-// still to run, in whatever order they are dispatched.  Otherwise, and
-// whenever the call is recorded into a graph (where other streams' kernels
-// may hold the device), a second launch walks: its polls find every slot
-// written.
+// Two launches, neither of which waits for another workgroup:
+// * the sweep: workgroup t loads 8192-entry chunk t % nchunks of verify row
+//   t / nchunks once (16-byte loads), finds its best entry and folds it, as
+//   one 64-bit key, into the row's key with an atomic max (no return, so the
+//   workgroup ends at once);
+// * the walk: one workgroup per request reads its rows' keys (every atomic
+//   of the sweep is complete at the kernel boundary), clears them for the
+//   next call (the workspace is zero after every call), finds every node's
+//   matching child in parallel and follows them from the root.
+// Nothing depends on which workgroups are resident, so the same two
+// launches run eagerly and recorded into a graph.
 #include <algorithm>
 #include <mutex>
 
@@ -51,13 +47,15 @@ struct GreedyArgs {
     int batch, n, s1, nchunks;
     const int32_t *cand, *r_index, *r_next, *r_sib;
     int32_t *predict, *accept_index, *accept_length, *target_predict, *status;
-    uint64_t *slots;     // [batch * n][nchunks] chunk keys, written once per call
-    unsigned poll_limit; // polls of one slot before giving up
+    uint64_t *keys;      // [batch * n] row keys: 0 on entry, the row's best after the sweep
 };
 
-// The best entry of chunk t % nchunks of verify row t / nchunks into slot t.
+// Sweep: the best entry of chunk t % nchunks of verify row t / nchunks,
+// folded into the row's key.
 template <int DT>
-__device__ __forceinline__ void chunk_item(const GreedyArgs &A, int64_t t, uint64_t *s_wave) {
+__global__ __launch_bounds__(kSweepThreads) void greedy_sweep_kernel(GreedyArgs A) {
+    __shared__ uint64_t s_wave[kSweepThreads / SPEC_WAVE];
+    const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t row = t / A.nchunks;
     const int64_t start = (t % A.nchunks) * kChunk;
@@ -97,91 +95,74 @@ __device__ __forceinline__ void chunk_item(const GreedyArgs &A, int64_t t, uint6
     if (tid == 0) {
 #pragma unroll
         for (int w = 1; w < kSweepThreads / SPEC_WAVE; ++w) key = s_wave[w] > key ? s_wave[w] : key;
-        __hip_atomic_store(A.slots + t, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max(A.keys + row, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-// Request b: collect its rows' keys from the slots (polling, bounded), clear
-// the slots, walk from the root and write the outputs.
-__device__ void walk_request(const GreedyArgs &A, int b) {
-    __shared__ uint64_t s_key[kMaxNodes];
+// Walk: request blockIdx.x.  Its tree and its rows' keys are loaded
+// together; the keys are cleared; every node's thread scans its own child
+// list for the child holding its row's choice; one thread then follows those
+// children from the root and the outputs are written.
+__global__ __launch_bounds__(kSweepThreads) void greedy_walk_kernel(GreedyArgs A) {
     __shared__ int s_tp[kMaxNodes], s_row[kMaxNodes], s_pred[kMaxNodes];
-    __shared__ int s_cand[kMaxNodes], s_next[kMaxNodes], s_sib[kMaxNodes];
+    __shared__ int s_cand[kMaxNodes], s_sib[kMaxNodes], s_hit[kMaxNodes], s_bad[kMaxNodes];
     __shared__ int s_ai[kMaxNodes + 1];
     __shared__ int s_len, s_err;
+    const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int n = A.n;
     const int base = b * n;
-    if (tid < n) s_key[tid] = 0;
     if (tid == 0) s_err = 0;
-    __syncthreads();
-    // loads of up to four slots per thread go out together, then any empty
-    // one is polled; one timed-out slot ends every poll of the walker
-    const int nslots = n * A.nchunks;
-    uint64_t *rs = A.slots + (int64_t)base * A.nchunks;
-    for (int j0 = tid; j0 < nslots; j0 += 4 * kSweepThreads) {
-        uint64_t k4[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = j0 + u * kSweepThreads;
-            k4[u] = j < nslots ? __hip_atomic_load(rs + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = j0 + u * kSweepThreads;
-            if (j >= nslots) continue;
-            uint64_t k = k4[u];
-            for (unsigned spins = 0; k == 0; ++spins) {
-                if (spins >= A.poll_limit || (__hip_atomic_load(&s_err, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_WORKGROUP) &
-                                            SPEC_ST_SYNC)) {
-                    atomicOr(&s_err, SPEC_ST_SYNC);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-                k = __hip_atomic_load(rs + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            atomicMax(reinterpret_cast<unsigned long long *>(&s_key[j / A.nchunks]),
-                      (unsigned long long)k);
-        }
-    }
-    __syncthreads();
-    // every slot of the request has been read: clear them for the next call
-    for (int j = tid; j < nslots; j += blockDim.x)
-        __hip_atomic_store(rs + j, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int err = 0;
     if (tid < n) {
         int row = A.r_index[base + tid];
+        const int next = A.r_next[base + tid];
         s_cand[tid] = A.cand[base + tid];
-        s_next[tid] = A.r_next[base + tid];
         s_sib[tid] = A.r_sib[base + tid];
+        const uint64_t key = A.keys[base + tid];      // row base + tid's key
+        A.keys[base + tid] = 0;
+        s_tp[tid] = arg_key_index(key);               // indexed by row here
         if (row < base || row >= base + n) { err |= SPEC_ST_RANGE; row = -1; }
-        s_tp[tid] = row >= 0 ? arg_key_index(s_key[row - base]) : -1;
         s_row[tid] = row;
         s_pred[tid] = 0;
+        s_hit[tid] = next;                            // the first child, for now
+    }
+    __syncthreads();
+    // node tid's choice (its row's key) and first child in sibling order
+    // holding it
+    int want = -1, hit = -1, bad = 0;
+    if (tid < n) {
+        want = s_row[tid] >= 0 ? s_tp[s_row[tid] - base] : -1;
+        int c = s_hit[tid];
+        for (int steps = 0; c != -1 && steps < n; ++steps) {
+            if (c < 0 || c >= n) { bad = SPEC_ST_RANGE; break; }
+            if (s_cand[c] == want) { hit = c; break; }
+            c = s_sib[c];
+        }
+    }
+    __syncthreads();
+    if (tid < n) {
+        s_tp[tid] = want;                             // indexed by node from here on
+        s_hit[tid] = hit;
+        s_bad[tid] = bad;
     }
     __syncthreads();
     if (tid == 0) {
-        int cur = 0, cnt = 0;
+        int cur = 0, cnt = 0, werr = 0;
         s_ai[0] = s_row[0];
         for (int guard = 0; guard < n; ++guard) {
-            const int want = s_tp[cur];
-            int c = s_next[cur];
-            int hit = -1;
-            for (int steps = 0; c != -1 && steps < n; ++steps) {
-                if (c < 0 || c >= n) { err |= SPEC_ST_RANGE; break; }
-                if (s_cand[c] == want) { hit = c; break; }
-                c = s_sib[c];
-            }
-            if (hit < 0) break;
-            if (cnt + 1 >= A.s1) { err |= SPEC_ST_DEPTH; break; }
-            s_pred[cur] = s_cand[hit];
+            werr |= s_bad[cur];
+            const int h = s_hit[cur];
+            if (h < 0) break;
+            if (cnt + 1 >= A.s1) { werr |= SPEC_ST_DEPTH; break; }
+            s_pred[cur] = s_cand[h];
             ++cnt;
-            s_ai[cnt] = s_row[hit];
-            cur = hit;
+            s_ai[cnt] = s_row[h];
+            cur = h;
         }
         s_pred[cur] = s_tp[cur];
         s_len = cnt + 1;
+        err |= werr;
     }
     __syncthreads();
     if (tid < n && s_row[tid] >= 0) {
@@ -196,35 +177,11 @@ __device__ void walk_request(const GreedyArgs &A, int b) {
     if (tid == 0) raise_status(A.status, s_err);
 }
 
-// Chunk work for every (row, chunk); with WALK the last `batch` workgroups
-// then walk a request each.
-template <int DT, bool WALK>
-__global__ __launch_bounds__(kSweepThreads) void greedy_kernel(GreedyArgs A) {
-    __shared__ uint64_t s_wave[kSweepThreads / SPEC_WAVE];
-    const int64_t t = blockIdx.x;
-    chunk_item<DT>(A, t, s_wave);
-    if constexpr (WALK) {
-        const int64_t first_walker = (int64_t)gridDim.x - A.batch;
-        if (t >= first_walker) walk_request(A, (int)(t - first_walker));
-    }
-}
-
-// Second launch when the walkers cannot all be resident with the chunk work.
-__global__ __launch_bounds__(kSweepThreads) void greedy_walk_kernel(GreedyArgs A) {
-    walk_request(A, blockIdx.x);
-}
-
-// Workgroups of the fused kernel the device holds at once (0 if unknown).
-template <int DT>
-int fused_capacity() {
-    return spec::resident_capacity(reinterpret_cast<const void *>(greedy_kernel<DT, true>),
-                                   kSweepThreads);
-}
-
 }  // namespace
 
 size_t spec_greedy_workspace_bytes(int batch, int n, int64_t vocab) {
-    return spec::align_up((size_t)batch * n * num_chunks(vocab) * sizeof(uint64_t), 256);
+    (void)vocab;
+    return spec::align_up((size_t)batch * n * sizeof(uint64_t), 256);
 }
 
 int spec_check_accept_args(int batch, int n, int s1, int64_t vocab, int dtype) {
@@ -237,13 +194,13 @@ int spec_check_accept_args(int batch, int n, int s1, int64_t vocab, int dtype) {
 
 namespace {
 
-// Validated launch of the greedy accept over the key slots `slots` (zero on
-// entry; left zero unless a wait gave up).
+// Validated launch of the greedy accept over the row keys `keys` (zero on
+// entry; left zero).
 int launch_greedy(int batch, int n, int s1, int64_t vocab, int dtype, const void *target_logits,
                   const int32_t *candidates, const int32_t *retrieve_index,
                   const int32_t *retrieve_next_token, const int32_t *retrieve_next_sibling,
                   int32_t *predict, int32_t *accept_index, int32_t *accept_length,
-                  int32_t *target_predict, uint64_t *slots, int32_t *dev_status, hipStream_t st) {
+                  int32_t *target_predict, uint64_t *keys, int32_t *dev_status, hipStream_t st) {
     const int nch = num_chunks(vocab);
     const int64_t items = (int64_t)batch * n * nch;
     const size_t eb = dtype == SPEC_BF16 ? 2 : 4;
@@ -264,24 +221,13 @@ int launch_greedy(int batch, int n, int s1, int64_t vocab, int dtype, const void
     A.accept_length = accept_length;
     A.target_predict = target_predict;
     A.status = dev_status;
-    A.slots = slots;
-    A.poll_limit = spec::poll_limit();
+    A.keys = keys;
     const dim3 grid((unsigned)items);
-    const bool fused = !spec::stream_capturing(st) &&
-                       batch < (dtype == SPEC_BF16 ? fused_capacity<SPEC_BF16>()
-                                                   : fused_capacity<SPEC_F32>());
-    if (fused) {
-        if (dtype == SPEC_BF16)
-            hipLaunchKernelGGL((greedy_kernel<SPEC_BF16, true>), grid, dim3(kSweepThreads), 0, st, A);
-        else
-            hipLaunchKernelGGL((greedy_kernel<SPEC_F32, true>), grid, dim3(kSweepThreads), 0, st, A);
-    } else {
-        if (dtype == SPEC_BF16)
-            hipLaunchKernelGGL((greedy_kernel<SPEC_BF16, false>), grid, dim3(kSweepThreads), 0, st, A);
-        else
-            hipLaunchKernelGGL((greedy_kernel<SPEC_F32, false>), grid, dim3(kSweepThreads), 0, st, A);
-        hipLaunchKernelGGL(greedy_walk_kernel, dim3(batch), dim3(kSweepThreads), 0, st, A);
-    }
+    if (dtype == SPEC_BF16)
+        hipLaunchKernelGGL((greedy_sweep_kernel<SPEC_BF16>), grid, dim3(kSweepThreads), 0, st, A);
+    else
+        hipLaunchKernelGGL((greedy_sweep_kernel<SPEC_F32>), grid, dim3(kSweepThreads), 0, st, A);
+    hipLaunchKernelGGL(greedy_walk_kernel, dim3(batch), dim3(kSweepThreads), 0, st, A);
     return spec::launch_status();
 }
 
@@ -327,14 +273,14 @@ extern "C" int spec_accept_greedy(int batch, int n, int s1, int64_t vocab, int d
 }
 
 // ---------------------------------------------------------------------------
-// The entry point that allocates nothing: the key slots live in a fixed
+// The entry point that allocates nothing: the row keys live in a fixed
 // array of the library, one copy per device.
 // ---------------------------------------------------------------------------
 
 namespace {
 
-constexpr int64_t kNoAllocSlots = 131072;   // 1 MiB of 64-bit keys
-static __device__ __align__(256) uint64_t scratch[kNoAllocSlots];
+constexpr int64_t kNoAllocKeys = 32768;     // 256 KiB of 64-bit row keys
+static __device__ __align__(256) uint64_t scratch[kNoAllocKeys];
 
 constexpr int kMaxDevices = 64;
 std::once_flag scratch_once[kMaxDevices];
@@ -354,10 +300,10 @@ uint64_t *scratch_address() {
     return scratch_ptr[dev];
 }
 
-__global__ __launch_bounds__(256) void clear_slots_kernel(uint64_t *slots, int64_t count) {
+__global__ __launch_bounds__(256) void clear_keys_kernel(uint64_t *keys, int64_t count) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
          i += (int64_t)gridDim.x * 256)
-        slots[i] = 0;
+        keys[i] = 0;
 }
 
 }  // namespace
@@ -374,17 +320,18 @@ extern "C" int spec_accept_greedy_noalloc(int batch, int n, int s1, int64_t voca
                                 retrieve_index, retrieve_next_token, retrieve_next_sibling,
                                 predict, accept_index, accept_length);
     if (rc != SPEC_OK) return rc == 1 ? SPEC_OK : rc;
-    const int64_t used = (int64_t)batch * n * num_chunks(vocab);
-    if (used > kNoAllocSlots) return SPEC_ERR_WORKSPACE;
-    uint64_t *slots = scratch_address();
-    if (slots == nullptr) return SPEC_ERR_HIP;
+    const int64_t used = (int64_t)batch * n;
+    if (used > kNoAllocKeys) return SPEC_ERR_WORKSPACE;
+    uint64_t *keys = scratch_address();
+    if (keys == nullptr) return SPEC_ERR_HIP;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    // the array keeps the last call's contents (a call whose wait gave up
-    // may leave keys behind): the slots this call uses start at zero
+    // every call leaves the keys it used zero, but the array is shared by
+    // every call on the device (one on another stream may overlap): the
+    // keys this call uses start at zero
     const unsigned blocks = (unsigned)std::min<int64_t>((used + 255) / 256, 512);
-    hipLaunchKernelGGL(clear_slots_kernel, dim3(blocks), dim3(256), 0, st, slots, used);
+    hipLaunchKernelGGL(clear_keys_kernel, dim3(blocks), dim3(256), 0, st, keys, used);
     if (hipPeekAtLastError() != hipSuccess) return spec::launch_status();
     return launch_greedy(batch, n, s1, vocab, dtype, target_logits, candidates, retrieve_index,
                          retrieve_next_token, retrieve_next_sibling, predict, accept_index,
-                         accept_length, target_predict, slots, dev_status, st);
+                         accept_length, target_predict, keys, dev_status, st);
 }

@@ -694,7 +694,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA split kernel with K/V loaded straight into LDS (head dim 128,
-// page size 16, one wave per 32-row block)
+// 8 waves, power-of-two page sizes up to 64)
 // ---------------------------------------------------------------------------
 //
 // The 8-wave form above without its register staging: each 64-key tile
@@ -708,11 +708,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_split_mfma_kernel(AttnParams 
 // Each wave loads 8 keys of a tile (two 1 KB runs of K, two of V) with
 // indexed loads (record = one slot's row of all KV heads, so no 64-bit
 // address per lane; a bad slot is an index past the records, which reads
-// zeros).  The 8 keys lie in one 16-slot page; the split's page ids are
-// copied into LDS before the loop, which then loads nothing but tiles.  Tile t sits in buffer t % 4, a static buffer per
-// unrolled step, so the compiler can tell one buffer's loads from another's
-// reads; the wait for tile t is explicit (this wave's vector-memory count,
-// then a barrier).  Scores, softmax and the PV product are the 8-wave form's.
+// zeros).  The split's page ids are copied into LDS before the loop, which
+// then loads nothing but tiles; with pages of 8 slots or more a wave's 8 keys
+// lie in one page (one id per wave), with smaller pages every lane looks its
+// key's page up.  Tile t sits in buffer t % 4, a static buffer per unrolled
+// step, so the compiler can tell one buffer's loads from another's reads;
+// the wait for tile t is explicit (this wave's vector-memory count, then a
+// barrier).  Scores, softmax and the PV product are the 8-wave form's; with
+// KH = 2 the waves pair up as in that form (each pair owns 32 rows, its two
+// waves take the two 32-key halves of every tile) and merge through LDS.
 
 constexpr int kDmaTile = kTileKeys * 128 * 2;          // 16 KB: K (or V) of one tile
 constexpr int kDmaMaxPages = 2048;                     // page ids of a split held in LDS
@@ -748,6 +752,20 @@ __device__ __forceinline__ char *dma_vbuf() {
     else return dma_v3;
 }
 
+// tile buffer i of the eight (K buffers 0..3, then V buffers 0..3)
+__device__ __forceinline__ char *dma_wave_buf(int i) {
+    switch (i) {
+        case 0: return dma_k0;
+        case 1: return dma_k1;
+        case 2: return dma_k2;
+        case 3: return dma_k3;
+        case 4: return dma_v0;
+        case 5: return dma_v1;
+        case 6: return dma_v2;
+        default: return dma_v3;
+    }
+}
+
 // position of 16-byte piece c of key k in its row is c ^ piece_swz(k)
 __device__ __forceinline__ int piece_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
 
@@ -763,9 +781,12 @@ __device__ __forceinline__ void wait_tiles_barrier(int n) {
 
 template <int V> using ic = std::integral_constant<int, V>;
 
+template <int KH>
 __global__ __launch_bounds__(512, 1) void attn_dma_kernel(AttnParams P, int xcd_remap) {
+    static_assert(KH == 1 || KH == 2, "key halves");
     constexpr int D = 128, NT = 512, DK = D / 16, DT = D / 32;
     constexpr int kOpsPerTile = 4;        // loads per wave and tile: two K runs, two V runs
+    constexpr int NRB = 8 / KH;           // row blocks per workgroup
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -773,6 +794,10 @@ __global__ __launch_bounds__(512, 1) void attn_dma_kernel(AttnParams P, int xcd_
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int half = lane >> 5;
     const int col = lane & 31;
+    const int rblk = wave_u % NRB;        // row block of this wave
+    const int khalf = wave_u / NRB;       // key half of this wave (KH = 2)
+    const int ps = P.page_size;           // a power of two, at most 64
+    const int psh = __builtin_ctz((unsigned)ps);
 
     int b, kvh, split, rg, nsp, kb, span;
     int64_t slot_j;                        // split slot of the partials
@@ -815,40 +840,24 @@ __global__ __launch_bounds__(512, 1) void attn_dma_kernel(AttnParams P, int xcd_
     span = __builtin_amdgcn_readfirstlane(span);
     __shared__ int32_t s_tree[kMaxTreeNodes];
     __shared__ int32_t s_pages[kDmaMaxPages];
+    // Loads that do not depend on the sequence length go out with it: the
+    // request's tree slots, the page-table entries of the whole split (kb is
+    // a multiple of 64, so of the page size; entries past the request's
+    // pages are loaded but never used), the query fragments and mask word.
+    constexpr int kPagesPerThread = kDmaMaxPages / NT;
     int pre_tree = -1;
     if (tid < P.n) pre_tree = P.out_cache_loc[(int64_t)b * P.n + tid];
-    const int L = P.seq_lens[b];
-    int err = 0;
-    if (L < 0 || L > P.max_seq_len) {
-        if (tid == 0 && split == 0 && rg == 0) spec::raise_status(P.status, SPEC_ST_RANGE);
-        mark_empty_split(P, b, kvh, split, rg);
-        return;
+    const int span_pages = (span + ps - 1) >> psh;
+    const int page0 = kb >> psh;
+    int pgv[kPagesPerThread];
+#pragma unroll
+    for (int j = 0; j < kPagesPerThread; ++j) {
+        const int i = tid + j * NT;
+        pgv[j] = (i < span_pages && page0 + i < P.max_pages)
+                     ? P.page_table[(int64_t)b * P.max_pages + page0 + i] : -1;
     }
-    const int ke = min(L + P.n, kb + span);
-    if (kb >= ke) {
-        mark_empty_split(P, b, kvh, split, rg);
-        return;
-    }
-    const int ntiles = (ke - kb + kTileKeys - 1) / kTileKeys;
-    if (tid < P.n) s_tree[tid] = pre_tree;
-    // the split's page-table entries into LDS (history keys kb .. min(L, ke)
-    // - 1; the host plans splits of at most kDmaMaxPages pages), so the loop
-    // makes no other memory loads than the tiles'
-    {
-        const int hist_end = min(L, ke);
-        const int npg = hist_end > kb ? (hist_end - kb + 15) / 16 : 0;
-        if (npg > kDmaMaxPages) {
-            if (tid == 0) spec::raise_status(P.status, SPEC_ST_RANGE);
-            mark_empty_split(P, b, kvh, split, rg);
-            return;
-        }
-        for (int i = tid; i < npg; i += NT)
-            s_pages[i] = P.page_table[(int64_t)b * P.max_pages + kb / 16 + i];
-    }
-
-    // ---- query fragments (B operand of S^T = K Q^T) ------------------------
-    const int rho = rg * P.rows_per_group + wave * 32 + col;
-    const bool wave_active = rg * P.rows_per_group + wave * 32 < P.rows;
+    const int rho = rg * P.rows_per_group + rblk * 32 + col;
+    const bool wave_active = rg * P.rows_per_group + rblk * 32 < P.rows;
     bf16x8 qf[DK];
     uint64_t mword = 0;
     if (rho < P.rows) {
@@ -863,6 +872,30 @@ __global__ __launch_bounds__(512, 1) void attn_dma_kernel(AttnParams P, int xcd_
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk) qf[kk] = bf16x8{};
     }
+    const int L = P.seq_lens[b];
+    int err = 0;
+    if (span_pages > kDmaMaxPages) {       // the host plans splits of at most kDmaMaxPages pages
+        if (tid == 0) spec::raise_status(P.status, SPEC_ST_RANGE);
+        mark_empty_split(P, b, kvh, split, rg);
+        return;
+    }
+    if (L < 0 || L > P.max_seq_len) {
+        if (tid == 0 && split == 0 && rg == 0) spec::raise_status(P.status, SPEC_ST_RANGE);
+        mark_empty_split(P, b, kvh, split, rg);
+        return;
+    }
+    const int ke = min(L + P.n, kb + span);
+    if (kb >= ke) {
+        mark_empty_split(P, b, kvh, split, rg);
+        return;
+    }
+    const int ntiles = (ke - kb + kTileKeys - 1) / kTileKeys;
+    if (tid < P.n) s_tree[tid] = pre_tree;
+    // the split's page-table entries into LDS, so the loop makes no other
+    // memory loads than the tiles'
+#pragma unroll
+    for (int j = 0; j < kPagesPerThread; ++j)
+        if (tid + j * NT < span_pages) s_pages[tid + j * NT] = pgv[j];
 
     // ---- loads: this lane's two keys of a tile are kl0 and kl0 + 4 ----------
     const int kl0 = 8 * wave + (lane >> 4);
@@ -878,30 +911,37 @@ __global__ __launch_bounds__(512, 1) void attn_dma_kernel(AttnParams P, int xcd_
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void *>(P.v_pool), (short)stride, (int)P.num_slots, (int)kRsrcWord3);
     // page id of this wave's 8 keys of tile t (-1 when its first key is not
-    // a history key), from the LDS copy of the split's page-table entries
+    // a history key, or pages are smaller than 8 slots), from the LDS copy of
+    // the split's page-table entries
     auto wave_page = [&](int t) -> int {
         const int p = kb + t * kTileKeys + 8 * wave_u;
-        if (t >= ntiles || p >= L) return -1;
-        return s_pages[(p - kb) / 16];
+        if (t >= ntiles || p >= L || ps < 8) return -1;
+        return s_pages[(p - kb) >> psh];
+    };
+    // slot of history key p of the split (-1 for a negative page id)
+    auto hist_slot = [&](int p) -> int64_t {
+        const int page = s_pages[(p - kb) >> psh];
+        return page < 0 ? -1 : ((int64_t)page << psh) + (p & (ps - 1));
     };
     auto dma_tile = [&](char *kdst, char *vdst, int t, int page) {
         uint32_t idx[2];
         const int tb = kb + t * kTileKeys;
-        if (tb + kTileKeys <= min(L, ke)) {
-            // a tile of history keys only: the wave's page (uniform), then
-            // the lane's slot within it
+        if (tb + kTileKeys <= min(L, ke) && ps >= 8) {
+            // a tile of history keys only, the wave's 8 keys in one page:
+            // the wave's page (uniform), then the lane's slot within it
             page = __builtin_amdgcn_readfirstlane(page);
-            const bool ok = page >= 0 && (int64_t)page * 16 + 16 <= P.num_slots;
+            const bool ok = page >= 0 && ((int64_t)page << psh) + ps <= P.num_slots;
             if (!ok) err |= SPEC_ST_RANGE;
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                idx[j] = ok ? (uint32_t)(page * 16 + ((kl0 + 4 * j) & 15)) : 0xFFFFFFFFu;
+                idx[j] = ok ? ((uint32_t)page << psh) + (uint32_t)((kl0 + 4 * j) & (ps - 1))
+                            : 0xFFFFFFFFu;
         } else {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int p = tb + kl0 + 4 * j;
                 int64_t slot = -1;
-                if (p < L) slot = page < 0 ? -1 : (int64_t)page * 16 + (p & 15);
+                if (p < L) slot = hist_slot(p);
                 else if (p < ke) slot = s_tree[p - L];
                 const bool ok = slot >= 0 && slot < P.num_slots;
                 if (!ok && p < ke) err |= SPEC_ST_RANGE;
@@ -964,7 +1004,8 @@ __global__ __launch_bounds__(512, 1) void attn_dma_kernel(AttnParams P, int xcd_
         const int tile_base = kb + it * kTileKeys;
         const bool edge = (tile_base + kTileKeys > ke) || (tile_base + kTileKeys > L);
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
+        for (int si = 0; si < 2 / KH; ++si) {
+            const int sub = KH == 2 ? khalf : si;
             floatx16 sacc = floatx16{};
 #pragma unroll
             for (int kk = 0; kk < DK; ++kk) {
@@ -1051,32 +1092,84 @@ __global__ __launch_bounds__(512, 1) void attn_dma_kernel(AttnParams P, int xcd_
         if (it + 3 < ntiles) step(ic<3>{}, it + 3);
     }
 
-    // ---- epilogue -------------------------------------------------------------
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    if (rho < P.rows) {
-        const int node = rho / P.group;
-        const int h = kvh * P.group + rho % P.group;
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        __bf16 *op;
-        if (nsp == 1) {
-            op = static_cast<__bf16 *>(P.out) + (((int64_t)b * P.n + node) * P.hq + h) * D;
-        } else {
-            const int64_t pidx = (slot_j * P.hkv + kvh) * P.rows + rho;
-            op = static_cast<__bf16 *>(P.part_o) + pidx * D;
-            if (half == 0) P.part_ml[pidx] = make_float2(m_run, l_tot);
+    // ---- key-half merge: the second wave of a pair hands over its state ----
+    // (the last step waited for every tile load, and the barrier below ends
+    // every wave's reads: K buffer rblk takes the pair's O^T, lane-minor, V
+    // buffer 0 the (max, sum) of every pair)
+    if constexpr (KH == 2) {
+        float *mo = reinterpret_cast<float *>(dma_wave_buf(rblk));
+        float *mml = reinterpret_cast<float *>(dma_v0) + rblk * 128;
+        __syncthreads();
+        if (khalf == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mo[(dt * 16 + i) * 64 + lane] = oacc[dt][i];
+            mml[lane] = m_run;
+            mml[64 + lane] = l_run;
         }
+        __syncthreads();
+        if (khalf == 1) {
+            for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, 64);
+            if (lane == 0) spec::raise_status(P.status, err);
+            return;
+        }
+        const float m2 = mml[lane], l2 = mml[64 + lane];
+        const float mm = fmaxf(m_run, m2);
+        const float a1 = m_run == -INFINITY ? 0.f : exp2f(m_run - mm);
+        const float a2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mm);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-                uint32_t hv[4];
+            for (int i = 0; i < 16; ++i)
+                oacc[dt][i] = oacc[dt][i] * a1 + mo[(dt * 16 + i) * 64 + lane] * a2;
+        l_run = l_run * a1 + l2 * a2;
+        m_run = mm;
+    }
+
+    // ---- epilogue: O / sum in bf16 (the output itself for a request with
+    // one split, else this split's partial, which the merge weights by its
+    // sum).  A lane's O^T fragment holds 4-dim runs of its row, so the
+    // wave's 32 x 128 block goes through LDS (rows 272 bytes apart) and
+    // leaves as whole 16-byte pieces of each row.
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (rho < P.rows && nsp != 1 && half == 0)
+        P.part_ml[(slot_j * P.hkv + kvh) * P.rows + rho] = make_float2(m_run, l_tot);
+    constexpr int kStageRow = D * 2 + 16;
+    if constexpr (KH == 1) __syncthreads();    // every wave is done with the tiles
+    // a buffer of this wave's own: with KH = 2 the one its pair merged in
+    char *stage = dma_wave_buf(KH == 2 ? rblk : wave_u);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    hv[j] = __builtin_bit_cast(uint16_t,
-                                               static_cast<__bf16>(oacc[dt][4 * j4 + j] * inv));
-                *reinterpret_cast<uint2 *>(op + dt * 32 + 8 * j4 + 4 * half) =
-                    make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+            uint32_t hv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                hv[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(oacc[dt][4 * j4 + j] * inv));
+            *reinterpret_cast<uint2 *>(stage + col * kStageRow + (dt * 32 + 8 * j4 + 4 * half) * 2) =
+                make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int row0 = rg * P.rows_per_group + rblk * 32;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int c = lane + 64 * r;
+        const int row = c >> 4, piece = c & 15;
+        const uint4 v = *reinterpret_cast<const uint4 *>(stage + row * kStageRow + piece * 16);
+        const int rr = row0 + row;
+        if (rr < P.rows) {
+            __bf16 *op;
+            if (nsp == 1) {
+                const int node = rr / P.group;
+                const int h = kvh * P.group + rr % P.group;
+                op = static_cast<__bf16 *>(P.out) + (((int64_t)b * P.n + node) * P.hq + h) * D;
+            } else {
+                op = static_cast<__bf16 *>(P.part_o) + ((slot_j * P.hkv + kvh) * P.rows + rr) * D;
             }
+            *reinterpret_cast<uint4 *>(op + piece * 8) = v;
+        }
     }
     for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, 64);
     if (lane == 0) spec::raise_status(P.status, err);
@@ -1377,22 +1470,26 @@ size_t workspace_bytes_for(const Plan &pl, int batch, int n, int hq, int hkv, in
     return o_plan + (pl.dyn ? spec::align_up((size_t)batch * sizeof(int2), 256) : 0);
 }
 
-// The LDS-load form serves 8-wave workgroups of one wave per 32-row block
-// at head dim 128 and page size 16, when a slot's row of all KV heads fits
-// a buffer record (stride below 2^14 bytes), the pool fits 32-bit buffer
-// offsets and no split spans more pages than the kernel holds in LDS.
+// The LDS-load form serves 8-wave workgroups (one or two waves per 32-row
+// block) at head dim 128 and power-of-two page sizes up to 64, when a slot's
+// row of all KV heads fits a buffer record (stride below 2^14 bytes), the
+// pool fits 32-bit buffer offsets and no split spans more pages than the
+// kernel holds in LDS.
 bool dma_form(const Plan &pl, const AttnParams &P, int d) {
     const int64_t stride = (int64_t)P.hkv * d * 2;
-    return d == 128 && pl.nw == 8 && pl.kh == 1 && P.page_size == 16 && stride < (1 << 14) &&
-           P.num_slots * stride < (int64_t(1) << 32) &&
-           (int64_t)pl.max_span_tiles * (kTileKeys / 16) <= kDmaMaxPages;
+    const int ps = P.page_size;
+    return d == 128 && pl.nw == 8 && ps >= 1 && ps <= kTileKeys && (ps & (ps - 1)) == 0 &&
+           stride < (1 << 14) && P.num_slots * stride < (int64_t(1) << 32) &&
+           (int64_t)pl.max_span_tiles * kTileKeys / ps <= kDmaMaxPages;
 }
 
 template <int D>
 void launch_mfma(const Plan &pl, const AttnParams &P, unsigned groups, hipStream_t st) {
     const int remap = groups % 8 == 0 ? 1 : 0;
-    if (D == 128 && dma_form(pl, P, D))
-        hipLaunchKernelGGL(attn_dma_kernel, dim3(groups), dim3(512), 0, st, P, remap);
+    if (D == 128 && dma_form(pl, P, D) && pl.kh == 2)
+        hipLaunchKernelGGL(attn_dma_kernel<2>, dim3(groups), dim3(512), 0, st, P, remap);
+    else if (D == 128 && dma_form(pl, P, D))
+        hipLaunchKernelGGL(attn_dma_kernel<1>, dim3(groups), dim3(512), 0, st, P, remap);
     else if (pl.kh == 2)
         hipLaunchKernelGGL((attn_split_mfma_kernel<D, 8, 2>), dim3(groups), dim3(512), 0, st, P, remap);
     else if (pl.nw == 4)

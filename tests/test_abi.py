@@ -47,6 +47,8 @@ def test_host_only_queries():
         assert S.spec_mask_word_bytes(n) * 8 == oracle.mask_word_bits(n)
     assert S.spec_mask_word_bytes(0) == 0 and S.spec_mask_word_bytes(65) == 0
     assert S.spec_accept_workspace_size(1, 64, 128256, 0) > 0
+    # greedy: one 64-bit key per verify row
+    assert S.spec_accept_workspace_size(5, 64, 128256, 0) == 5 * 64 * 8
     assert S.spec_accept_workspace_size(1, 64, 128256, 1) > S.spec_accept_workspace_size(1, 64, 128256, 0)
     # one (max, sum) pair of 64-bit words per verify row and 8192-entry chunk
     assert S.spec_accept_target_only_workspace_size(1, 64, 128256) == 64 * 16 * 16
@@ -113,9 +115,10 @@ def test_host_errors_before_launch():
     assert na(1, 6, 4, 32, 9, *f10) == -3
     assert na(1, 6, 4, 32, 0, *([P0] * 11)) == -1
     assert na(0, 6, 4, 32, 0, *([P0] * 11)) == 0
-    # 200 requests x 64 nodes x 16 chunks of a 128256 vocabulary: more keys
-    # than the library's fixed array holds (131072)
-    assert na(200, 64, 7, 128256, 1, *f10) == -5
+    # 513 requests x 64 nodes: more row keys than the library's fixed array
+    # holds (32768)
+    assert na(513, 64, 7, 128256, 1, *f10) == -5
+    assert na(32769, 1, 2, 128256, 1, *f10) == -5
     asm = lib.spec_accept_sample
     asm.restype = I
     asm.argtypes = [I, I, I, ctypes.c_int64, I] + [ctypes.c_void_p] * 12 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]

@@ -296,8 +296,12 @@ def full(cid, attention):
 
 # Split-KV plans whose last key split holds 1, 2, 3 or 4 tiles, or ends in a
 # part tile, or whose splits are 4 tiles long: every output vector against
-# the oracle.
+# the oracle.  One-slot pages take the LDS-load form; 12-slot pages (not a
+# power of two) keep the register-staged form with key halves.
 SPLIT_CASES = {
+    "L4160_last1_ps12": W.shrink(W.CONFIGS[2], hist=("fixed", 4160), vocab=1000, page_size=12),
+    "L4288_last3_ps12": W.shrink(W.CONFIGS[2], hist=("fixed", 4288), vocab=1000, page_size=12),
+    "L4100_part_ps12": W.shrink(W.CONFIGS[2], hist=("fixed", 4100), vocab=1000, page_size=12),
     "L4160_last1": W.shrink(W.CONFIGS[2], hist=("fixed", 4160), vocab=1000),
     "L4224_last2": W.shrink(W.CONFIGS[2], hist=("fixed", 4224), vocab=1000),
     "L4288_last3": W.shrink(W.CONFIGS[2], hist=("fixed", 4288), vocab=1000),
@@ -339,14 +343,25 @@ LONG_SPLIT_CASES = {
 }
 
 
-# Shapes of the LDS-load form (8-wave workgroups, one wave per 32-row block,
-# page size 16): the length-balanced plan over ragged lengths (history ends
-# inside a page and inside a wave's 8 keys; tree keys share its page), and
-# the static plan of one request.  Every output vector is compared.
+# Shapes of the LDS-load form: one wave per 32-row block (KH = 1) and wave
+# pairs taking key halves (KH = 2), pages of 1 to 64 slots (below 8 every
+# lane looks its key's page up; from 8 on a wave's keys share one page id),
+# static and length-balanced plans, and a row count (35) that leaves whole
+# row blocks of the workgroup idle.
 DMA_CASES = {
     "b4_Lu_ragged": W.shrink(W.CONFIGS[5], batch=4, hist=("uniform", 9001, 17003), vocab=1000),
     "b1_L50005": W.shrink(W.CONFIGS[5], batch=1, hist=("fixed", 50005), vocab=1000),
     "b3_L8195": W.shrink(W.CONFIGS[5], batch=3, hist=("fixed", 8195), vocab=1000),
+    "kh1_b2_ps8_Lu": W.shrink(W.CONFIGS[5], batch=2, hist=("uniform", 5000, 9000), vocab=1000,
+                              page_size=8),
+    "kh2_b1_ps1_L3001": W.shrink(W.CONFIGS[2], hist=("fixed", 3001), vocab=1000),
+    "kh2_b2_ps1_Lu": W.shrink(W.CONFIGS[2], batch=2, hist=("uniform", 600, 1900), vocab=1000),
+    "kh2_b2_ps2_Lu": W.shrink(W.CONFIGS[3], batch=2, hist=("uniform", 300, 1900), vocab=1000,
+                              page_size=2),
+    "kh2_b3_ps4_Lu": W.shrink(W.CONFIGS[3], batch=3, hist=("uniform", 100, 2500), vocab=1000,
+                              page_size=4),
+    "kh2_b1_ps64_L2600": W.shrink(W.CONFIGS[2], hist=("fixed", 2600), vocab=1000, page_size=64),
+    "kh2_b16_rows35": W.shrink(W.CONFIGS[4], batch=16, hist=("fixed", 700), vocab=1000),
 }
 
 
@@ -464,7 +479,10 @@ def test_full_attention_vector_complete(cid):
 
 @pytest.mark.parametrize("name,cfg", [
     ("lds_load_form", DMA_CASES["b3_L8195"]),
-    ("register_staged", W.shrink(W.CONFIGS[3], batch=3, hist=("fixed", 2000), vocab=1000)),
+    ("lds_load_form_kh2_ps1", W.shrink(W.CONFIGS[2], batch=3, hist=("fixed", 700), vocab=1000)),
+    # a page size that is not a power of two keeps the register-staged form
+    ("register_staged", W.shrink(W.CONFIGS[3], batch=3, hist=("fixed", 2000), vocab=1000,
+                                 page_size=12)),
 ])
 def test_verify_attention_bad_slots(name, cfg):
     """Page ids and tree slots out of range in requests 1 and 2: the call

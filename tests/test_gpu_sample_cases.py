@@ -160,13 +160,13 @@ def test_greedy_workspace_reused():
         assert int(torch.count_nonzero(ws)) == 0
 
 
-def test_greedy_two_launch_path():
-    """More requests than the one-launch greedy accept keeps resident at once
-    (its walkers would crowd out the chunk work): the walk runs as a second
-    launch.  Bit-exact against the oracle; the workspace is left zero."""
+def test_greedy_many_requests():
+    """More requests than the device holds workgroups at once (2200 walk
+    workgroups after 2200 x 5 sweep workgroups).  Bit-exact against the
+    oracle; the workspace is left zero."""
     cfg = W.shrink(W.CONFIGS[4], batch=2200, hist=H8, vocab=300)
     b, n, s1 = cfg.batch, cfg.num_draft_tokens, cfg.num_steps + 1
-    say(f"[greedy two launches] b={b} n={n} V={cfg.vocab}")
+    say(f"[greedy many requests] b={b} n={n} V={cfg.vocab}")
     w, t, tl, dl = _setup(cfg, 51)
     ws = torch.zeros(S.spec_accept_workspace_size(b, n, cfg.vocab, 0), dtype=torch.uint8,
                      device="cuda")

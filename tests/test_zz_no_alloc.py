@@ -1,4 +1,4 @@
-"""spec_accept_greedy_noalloc (keys in the library's fixed device array)
+"""spec_accept_greedy_noalloc (row keys in the library's fixed device array)
 against spec_accept_greedy (keys in a caller workspace): two calls in a row,
 the second on a smaller input, each bit-exact against the workspace entry
 point and the oracle.  The second call also checks that the array's
@@ -69,9 +69,9 @@ def test_noalloc_matches_workspace_entry_two_calls():
 
 
 def test_noalloc_refuses_more_keys_than_the_array_holds():
-    # 129 requests x 64 nodes x 16 chunks of a 128256 vocabulary = 132096
-    # keys, more than the fixed array's 131072: refused before any launch
-    b, n, s1, V = 129, 64, 7, 128256
+    # 513 requests x 64 nodes = 32832 row keys, more than the fixed array's
+    # 32768: refused before any launch
+    b, n, s1, V = 513, 64, 7, 300
     logits = torch.zeros(b * n * V, dtype=torch.int16, device="cuda")
     idx = torch.zeros(b * n, dtype=torch.int32, device="cuda")
     out = torch.zeros(b * s1, dtype=torch.int32, device="cuda")
