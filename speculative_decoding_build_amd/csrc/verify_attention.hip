@@ -1006,12 +1006,33 @@ __global__ __launch_bounds__(512, 1) void attn_dma_kernel(AttnParams P, int xcd_
 #pragma unroll
         for (int si = 0; si < 2 / KH; ++si) {
             const int sub = KH == 2 ? khalf : si;
+            // the sub-block's K fragments, then its score products; its V^T
+            // fragments (which do not depend on the scores) go out before
+            // the softmax, so their LDS latency passes under it
             floatx16 sacc = floatx16{};
+            bf16x8 kfa[DK];
 #pragma unroll
-            for (int kk = 0; kk < DK; ++kk) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kt + sub * 8192 + kaddr[kk]);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc, 0, 0, 0);
-            }
+            for (int kk = 0; kk < DK; ++kk)
+                kfa[kk] = *reinterpret_cast<const bf16x8 *>(kt + sub * 8192 + kaddr[kk]);
+#pragma unroll
+            for (int kk = 0; kk < DK; ++kk)
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfa[kk], qf[kk], sacc, 0, 0, 0);
+            bf16x8 vfa[2][DT];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    // V^T rows dt*32 .. +31, keys sub*32 + 16*st + 4*half +
+                    // {0..3, 8..11}: two transposing reads
+                    const char *vb = vt + sub * 8192 + st * 4096;
+                    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_short4v *)(vb + vaddr[dt][0]));
+                    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_short4v *)(vb + vaddr[dt][1]));
+                    const short4v v8[2] = {lo, hi};
+                    vfa[st][dt] = __builtin_bit_cast(bf16x8, v8);
+                }
+            __builtin_amdgcn_sched_barrier(0);
             // lane holds keys sub*32 + 8*(i/4) + 4*half + i%4 of query col
             float sv[16];
 #pragma unroll
@@ -1067,22 +1088,11 @@ __global__ __launch_bounds__(512, 1) void attn_dma_kernel(AttnParams P, int xcd_
             }
             l_run += lsum;
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    // V^T rows dt*32 .. +31, keys sub*32 + 16*st + 4*half +
-                    // {0..3, 8..11}: two transposing reads
-                    const char *vb = vt + sub * 8192 + st * 4096;
-                    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_short4v *)(vb + vaddr[dt][0]));
-                    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_short4v *)(vb + vaddr[dt][1]));
-                    const short4v v8[2] = {lo, hi};
-                    const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], oacc[dt],
-                                                                       0, 0, 0);
-                }
-            }
+                for (int dt = 0; dt < DT; ++dt)
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfa[st][dt], pf[st],
+                                                                       oacc[dt], 0, 0, 0);
         }
     };
     for (int it = 0; it < ntiles; it += 4) {
