@@ -203,7 +203,9 @@ __device__ __forceinline__ double rescale(float m, double s, float M, float chi,
 }
 
 // Max and sum of exponentials from every thread's partial (m, s), target and
-// draft at once; every thread gets the workgroup's values.
+// draft at once; every thread gets the workgroup's values.  No barrier after
+// the reads of sm / ss: the walk passes a barrier (the statistics exchange's)
+// before it calls this again.
 template <int NT>
 __device__ void block_stats(float &mt, double &st, float &md, double &sd, float chi, float clo,
                             float *sm, double *ss) {
@@ -230,7 +232,6 @@ __device__ void block_stats(float &mt, double &st, float &md, double &sd, float 
         St += rescale(sm[2 * w], ss[2 * w], Mt, chi, clo);
         Sd += rescale(sm[2 * w + 1], ss[2 * w + 1], Md, chi, clo);
     }
-    __syncthreads();
     mt = Mt;
     st = St;
     md = Md;
@@ -261,6 +262,8 @@ __device__ double block_exclusive_scan(double v, double *scratch, double &total)
     return before + incl - v;
 }
 
+// Sum of v over the workgroup.  No barrier after the reads of scratch: the
+// caller passes one before the next use of it.
 template <int NT>
 __device__ double block_sum(double v, double *scratch) {
     v = full_wave_sum_d(v);
@@ -269,7 +272,6 @@ __device__ double block_sum(double v, double *scratch) {
     double s = 0.0;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) s += scratch[w];
-    __syncthreads();
     return s;
 }
 
@@ -510,6 +512,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     // total over the slices of a per-workgroup sum
     auto exchange_sum = [&](double slice_sum) -> double {
         if (!COOP) {
+            __syncthreads();           // every thread has read the block sum's scratch
             sj = slice_sum;
             return slice_sum;
         }
