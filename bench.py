@@ -382,6 +382,40 @@ def _traffic(cfg):
                                      "verify_attention.hip"))
 
 
+def measured_peaks(torch):
+    """Achievable peaks on this machine, reported beside the nominal ones: a plain
+    device copy of 2 GiB (bytes read plus bytes written over its time) and a
+    bf16 8192 x 8192 x 8192 matrix product through torch.matmul (the vendor
+    BLAS on the matrix cores: 2 * 8192^3 FLOP over its time); best of five
+    HIP-event timings each, after one untimed call."""
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = best(lambda: dst.copy_(src))
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16).contiguous()
+    bm = torch.randn(m, m, device="cuda").to(torch.bfloat16).contiguous()
+    t_mm = best(lambda: torch.matmul(a, bm))
+    del a, bm
+    torch.cuda.synchronize()
+    return {"copy_gbs": 2 * nbytes / t_copy / 1e9, "bf16_gemm_tflops": 2 * m ** 3 / t_mm / 1e12,
+            "how": "device copy of 2 GiB (read + write bytes); bf16 8192^3 torch.matmul; "
+                   "best of 5"}
+
+
 def _log(msg):
     """Progress of the run on stderr (the JSON line alone goes to stdout)."""
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -658,6 +692,20 @@ def run(args):
                                   "frac": greedy_gbs / HBM_PEAK_GBS,
                                   "algorithmic_bytes": sweep_g},
     }
+    # fractions against what this box achieves, beside the nominal ones
+    peaks = measured_peaks(torch)
+    line["measured_peaks"] = peaks
+    if mfma_bound:
+        roof["measured_peak"] = peaks["bf16_gemm_tflops"]
+        roof["frac_measured"] = attn_tflops / peaks["bf16_gemm_tflops"]
+        roof["frac_hbm_measured"] = attn_gbs / peaks["copy_gbs"]
+    else:
+        roof["measured_peak"] = peaks["copy_gbs"]
+        roof["frac_measured"] = attn_gbs / peaks["copy_gbs"]
+    line["roofline_accept_sweep"]["measured_peak"] = peaks["copy_gbs"]
+    line["roofline_accept_sweep"]["frac_measured"] = greedy_gbs / peaks["copy_gbs"]
+    _log(f"measured peaks: copy {peaks['copy_gbs']:.0f} GB/s, "
+         f"bf16 GEMM {peaks['bf16_gemm_tflops']:.0f} TFLOP/s")
     if not args.no_cpu_baseline:
         _log("CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(cfg, w, tl, dl, args.cpu_budget_s)
