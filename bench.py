@@ -669,6 +669,8 @@ def run(args):
         "graph_replay_matches_eager": graph_check,
         "ms_per_step_eager": eager_ms,
         "accept_steps_per_s": b / (op_ms[accept_op] * 1e-3),
+        "accepted_tokens_per_s": float(acc_len.sum()) / (op_ms[accept_op] * 1e-3),
+        "attention_tokens_per_s": b * n / t_attn,
         "op_ms": op_ms,
         "verify_attn_gbs": attn_gbs,
         "verify_attn_frac_hbm": attn_gbs / HBM_PEAK_GBS,
