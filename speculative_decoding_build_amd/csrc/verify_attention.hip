@@ -1329,9 +1329,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
         const WT *po = words(i);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int sidx = max(0, min(u, ns[i] - 1));
 #pragma unroll
-            for (int j = 0; j < NW_; ++j) x[i][u][j] = ns[i] > 0 ? po[sidx * sstride + j] : WT(0);
+            for (int j = 0; j < NW_; ++j) x[i][u][j] = u < ns[i] ? po[u * sstride + j] : WT(0);
         }
     }
 #pragma unroll
@@ -1348,9 +1347,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams P) {
             if (s0 > 0) {
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u) {
-                    const int sidx = min(s0 + u, ns[i] - 1);
 #pragma unroll
-                    for (int j = 0; j < NW_; ++j) x[i][u][j] = po[sidx * sstride + j];
+                    for (int j = 0; j < NW_; ++j)
+                        x[i][u][j] = s0 + u < ns[i] ? po[(s0 + u) * sstride + j] : WT(0);
                 }
             }
 #pragma unroll
