@@ -391,6 +391,42 @@ def test_verify_attention_lds_load_form(name):
     assert err <= ATTN_TOL[cfg.dtype]
 
 
+# One-slot pages around the LDS-load form's bound of 2048 page ids per split:
+# at 131008 history keys the splits hold 32 tiles (2048 ids) and take that
+# form; one key more makes them 33 tiles and the register-staged form runs.
+# Every output vector, one (request, KV head) unit at a time.
+PAGE_ID_BOUND_CASES = {
+    "ps1_L131008_2048_ids": W.shrink(W.CONFIGS[2], hist=("fixed", 131008), vocab=1000),
+    "ps1_L131009_register_staged": W.shrink(W.CONFIGS[2], hist=("fixed", 131009), vocab=1000),
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(PAGE_ID_BOUND_CASES))
+def test_verify_attention_page_id_bound(name):
+    cfg = PAGE_ID_BOUND_CASES[name]
+    w = W.make_workload(cfg, 37)
+    t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
+                          cfg.num_steps, cfg.num_draft_tokens)
+    b, n, hq, hkv = cfg.batch, cfg.num_draft_tokens, cfg.num_q_heads, cfg.num_kv_heads
+    G_ = hq // hkv
+    say(f"[attention, page-id bound] {name} b={b} L={w.seq_lens.tolist()}")
+    words = oracle.pack_mask(t["mask"], oracle.MASK_QLEN_BITS)
+    got, st = G.verify_attention(w, words)
+    assert st == 0
+    err = 0.0
+    for r in range(b):
+        for g in range(hkv):
+            ref = oracle.verify_attention_unit(w.q, w.k_pool[0], w.v_pool[0], w.page_table,
+                                               w.seq_lens, w.out_cache_loc, t["mask"], hq, hkv,
+                                               cfg.page_size, cfg.dtype, r, g)
+            mine = got[r * n:(r + 1) * n, g * G_:(g + 1) * G_]
+            err = max(err, _attn_err(mine.reshape(-1, mine.shape[-1]),
+                                     ref.reshape(-1, ref.shape[-1])))
+    say(f"    max rel err {err:.3e} over {b * hkv * n * G_} vectors")
+    assert err <= ATTN_TOL[cfg.dtype]
+
+
 @pytest.mark.parametrize("name", list(LONG_SPLIT_CASES))
 def test_verify_attention_long_splits_sampled(name):
     cfg = LONG_SPLIT_CASES[name]
