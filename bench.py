@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--config", type=int, default=5, choices=sorted(W.CONFIGS))
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured copy / GEMM peaks (profiler runs: keeps their "
+                         "kernels out of traces and counter calibration)")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="graph: each input copy's step is captured once into a HIP graph and "
@@ -694,20 +697,27 @@ def run(args):
                                   "frac": greedy_gbs / HBM_PEAK_GBS,
                                   "algorithmic_bytes": sweep_g},
     }
-    # fractions against what this box achieves, beside the nominal ones
-    peaks = measured_peaks(torch)
-    line["measured_peaks"] = peaks
-    if mfma_bound:
+    # fractions against what this box achieves, beside the nominal ones (not
+    # in a counter-calibration run: its plain copy must be the largest one)
+    if args.no_peaks or args.calibrate_copy_mb:
+        peaks = None
+    else:
+        peaks = measured_peaks(torch)
+        line["measured_peaks"] = peaks
+    if peaks is None:
+        pass
+    elif mfma_bound:
         roof["measured_peak"] = peaks["bf16_gemm_tflops"]
         roof["frac_measured"] = attn_tflops / peaks["bf16_gemm_tflops"]
         roof["frac_hbm_measured"] = attn_gbs / peaks["copy_gbs"]
     else:
         roof["measured_peak"] = peaks["copy_gbs"]
         roof["frac_measured"] = attn_gbs / peaks["copy_gbs"]
-    line["roofline_accept_sweep"]["measured_peak"] = peaks["copy_gbs"]
-    line["roofline_accept_sweep"]["frac_measured"] = greedy_gbs / peaks["copy_gbs"]
-    _log(f"measured peaks: copy {peaks['copy_gbs']:.0f} GB/s, "
-         f"bf16 GEMM {peaks['bf16_gemm_tflops']:.0f} TFLOP/s")
+    if peaks is not None:
+        line["roofline_accept_sweep"]["measured_peak"] = peaks["copy_gbs"]
+        line["roofline_accept_sweep"]["frac_measured"] = greedy_gbs / peaks["copy_gbs"]
+        _log(f"measured peaks: copy {peaks['copy_gbs']:.0f} GB/s, "
+             f"bf16 GEMM {peaks['bf16_gemm_tflops']:.0f} TFLOP/s")
     if not args.no_cpu_baseline:
         _log("CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(cfg, w, tl, dl, args.cpu_budget_s)
