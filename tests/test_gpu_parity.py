@@ -38,6 +38,7 @@ SMALL = {
     "c3s": W.shrink(W.CONFIGS[3], batch=3, hist=("uniform", 0, 400), vocab=9000),
     "c4s": W.shrink(W.CONFIGS[4], batch=5, hist=("fixed", 130), vocab=17000),
     "c5s": W.shrink(W.CONFIGS[5], batch=2, hist=("fixed", 700), vocab=8200),
+    "c5_L0mix": W.shrink(W.CONFIGS[5], batch=3, hist=("list", [0, 300, 5]), vocab=8200),
     "ps3_v1001": W.shrink(W.CONFIGS[3], batch=2, hist=("uniform", 50, 90), vocab=1001, page_size=3),
     "root_only": W.shrink(W.CONFIGS[3], batch=2, hist=("fixed", 40), vocab=500, num_draft_tokens=1),
     "d64_bf16": W.shrink(W.CONFIGS[3], batch=2, hist=("fixed", 200), vocab=700, head_dim=64),
@@ -222,7 +223,7 @@ def test_accept_sample_small(name):
     assert bad == []
 
 
-@pytest.mark.parametrize("name", ["c1", "c3s", "c5s", "ps3_v1001"])
+@pytest.mark.parametrize("name", ["c1", "c3s", "c5s", "c5_L0mix", "ps3_v1001"])
 @pytest.mark.parametrize("layers", [1, 3])
 def test_compact_kv_small(name, layers):
     w, t, tl, _ = workload(name)
@@ -367,13 +368,36 @@ DMA_CASES = {
 
 @pytest.mark.parametrize("name", list(DMA_CASES))
 def test_verify_attention_lds_load_form(name):
-    cfg = DMA_CASES[name]
+    _attention_every_unit(DMA_CASES[name], name, "LDS-load form")
+
+
+# Requests with no history (only the tree keys), alone and beside long ones:
+# the static plan's one-split path, the length-balanced plan with a request
+# of one tile, both kernel forms (one-slot and 16-slot pages: LDS-load form;
+# 12-slot pages: register-staged form) and the f32 path.
+ZERO_HIST_CASES = {
+    "L0_all_g8_ps16": W.shrink(W.CONFIGS[5], batch=2, hist=("fixed", 0), vocab=1000),
+    "L0_mixed_g8_ps16": W.shrink(W.CONFIGS[5], batch=3, hist=("list", [0, 20000, 5]), vocab=1000),
+    "L0_mixed_g4_ps1": W.shrink(W.CONFIGS[2], batch=3, hist=("list", [3000, 0, 64]), vocab=1000),
+    "L0_mixed_g8_ps12": W.shrink(W.CONFIGS[5], batch=3, hist=("list", [0, 9000, 1]), vocab=1000,
+                                 page_size=12),
+    "L0_all_f32": W.shrink(W.CONFIGS[1], hist=("fixed", 0), vocab=100),
+    "L0_mixed_f32": W.shrink(W.CONFIGS[1], hist=("list", [0, 700]), vocab=100),
+}
+
+
+@pytest.mark.parametrize("name", list(ZERO_HIST_CASES))
+def test_verify_attention_zero_history(name):
+    _attention_every_unit(ZERO_HIST_CASES[name], name, "zero history")
+
+
+def _attention_every_unit(cfg, name, label):
     w = W.make_workload(cfg, 29)
     t = oracle.build_tree(w.scores, w.tokens, w.parents, w.bonus, w.seq_lens, cfg.topk,
                           cfg.num_steps, cfg.num_draft_tokens)
     b, n, hq, hkv = cfg.batch, cfg.num_draft_tokens, cfg.num_q_heads, cfg.num_kv_heads
     G_ = hq // hkv
-    say(f"[attention, LDS-load form] {name} b={b} L={w.seq_lens.tolist()}")
+    say(f"[attention, {label}] {name} b={b} L={w.seq_lens.tolist()}")
     words = oracle.pack_mask(t["mask"], oracle.MASK_QLEN_BITS)
     got, st = G.verify_attention(w, words)
     assert st == 0

@@ -186,6 +186,10 @@ def _hist_lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
     kind = cfg.hist_len[0]
     if kind == "fixed":
         return np.full(cfg.batch, cfg.hist_len[1], dtype=np.int32)
+    if kind == "list":                     # explicit per-request lengths
+        lens = np.asarray(cfg.hist_len[1], dtype=np.int32)
+        assert lens.shape == (cfg.batch,)
+        return lens.copy()
     lo, hi = cfg.hist_len[1], cfg.hist_len[2]
     return rng.integers(lo, hi + 1, size=cfg.batch).astype(np.int32)
 
