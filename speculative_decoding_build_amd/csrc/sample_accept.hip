@@ -391,6 +391,18 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     // when seg is 16 (a uniform branch around the work on it otherwise)
     const bool wide = seg > 8;
     int cached_row = -1;               // local row whose raw logits ct / cd hold
+    // body(i) over the cached entries in order: 0..7, then 8..15 when the
+    // segment has 16.  Two loops of fixed length, so both unroll and the
+    // register arrays are only ever indexed by constants (a loop with an
+    // early exit was left rolled, indexing them through gpr-index mode).
+    auto cached_each = [&](auto &&body) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) body(i);
+        if (wide) {
+#pragma unroll
+            for (int i = 8; i < kCacheEntries; ++i) body(i);
+        }
+    };
     auto load_cache = [&](int lrow) {
         const void *trow = row_ptr(A.tlogits, lrow);
         const void *drow = row_ptr(A.dlogits, lrow);
@@ -553,11 +565,7 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
     auto segment_sum = [&](double cc) -> double {
         double m = 0.0;
         if constexpr (use_cache) {
-#pragma unroll
-            for (int i = 0; i < kCacheEntries; ++i) {
-                if (i == 8 && !wide) break;
-                m += resid_from_exp(ct[i], cd[i], rd, cc);
-            }
+            cached_each([&](int i) { m += resid_from_exp(ct[i], cd[i], rd, cc); });
         } else {
             for_each8<DT>(row_ptr(A.tlogits, lr), row_ptr(A.dlogits, lr), sa, sb, A.vec_ok,
                           [&](int64_t, const float (&xt)[8], const float (&xd)[8], int) {
@@ -593,24 +601,20 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
         double st = 0.0, sd = 0.0;
         if constexpr (use_cache) {
             if (cached_row != lr) load_cache(lr);
-#pragma unroll
-            for (int i = 0; i < kCacheEntries; ++i) {
-                if (i == 8 && !wide) break;
+            cached_each([&](int i) {
                 mt = fmaxf(mt, ct[i]);
                 md = fmaxf(md, cd[i]);
-            }
+            });
             // the registers now take the exponentials relative to this
             // thread's max; one factor per row moves them to the row's max
             const Scale2 sct{mt, chi, clo}, scd{md, chi, clo};
             float ft = 0.f, fd = 0.f;
-#pragma unroll
-            for (int i = 0; i < kCacheEntries; ++i) {
-                if (i == 8 && !wide) break;
+            cached_each([&](int i) {
                 ct[i] = exp2_scaled(ct[i], sct);
                 cd[i] = exp2_scaled(cd[i], scd);
                 ft += ct[i];
                 fd += cd[i];
-            }
+            });
             cached_row = -1;
             st = ft;
             sd = fd;
@@ -650,12 +654,10 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
         if constexpr (use_cache) {
             const float ft = thr_mt == -INFINITY ? 0.f : exp2_scaled(thr_mt, rd.t);
             const float fd = thr_md == -INFINITY ? 0.f : exp2_scaled(thr_md, rd.d);
-#pragma unroll
-            for (int i = 0; i < kCacheEntries; ++i) {
-                if (i == 8 && !wide) break;
+            cached_each([&](int i) {
                 ct[i] *= ft;
                 cd[i] *= fd;
-            }
+            });
         }
 
         c = 0.0;
@@ -755,12 +757,10 @@ __global__ __launch_bounds__(NT) void sample_walk_kernel(WalkArgs A) {
                     double run = before;
                     int64_t x = -1;
                     if constexpr (use_cache) {
-#pragma unroll
-                        for (int i = 0; i < kCacheEntries; ++i) {
-                            if (i == 8 && !wide) break;
+                        cached_each([&](int i) {
                             run += resid_from_exp(ct[i], cd[i], rd, c);
                             if (x < 0 && run > tgt) x = sa + i;
-                        }
+                        });
                     } else {
                         for_each8<DT>(row_ptr(A.tlogits, lr), row_ptr(A.dlogits, lr), sa, sb,
                                       A.vec_ok,
