@@ -1495,6 +1495,21 @@ bool dma_form(const Plan &pl, const AttnParams &P, int d) {
 template <int D>
 void launch_mfma(const Plan &pl, const AttnParams &P, unsigned groups, hipStream_t st) {
     const int remap = groups % 8 == 0 ? 1 : 0;
+    // Up to two rounds of workgroups (the length-balanced plan's usual 512),
+    // 4-wave register-staged workgroups two per CU give way to the LDS-load
+    // form's 8-wave key-half workgroups one per CU where that form applies
+    // (16 x 1024..8192 keys, 32 rows per KV head: 98 -> 87 us per call).
+    // The key halves change no row group, so neither the workspace nor the
+    // split plan changes.
+    if (D == 128 && pl.nw == 4 && groups <= 2 * kOneRound) {
+        Plan kh2 = pl;
+        kh2.nw = 8;
+        kh2.kh = 2;
+        if (dma_form(kh2, P, D)) {
+            hipLaunchKernelGGL(attn_dma_kernel<2>, dim3(groups), dim3(512), 0, st, P, remap);
+            return;
+        }
+    }
     if (D == 128 && dma_form(pl, P, D) && pl.kh == 2)
         hipLaunchKernelGGL(attn_dma_kernel<2>, dim3(groups), dim3(512), 0, st, P, remap);
     else if (D == 128 && dma_form(pl, P, D))

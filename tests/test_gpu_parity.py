@@ -363,6 +363,9 @@ DMA_CASES = {
                               page_size=4),
     "kh2_b1_ps64_L2600": W.shrink(W.CONFIGS[2], hist=("fixed", 2600), vocab=1000, page_size=64),
     "kh2_b16_rows35": W.shrink(W.CONFIGS[4], batch=16, hist=("fixed", 700), vocab=1000),
+    # 512 workgroups of 128 rows (two rounds): the key-half form one per CU
+    "kh2_two_rounds_b16_Lu": W.shrink(W.CONFIGS[3], batch=16, hist=("uniform", 200, 1500),
+                                      vocab=1000),
 }
 
 
